@@ -1,0 +1,316 @@
+"""Pins for the CPU oracle: closed forms, independently written reductions,
+exact rational arithmetic, brute force and invariants.
+
+Every check here runs on the CPU (no GPU marker).  Shapes use dk != dv so a
+transposed state (decay applied to value columns instead of key rows) fails.
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import rel_fro
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rnd_inputs(seed, B=2, T=12, H=3, dk=5, dv=3, loga_lo=-5.0, beta_max=1.0, s0=True, unit_k=True):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, T, H, dk))
+    k = rng.standard_normal((B, T, H, dk))
+    if unit_k:
+        k /= np.linalg.norm(k, axis=-1, keepdims=True)
+        q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    v = rng.standard_normal((B, T, H, dv))
+    la = rng.uniform(loga_lo, 0.0, (B, T, H, dk))
+    beta = rng.uniform(0.0, beta_max, (B, T, H))
+    S0 = rng.standard_normal((B, H, dk, dv)) if s0 else None
+    return q, k, v, la, beta, S0
+
+
+# ---------------------------------------------------------------- P14 constants
+
+def _golden_constants():
+    vals = {}
+    with open(os.path.join(GOLDEN, "floor_constants.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                name, val = line.split()[:2]
+                vals[name] = float(val)
+    return vals
+
+
+def test_page_floor_constants():
+    """The floor numbers printed on the page follow from log-alpha >= -5 and 16-token tiles."""
+    import torch
+    g = _golden_constants()
+    floor, tile = oracle.LOG_ALPHA_FLOOR, oracle.SUBTILE
+    assert round(100 * math.exp(floor), 2) == g["keep_per_step_percent"]
+    assert tile == g["tile_tokens"]
+    assert tile * floor == g["tile_log_decay_min"]
+    recip = math.exp(-tile * floor)
+    assert round(recip / 1e34, 1) * 1e34 == pytest.approx(g["reciprocal_bound"])
+    bf16_max = float(torch.finfo(torch.bfloat16).max)
+    assert round(bf16_max / 1e38, 1) * 1e38 == pytest.approx(g["bf16_max"])
+    assert recip < bf16_max and recip < float(torch.finfo(torch.float32).max)
+    # one tile more would not fit: e^(-5*32) overflows fp32 and bf16
+    assert math.exp(-2 * tile * floor) > float(torch.finfo(torch.float32).max)
+
+
+# ---------------------------------------------------------------- P7 brute force
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_loop_matches_bruteforce(seed):
+    x = rnd_inputs(seed, T=7)
+    o1, S1 = oracle.kda_loop(*x)
+    o2, S2 = oracle.kda_bruteforce(*x)
+    assert rel_fro(o1, o2) < 1e-12 and rel_fro(S1, S2) < 1e-12
+
+
+def _frac_matmul(A, B):
+    return [[sum(A[i][k] * B[k][j] for k in range(len(B))) for j in range(len(B[0]))]
+            for i in range(len(A))]
+
+
+def test_loop_matches_exact_rational():
+    """Exact rational evaluation of the definition on a tiny case (dk=2, dv=3, T=3)."""
+    F = Fraction
+    alphas = [[F(1, 2), F(3, 4)], [F(1, 1), F(1, 3)], [F(2, 3), F(1, 2)]]
+    betas = [F(1, 2), F(1, 1), F(1, 4)]
+    ks = [[F(3, 5), F(4, 5)], [F(1, 1), F(0)], [F(-4, 5), F(3, 5)]]
+    vs = [[F(1), F(-2), F(1, 2)], [F(3, 2), F(0), F(-1)], [F(-1, 3), F(2), F(1)]]
+    qs = [[F(1, 2), F(-1)], [F(2), F(1, 3)], [F(-1, 4), F(1)]]
+    S = [[F(1, 3), F(0), F(-1)], [F(1, 2), F(2), F(0)]]
+    S0 = [row[:] for row in S]
+    outs = []
+    for t in range(3):
+        Pm = [[(F(1) if i == j else F(0)) - betas[t] * ks[t][i] * ks[t][j] for j in range(2)] for i in range(2)]
+        Dm = [[alphas[t][i] if i == j else F(0) for j in range(2)] for i in range(2)]
+        S = _frac_matmul(_frac_matmul(Pm, Dm), S)
+        S = [[S[i][j] + betas[t] * ks[t][i] * vs[t][j] for j in range(3)] for i in range(2)]
+        outs.append([sum(S[i][j] * qs[t][i] for i in range(2)) for j in range(3)])
+    f = lambda a: np.array(a, dtype=np.float64)  # noqa: E731
+    la = np.log(f(alphas))
+    o, S_T = oracle.kda_loop(f(qs)[None, :, None], f(ks)[None, :, None], f(vs)[None, :, None],
+                             la[None, :, None], f(betas)[None, :, None], f(S0)[None, None])
+    assert np.abs(o[0, :, 0] - f(outs)).max() < 1e-14
+    assert np.abs(S_T[0, 0] - f(S)).max() < 1e-14
+
+
+# ---------------------------------------------------------------- P1 beta = 0
+
+def test_beta_zero_is_pure_decay():
+    q, k, v, la, beta, S0 = rnd_inputs(3)
+    beta = np.zeros_like(beta)
+    o, S_T = oracle.kda_loop(q, k, v, la, beta, S0)
+    G = np.cumsum(la, axis=1)                                  # [B,T,H,dk]
+    o_ref = np.einsum("bhcj,bthc->bthj", S0, q * np.exp(G))
+    S_ref = np.exp(G[:, -1])[..., None] * S0
+    assert rel_fro(o, o_ref) < 1e-13 and rel_fro(S_T, S_ref) < 1e-13
+
+
+# ---------------------------------------------------------------- P2 GLA limit
+
+def test_small_beta_is_gla_limit():
+    q, k, v, la, beta, _ = rnd_inputs(4, T=20)
+    eps = 1e-7
+    o, _ = oracle.kda_loop(q, k, v, la, np.full_like(beta, eps), None)
+    o_gla = oracle.gla_loop(q, k, v, la, None)
+    err = rel_fro(o / eps, o_gla)
+    assert err < 1e-5
+    # and the difference is first order in eps (a missing erase term would show as O(1))
+    o2, _ = oracle.kda_loop(q, k, v, la, np.full_like(beta, 2 * eps), None)
+    err2 = rel_fro(o2 / (2 * eps), o_gla)
+    assert 1.5 < err2 / err < 2.5
+
+
+# ---------------------------------------------------------------- P3 GDN reduction
+
+def test_scalar_gate_is_gated_deltanet():
+    q, k, v, la, beta, S0 = rnd_inputs(5, T=16)
+    la_head = la[..., 0]                                       # one gate per (b,t,h)
+    la_b = np.repeat(la_head[..., None], la.shape[-1], axis=-1)
+    o, S_T = oracle.kda_loop(q, k, v, la_b, beta, S0)
+    o_g, S_g = oracle.gdn_loop(q, k, v, la_head, beta, S0)
+    assert rel_fro(o, o_g) < 1e-12 and rel_fro(S_T, S_g) < 1e-12
+
+
+# ---------------------------------------------------------------- P4 write-then-read
+
+def test_write_then_read_returns_v():
+    q, k, v, la, beta, S0 = rnd_inputs(6, T=10)
+    o, _ = oracle.kda_loop(k, k, v, np.zeros_like(la), np.ones_like(beta), S0)
+    assert np.abs(o - v).max() < 1e-12
+
+
+# ---------------------------------------------------------------- P5 one-hot keys
+
+def test_one_hot_keys_decouple_into_row_emas():
+    rng = np.random.default_rng(7)
+    B, T, H, dk, dv = 1, 30, 2, 4, 6
+    idx = rng.integers(0, dk, (B, T, H))
+    k = np.eye(dk)[idx]
+    q = rng.standard_normal((B, T, H, dk))
+    v = rng.standard_normal((B, T, H, dv))
+    la = rng.uniform(-5, 0, (B, T, H, dk))
+    beta = rng.uniform(0, 1, (B, T, H))
+    S0 = rng.standard_normal((B, H, dk, dv))
+    o, S_T = oracle.kda_loop(q, k, v, la, beta, S0)
+    for h in range(H):
+        S = S0[0, h].copy()
+        for t in range(T):
+            for c in range(dk):
+                S[c] = math.exp(la[0, t, h, c]) * S[c]
+            c = idx[0, t, h]
+            S[c] = (1 - beta[0, t, h]) * S[c] + beta[0, t, h] * v[0, t, h]
+            assert np.abs(o[0, t, h] - S.T @ q[0, t, h]).max() < 1e-12
+        assert np.abs(S_T[0, h] - S).max() < 1e-12
+
+
+# ---------------------------------------------------------------- P6 orthonormal keys
+
+def test_orthonormal_keys_no_erasure():
+    rng = np.random.default_rng(8)
+    dk, dv, T = 8, 5, 8
+    Qm, _ = np.linalg.qr(rng.standard_normal((dk, dk)))
+    k = Qm.T[None, :, None, :]                                  # rows are orthonormal
+    q = rng.standard_normal((1, T, 1, dk))
+    v = rng.standard_normal((1, T, 1, dv))
+    beta = rng.uniform(0, 1, (1, T, 1))
+    o, _ = oracle.kda_loop(q, k, v, np.zeros((1, T, 1, dk)), beta, None)
+    for t in range(T):
+        ref = sum(beta[0, s, 0] * (q[0, t, 0] @ k[0, s, 0]) * v[0, s, 0] for s in range(t + 1))
+        assert np.abs(o[0, t, 0] - ref).max() < 1e-12
+
+
+# ---------------------------------------------------------------- P8 chunked form
+
+@pytest.mark.parametrize("chunk", [1, 2, 4, 8, 16, 32, 64, 128])
+@pytest.mark.parametrize("pairwise", [False, True])
+def test_chunked_matches_loop(chunk, pairwise):
+    if pairwise and chunk > 32:
+        pytest.skip("pairwise form is O(C^2 dk) memory; checked on small chunks")
+    x = rnd_inputs(9, B=1, T=150, H=2, dk=6, dv=4)
+    o1, S1 = oracle.kda_loop(*x)
+    o2, S2 = oracle.kda_chunked(*x, chunk=chunk, pairwise=pairwise)
+    assert rel_fro(o2, o1) < 1e-11 and rel_fro(S2, S1) < 1e-11
+
+
+def test_chunked_at_the_floor():
+    """Every token at the floor: a 16-token tile reaches exactly -80 and a 64-chunk -320."""
+    q, k, v, la, beta, S0 = rnd_inputs(10, B=1, T=96, H=2, dk=6, dv=4)
+    la = np.full_like(la, -5.0)
+    o1, S1 = oracle.kda_loop(q, k, v, la, beta, S0)
+    for C in (16, 64):
+        o2, S2 = oracle.kda_chunked(q, k, v, la, beta, S0, chunk=C)
+        assert np.isfinite(o2).all() and rel_fro(o2, o1) < 1e-10 and rel_fro(S2, S1) < 1e-10
+
+
+# ---------------------------------------------------------------- P9 split / resume
+
+def test_split_resume():
+    q, k, v, la, beta, S0 = rnd_inputs(11, T=40)
+    o, S_T = oracle.kda_loop(q, k, v, la, beta, S0)
+    o1, S_mid = oracle.kda_loop(q[:, :17], k[:, :17], v[:, :17], la[:, :17], beta[:, :17], S0)
+    o2, S_end = oracle.kda_loop(q[:, 17:], k[:, 17:], v[:, 17:], la[:, 17:], beta[:, 17:], S_mid)
+    assert rel_fro(np.concatenate([o1, o2], 1), o) < 1e-12 and rel_fro(S_end, S_T) < 1e-12
+
+
+def test_decode_steps_equal_loop():
+    q, k, v, la, beta, S0 = rnd_inputs(12, T=9)
+    o, S_T = oracle.kda_loop(q, k, v, la, beta, S0)
+    S = S0.copy()
+    for t in range(q.shape[1]):
+        ot, S = oracle.kda_decode_step(S, q[:, t], k[:, t], v[:, t], la[:, t], beta[:, t])
+        assert np.abs(ot - o[:, t]).max() < 1e-12
+    assert rel_fro(S, S_T) < 1e-12
+
+
+# ---------------------------------------------------------------- P10 segments
+
+def test_segment_composition_equals_full_run():
+    q, k, v, la, beta, S0 = rnd_inputs(13, B=1, T=50, H=2)
+    o, S_T = oracle.kda_loop(q, k, v, la, beta, S0)
+    for seg in (7, 16, 50):
+        o2, S2 = oracle.kda_segmented(q, k, v, la, beta, S0, seg_len=seg)
+        assert rel_fro(o2, o) < 1e-11 and rel_fro(S2, S_T) < 1e-11
+
+
+def test_segment_pairs_compose_associatively_and_naive_sum_fails():
+    q, k, v, la, beta, S0 = rnd_inputs(14, B=1, T=48, H=1)
+    pairs = oracle.segment_pairs(k[0, :, 0], v[0, :, 0], la[0, :, 0], beta[0, :, 0], 12)
+    _, S_T = oracle.kda_loop(q, k, v, la, beta, None)
+    left = oracle.compose(oracle.compose(pairs[3], pairs[2]), oracle.compose(pairs[1], pairs[0]))
+    right = oracle.compose(pairs[3], oracle.compose(pairs[2], oracle.compose(pairs[1], pairs[0])))
+    assert rel_fro(left[1], S_T[0, 0]) < 1e-12 and rel_fro(right[0], left[0]) < 1e-12
+    naive = sum(p[1] for p in pairs)       # what plain linear attention could do; wrong for KDA
+    assert rel_fro(naive, S_T[0, 0]) > 1e-2
+
+
+def test_segment_transition_is_the_recurrence_on_identity():
+    """By linearity in S0, running with S0 = I and v = 0 yields the transition matrix."""
+    q, k, v, la, beta, _ = rnd_inputs(15, B=1, T=20, H=1, dk=5, dv=5)
+    M = oracle.segment_transition(k[0, :, 0], la[0, :, 0], beta[0, :, 0])
+    _, S = oracle.kda_loop(q, k, np.zeros_like(v), la, beta, np.eye(5)[None, None])
+    assert rel_fro(M, S[0, 0]) < 1e-12
+
+
+# ---------------------------------------------------------------- P11 structure
+
+def test_linearity_in_v_and_state():
+    q, k, v1, la, beta, S01 = rnd_inputs(16)
+    _, _, v2, _, _, S02 = rnd_inputs(17)
+    a, b = 0.7, -1.3
+    o, S = oracle.kda_loop(q, k, a * v1 + b * v2, la, beta, a * S01 + b * S02)
+    o1, Sa = oracle.kda_loop(q, k, v1, la, beta, S01)
+    o2, Sb = oracle.kda_loop(q, k, v2, la, beta, S02)
+    assert rel_fro(o, a * o1 + b * o2) < 1e-12 and rel_fro(S, a * Sa + b * Sb) < 1e-12
+
+
+def test_value_columns_are_separable():
+    q, k, v, la, beta, S0 = rnd_inputs(18, dv=6)
+    o, S = oracle.kda_loop(q, k, v, la, beta, S0)
+    cols = [1, 4]
+    o2, S2 = oracle.kda_loop(q, k, v[..., cols], la, beta, S0[..., cols])
+    assert rel_fro(o2, o[..., cols]) < 1e-12 and rel_fro(S2, S[..., cols]) < 1e-12
+
+
+def test_head_and_batch_permutation_equivariance():
+    q, k, v, la, beta, S0 = rnd_inputs(19, B=3, H=4)
+    o, S = oracle.kda_loop(q, k, v, la, beta, S0)
+    ph, pb = [2, 0, 3, 1], [1, 2, 0]
+    xp = [x[pb][:, :, ph] for x in (q, k, v, la)]
+    o2, S2 = oracle.kda_loop(*xp, beta[pb][:, :, ph], S0[pb][:, ph])
+    assert rel_fro(o2, o[pb][:, :, ph]) < 1e-13 and rel_fro(S2, S[pb][:, ph]) < 1e-13
+
+
+# ---------------------------------------------------------------- P12 non-expansiveness
+
+def test_state_growth_bound():
+    q, k, v, la, beta, S0 = rnd_inputs(20, B=1, H=1, T=60)
+    S = S0
+    for t in range(60):
+        _, S_new = oracle.kda_decode_step(S, q[:, t], k[:, t], v[:, t], la[:, t], beta[:, t])
+        bound = np.linalg.norm(S[0, 0], 2) + beta[0, t, 0] * np.linalg.norm(v[0, t, 0])
+        assert np.linalg.norm(S_new[0, 0], 2) <= bound * (1 + 1e-12)
+        S = S_new
+
+
+# ---------------------------------------------------------------- P13 floor clamp
+
+def test_floor_clamps_out_of_range_gates():
+    q, k, v, la, beta, S0 = rnd_inputs(21, T=20)
+    la_out = la.copy()
+    la_out[:, ::3] = -9.0          # below the floor
+    la_out[:, 1::5] = 0.4          # above 0 (no growth)
+    la_in = np.minimum(np.maximum(la_out, -5.0), 0.0)
+    o1, S1 = oracle.kda_loop(q, k, v, la_out, beta, S0)
+    o2, S2 = oracle.kda_loop(q, k, v, la_in, beta, S0)
+    assert np.array_equal(o1, o2) and np.array_equal(S1, S2)
+    # a wrong clamp would change the result: -9 is not -5
+    o3, _ = oracle.kda_loop(q, k, v, np.where(la_out < -5, -9.0, la_in), beta, S0)
+    assert np.array_equal(o3, o1)          # the oracle itself clamps -9 to -5
+    assert oracle.floor_log_alpha(np.array([-9.0, -5.0, -1.0, 0.0, 0.4])).tolist() == [-5, -5, -1, 0, 0]
