@@ -1,0 +1,195 @@
+"""KDA (Kimi Delta Attention) hot path on MI355X: Python binding of libkda.so.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/kda.h.  PyTorch supplies device
+memory and the current stream.  Importing this package loads libkda.so and
+fails loudly if it has not been built (``python -m gated_delta_rule_107_amd.build``).
+
+    o, S_T = chunk_fwd(q, k, v, log_alpha, beta, S0=None, chunk=64)
+    o      = decode_step(state, q, k, v, log_alpha, beta)      # state updated in place
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["KdaError", "Plan", "chunk_fwd", "decode_step", "default_plan", "workspace_bytes",
+           "library_path", "ERRORS"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libkda.so")
+
+ERRORS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE", 4: "KDA_ERR_ALIGN",
+          5: "KDA_ERR_UNSUPPORTED", 6: "KDA_ERR_WORKSPACE", 7: "KDA_ERR_HIP", 8: "KDA_ERR_ALIAS"}
+DTYPE_F32, DTYPE_BF16 = 0, 1
+
+
+class KdaError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{ERRORS.get(code, code)}: {msg}")
+        self.code = code
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("n_segments", ctypes.c_int32), ("dv_block", ctypes.c_int32)]
+
+    def __repr__(self):
+        return f"Plan(n_segments={self.n_segments}, dv_block={self.dv_block})"
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build it with `python -m gated_delta_rule_107_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
+    lib.kda_chunk_fwd.restype = i32
+    lib.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, i32,
+                                  ctypes.POINTER(Plan), vp, sz, vp]
+    lib.kda_decode_step.restype = i32
+    lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, vp]
+    lib.kda_chunk_fwd_default_plan.restype = i32
+    lib.kda_chunk_fwd_default_plan.argtypes = [i64, i64, i32, i32, i32, i32, i32, ctypes.POINTER(Plan)]
+    lib.kda_chunk_fwd_workspace_bytes.restype = i32
+    lib.kda_chunk_fwd_workspace_bytes.argtypes = [i64, i64, i32, i32, i32, i32, i32, ctypes.POINTER(Plan),
+                                                  ctypes.POINTER(sz)]
+    lib.kda_status_str.restype = ctypes.c_char_p
+    lib.kda_status_str.argtypes = [i32]
+    lib.kda_last_error.restype = ctypes.c_char_p
+    lib.kda_last_error.argtypes = []
+    lib.kda_abi_version.restype = i32
+    lib.kda_abi_version.argtypes = []
+    return lib
+
+
+_lib = _load()
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libkda.so (ctypes handle)."""
+    return _lib
+
+
+def _check(code: int):
+    if code != 0:
+        raise KdaError(code, _lib.kda_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    raise KdaError(3, f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _require(t: torch.Tensor, name: str, dtype: torch.dtype | None, shape: tuple, device):
+    if not isinstance(t, torch.Tensor):
+        raise KdaError(1, f"{name} must be a tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise KdaError(3, f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise KdaError(2, f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.device != device:
+        raise KdaError(2, f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise KdaError(2, f"{name} must be contiguous")
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def default_plan(B, T, H, dk, dv, chunk=64, dtype=torch.bfloat16) -> Plan:
+    plan = Plan()
+    code = DTYPE_BF16 if dtype == torch.bfloat16 else DTYPE_F32
+    _check(_lib.kda_chunk_fwd_default_plan(B, T, H, dk, dv, chunk, code, ctypes.byref(plan)))
+    return plan
+
+
+def workspace_bytes(B, T, H, dk, dv, chunk=64, dtype=torch.bfloat16, plan: Plan | None = None) -> int:
+    n = ctypes.c_size_t(0)
+    code = DTYPE_BF16 if dtype == torch.bfloat16 else DTYPE_F32
+    _check(_lib.kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk, code,
+                                              ctypes.byref(plan) if plan is not None else None,
+                                              ctypes.byref(n)))
+    return n.value
+
+
+def chunk_fwd(q, k, v, log_alpha, beta, S0=None, chunk: int = 64, plan: Plan | None = None,
+              o=None, S_T=None, workspace=None):
+    """Chunked prefill: returns (o [B,T,H,dv] in q's dtype, S_T [B,H,dk,dv] float32).
+
+    ``S_T`` may be passed as ``S0`` itself to advance the state in place.
+    ``plan`` (a Plan) overrides the library's default segmentation / column blocking.
+    """
+    if q.dim() != 4:
+        raise KdaError(2, "q must be [B,T,H,dk]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise KdaError(2, "tensors must be on a GPU")
+    dt = _dtype_code(q)
+    _require(q, "q", q.dtype, (B, T, H, dk), dev)
+    _require(k, "k", q.dtype, (B, T, H, dk), dev)
+    _require(v, "v", q.dtype, (B, T, H, dv), dev)
+    _require(log_alpha, "log_alpha", torch.float32, (B, T, H, dk), dev)
+    _require(beta, "beta", torch.float32, (B, T, H), dev)
+    if S0 is not None:
+        _require(S0, "S0", torch.float32, (B, H, dk, dv), dev)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
+    else:
+        _require(o, "o", q.dtype, (B, T, H, dv), dev)
+    if S_T is None:
+        S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    else:
+        _require(S_T, "S_T", torch.float32, (B, H, dk, dv), dev)
+    nws = workspace_bytes(B, T, H, dk, dv, chunk, q.dtype, plan)
+    if nws > 0:
+        if workspace is None or workspace.numel() * workspace.element_size() < nws:
+            workspace = torch.empty(nws, dtype=torch.uint8, device=dev)
+    else:
+        workspace = None
+    code = _lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0),
+                              _ptr(o), _ptr(S_T), B, T, H, dk, dv, chunk, dt,
+                              ctypes.byref(plan) if plan is not None else None,
+                              _ptr(workspace), nws, _stream(dev))
+    _check(code)
+    return o, S_T
+
+
+def decode_step(state, q, k, v, log_alpha, beta, o=None):
+    """One recurrent step for N sequences; ``state`` [N,H,dk,dv] float32 is updated in place.
+    q, k [N,H,dk], v [N,H,dv] (bf16 or float32), log_alpha [N,H,dk], beta [N,H] float32.
+    Returns o [N,H,dv]."""
+    if state.dim() != 4:
+        raise KdaError(2, "state must be [N,H,dk,dv]")
+    N, H, dk, dv = state.shape
+    dev = state.device
+    if dev.type != "cuda":
+        raise KdaError(2, "tensors must be on a GPU")
+    dt = _dtype_code(q)
+    _require(state, "state", torch.float32, (N, H, dk, dv), dev)
+    _require(q, "q", q.dtype, (N, H, dk), dev)
+    _require(k, "k", q.dtype, (N, H, dk), dev)
+    _require(v, "v", q.dtype, (N, H, dv), dev)
+    _require(log_alpha, "log_alpha", torch.float32, (N, H, dk), dev)
+    _require(beta, "beta", torch.float32, (N, H), dev)
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=q.dtype, device=dev)
+    else:
+        _require(o, "o", q.dtype, (N, H, dv), dev)
+    _check(_lib.kda_decode_step(_ptr(state), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                _ptr(o), N, H, dk, dv, dt, _stream(dev)))
+    return o

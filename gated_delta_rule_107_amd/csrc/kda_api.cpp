@@ -1,0 +1,273 @@
+// C ABI of libkda.so: argument validation, plan selection and launch order.
+// Every argument error is detected before the first HIP call.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "kda.h"
+#include "kda_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+kda_status_t fail(kda_status_t s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+kda_status_t hip_fail(hipError_t e, const char* what) {
+    return fail(KDA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool dim_ok(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool chunk_ok(int32_t c) { return c == 16 || c == 32 || c == 64; }
+bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Compute units of the current device, cached per device; 256 (MI355X) if no device is visible.
+int device_cus() {
+    static std::mutex mu;
+    static std::vector<int> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    std::lock_guard<std::mutex> lk(mu);
+    if ((int)cache.size() <= dev) cache.resize(dev + 1, 0);
+    if (cache[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+            (void)hipGetLastError();
+            cus = 256;
+        }
+        cache[dev] = cus;
+    }
+    return cache[dev];
+}
+
+kda_status_t check_problem(int64_t B, int64_t T, int32_t H, int32_t dk, int32_t dv, int32_t chunk,
+                           kda_dtype_t dt) {
+    if (B < 1 || H < 1 || T < 0) return fail(KDA_ERR_SHAPE, "need B >= 1, H >= 1, T >= 0 (got B=%lld H=%d T=%lld)",
+                                             (long long)B, H, (long long)T);
+    if (dt != KDA_DTYPE_F32 && dt != KDA_DTYPE_BF16) return fail(KDA_ERR_DTYPE, "unknown dtype %d", (int)dt);
+    if (!dim_ok(dk) || !dim_ok(dv)) return fail(KDA_ERR_UNSUPPORTED, "dk, dv must be 16, 32, 64 or 128 (got %d, %d)", dk, dv);
+    if (!chunk_ok(chunk)) return fail(KDA_ERR_UNSUPPORTED, "chunk must be 16, 32 or 64 (got %d)", chunk);
+    if (dt == KDA_DTYPE_F32 && chunk * dk > 4096)
+        return fail(KDA_ERR_UNSUPPORTED, "float32 inputs need chunk * dk <= 4096 (got %d)", chunk * dk);
+    if (B * T * (int64_t)H > (int64_t)1 << 40) return fail(KDA_ERR_SHAPE, "problem too large");
+    return KDA_OK;
+}
+
+struct Resolved {
+    int32_t n_seg;
+    int64_t seg_len;
+    int32_t dv_block;
+};
+
+kda_status_t resolve_plan(int64_t B, int64_t T, int32_t H, int32_t dk, int32_t dv, int32_t chunk,
+                          kda_dtype_t dt, const kda_plan_t* plan, Resolved* out) {
+    kda_plan_t p = plan ? *plan : kda_plan_t{0, 0};
+    int32_t dvb = p.dv_block;
+    if (dvb == 0) dvb = dv;                                   // one column block per (b, h)
+    if (dvb < 16 || dvb > 128 || dvb % 16 != 0 || dv % dvb != 0)
+        return fail(KDA_ERR_UNSUPPORTED, "dv_block %d must be a multiple of 16 that divides dv=%d, at most 128", dvb, dv);
+    if (kda::chunk_lds_bytes(dt == KDA_DTYPE_BF16, dk, chunk, dvb) > 163840)
+        return fail(KDA_ERR_UNSUPPORTED, "dk=%d chunk=%d dv_block=%d exceeds the 160 KiB LDS of a workgroup", dk, chunk, dvb);
+    const int64_t nchunks = (T + chunk - 1) / chunk;
+    int64_t nseg = p.n_segments;
+    if (nseg < 0) return fail(KDA_ERR_UNSUPPORTED, "n_segments must be >= 0");
+    if (nseg == 0) {
+        // enough workgroups to cover every compute unit; segments only when (b, h, column
+        // block) units alone cannot, and only if each segment keeps at least 2 chunks
+        const int64_t units = B * H * (dv / dvb);
+        const int64_t cus = device_cus();
+        nseg = 1;
+        if (units < cus && dk % dvb == 0) {
+            nseg = (cus + units - 1) / units;
+            if (nseg > nchunks / 2) nseg = nchunks / 2;
+            if (nseg < 1) nseg = 1;
+        }
+    }
+    if (nseg > 1 && dk % dvb != 0)
+        return fail(KDA_ERR_UNSUPPORTED, "segments need dv_block (%d) to divide dk (%d)", dvb, dk);
+    if (nseg > 65535) return fail(KDA_ERR_UNSUPPORTED, "too many segments");
+    int64_t seg_chunks = nchunks == 0 ? 1 : (nchunks + nseg - 1) / nseg;
+    if (seg_chunks < 1) seg_chunks = 1;
+    out->seg_len = seg_chunks * chunk;
+    out->n_seg = nchunks == 0 ? 1 : (int32_t)((nchunks + seg_chunks - 1) / seg_chunks);
+    out->dv_block = dvb;
+    return KDA_OK;
+}
+
+size_t workspace_for(int64_t B, int32_t H, int32_t dk, int32_t dv, const Resolved& r) {
+    if (r.n_seg <= 1) return 0;
+    return (size_t)B * H * r.n_seg * ((size_t)2 * dk * dv + (size_t)dk * dk) * sizeof(float);
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_status_str(kda_status_t s) {
+    switch (s) {
+        case KDA_OK: return "ok";
+        case KDA_ERR_NULL: return "null pointer";
+        case KDA_ERR_SHAPE: return "invalid shape";
+        case KDA_ERR_DTYPE: return "invalid dtype";
+        case KDA_ERR_ALIGN: return "pointer not 16-byte aligned";
+        case KDA_ERR_UNSUPPORTED: return "unsupported size or plan";
+        case KDA_ERR_WORKSPACE: return "workspace too small";
+        case KDA_ERR_HIP: return "HIP runtime error";
+        case KDA_ERR_ALIAS: return "output overlaps an input";
+    }
+    return "unknown status";
+}
+
+const char* kda_last_error(void) { return g_err; }
+
+int32_t kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+kda_status_t kda_chunk_fwd_default_plan(int64_t B, int64_t T, int32_t H, int32_t dk, int32_t dv,
+                                        int32_t chunk, kda_dtype_t dt, kda_plan_t* plan) {
+    if (!plan) return fail(KDA_ERR_NULL, "plan is NULL");
+    kda_status_t s = check_problem(B, T, H, dk, dv, chunk, dt);
+    if (s != KDA_OK) return s;
+    Resolved r;
+    s = resolve_plan(B, T, H, dk, dv, chunk, dt, nullptr, &r);
+    if (s != KDA_OK) return s;
+    plan->n_segments = r.n_seg;
+    plan->dv_block = r.dv_block;
+    return KDA_OK;
+}
+
+kda_status_t kda_chunk_fwd_workspace_bytes(int64_t B, int64_t T, int32_t H, int32_t dk, int32_t dv,
+                                           int32_t chunk, kda_dtype_t dt, const kda_plan_t* plan,
+                                           size_t* bytes) {
+    if (!bytes) return fail(KDA_ERR_NULL, "bytes is NULL");
+    kda_status_t s = check_problem(B, T, H, dk, dv, chunk, dt);
+    if (s != KDA_OK) return s;
+    Resolved r;
+    s = resolve_plan(B, T, H, dk, dv, chunk, dt, plan, &r);
+    if (s != KDA_OK) return s;
+    *bytes = workspace_for(B, H, dk, dv, r);
+    return KDA_OK;
+}
+
+kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
+                           const float* beta, const float* S0, void* o, float* S_T, int64_t B,
+                           int64_t T, int32_t H, int32_t dk, int32_t dv, int32_t chunk,
+                           kda_dtype_t dt, const kda_plan_t* plan, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    kda_status_t s = check_problem(B, T, H, dk, dv, chunk, dt);
+    if (s != KDA_OK) return s;
+    if (!S_T) return fail(KDA_ERR_NULL, "S_T is NULL");
+    if (T > 0 && (!q || !k || !v || !log_alpha || !beta || !o))
+        return fail(KDA_ERR_NULL, "q, k, v, log_alpha, beta and o are required when T > 0");
+    const void* ptrs[] = {q, k, v, log_alpha, beta, S0, o, S_T, workspace};
+    for (const void* p : ptrs)
+        if (p && !aligned(p)) return fail(KDA_ERR_ALIGN, "pointer %p is not 16-byte aligned", p);
+    Resolved r;
+    s = resolve_plan(B, T, H, dk, dv, chunk, dt, plan, &r);
+    if (s != KDA_OK) return s;
+    const size_t need = workspace_for(B, H, dk, dv, r);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : (size_t)0);
+
+    const size_t es = dt == KDA_DTYPE_BF16 ? 2 : 4;
+    const size_t n_qk = (size_t)(B * T * H) * dk, n_v = (size_t)(B * T * H) * dv;
+    const size_t n_s = (size_t)(B * H) * dk * dv * 4;
+    const size_t n_o = n_v * es;
+    struct Span { const void* p; size_t n; const char* name; } ins[] = {
+        {q, n_qk * es, "q"}, {k, n_qk * es, "k"}, {v, n_v * es, "v"}, {log_alpha, n_qk * 4, "log_alpha"},
+        {beta, (size_t)(B * T * H) * 4, "beta"}, {S0, S0 ? n_s : 0, "S0"}, {S_T, n_s, "S_T"},
+        {workspace, need, "workspace"}};
+    for (const Span& in : ins)
+        if (T > 0 && overlaps(o, n_o, in.p, in.n)) return fail(KDA_ERR_ALIAS, "o overlaps %s", in.name);
+    for (int i = 0; i < 5; ++i)
+        if (overlaps(S_T, n_s, ins[i].p, ins[i].n)) return fail(KDA_ERR_ALIAS, "S_T overlaps %s", ins[i].name);
+    if (S0 && S0 != S_T && overlaps(S0, n_s, S_T, n_s)) return fail(KDA_ERR_ALIAS, "S_T partially overlaps S0");
+    if (need > 0) {
+        for (int i = 0; i < 7; ++i)
+            if (overlaps(workspace, need, ins[i].p, ins[i].n)) return fail(KDA_ERR_ALIAS, "workspace overlaps %s", ins[i].name);
+    }
+
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    kda::ChunkArgs a{};
+    a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta;
+    a.o = o; a.s_final = S_T;
+    a.B = B; a.T = T; a.H = H; a.dk = dk; a.dv = dv; a.chunk = chunk;
+    a.n_seg = r.n_seg; a.seg_len = r.seg_len; a.dv_block = r.dv_block;
+    a.bf16 = dt == KDA_DTYPE_BF16;
+    hipError_t e;
+    if (r.n_seg == 1) {
+        a.mode = 0;
+        a.s0 = S0;
+        e = kda::launch_chunk(a, st);
+        if (e != hipSuccess) return hip_fail(e, "chunk kernel launch");
+        return KDA_OK;
+    }
+    float* ws = reinterpret_cast<float*>(workspace);
+    const size_t per = (size_t)B * H * r.n_seg;
+    float* s_loc = ws;
+    float* m_tr = s_loc + per * dk * dv;
+    float* starts = m_tr + per * dk * dk;
+    // pass 1: segment pairs
+    a.mode = 1;
+    a.s_loc = s_loc;
+    a.m_tr = m_tr;
+    e = kda::launch_chunk(a, st);
+    if (e != hipSuccess) return hip_fail(e, "segment pass-1 launch");
+    // prefix scan over the pairs
+    kda::ScanArgs sc{S0, s_loc, m_tr, starts, B, H, dk, dv, r.n_seg};
+    e = kda::launch_scan(sc, st);
+    if (e != hipSuccess) return hip_fail(e, "segment scan launch");
+    // pass 2: every segment from its true start state
+    a.mode = 0;
+    a.s0 = nullptr;
+    a.starts = starts;
+    e = kda::launch_chunk(a, st);
+    if (e != hipSuccess) return hip_fail(e, "segment pass-2 launch");
+    return KDA_OK;
+}
+
+kda_status_t kda_decode_step(float* state, const void* q, const void* k, const void* v,
+                             const float* log_alpha, const float* beta, void* o, int64_t N,
+                             int32_t H, int32_t dk, int32_t dv, kda_dtype_t dt, void* stream) {
+    if (N < 1 || H < 1) return fail(KDA_ERR_SHAPE, "need N >= 1, H >= 1 (got N=%lld H=%d)", (long long)N, H);
+    if (dt != KDA_DTYPE_F32 && dt != KDA_DTYPE_BF16) return fail(KDA_ERR_DTYPE, "unknown dtype %d", (int)dt);
+    if (!dim_ok(dk) || !dim_ok(dv)) return fail(KDA_ERR_UNSUPPORTED, "dk, dv must be 16, 32, 64 or 128 (got %d, %d)", dk, dv);
+    if (N * (int64_t)H > 0x7fffffff) return fail(KDA_ERR_SHAPE, "N * H too large");
+    if (!state || !q || !k || !v || !log_alpha || !beta || !o) return fail(KDA_ERR_NULL, "all pointers are required");
+    const void* ptrs[] = {state, q, k, v, log_alpha, beta, o};
+    for (const void* p : ptrs)
+        if (!aligned(p)) return fail(KDA_ERR_ALIGN, "pointer %p is not 16-byte aligned", p);
+    const size_t es = dt == KDA_DTYPE_BF16 ? 2 : 4;
+    const size_t nh = (size_t)N * H;
+    struct Span { const void* p; size_t n; const char* name; } ins[] = {
+        {state, nh * dk * dv * 4, "state"}, {q, nh * dk * es, "q"}, {k, nh * dk * es, "k"}, {v, nh * dv * es, "v"},
+        {log_alpha, nh * dk * 4, "log_alpha"}, {beta, nh * 4, "beta"}};
+    for (const Span& in : ins)
+        if (overlaps(o, nh * dv * es, in.p, in.n)) return fail(KDA_ERR_ALIAS, "o overlaps %s", in.name);
+    for (int i = 1; i < 6; ++i)
+        if (overlaps(state, ins[0].n, ins[i].p, ins[i].n)) return fail(KDA_ERR_ALIAS, "state overlaps %s", ins[i].name);
+    kda::DecodeArgs a{state, q, k, v, log_alpha, beta, o, N, H, dk, dv, dt == KDA_DTYPE_BF16};
+    hipError_t e = kda::launch_decode(a, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
+    return KDA_OK;
+}
+
+}  // extern "C"

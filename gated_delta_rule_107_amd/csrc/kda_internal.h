@@ -1,0 +1,65 @@
+// Host-side launch interface between the C ABI layer (kda_api.cpp) and the
+// HIP kernels.  Arguments are validated by the ABI layer before they get here.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct DecodeArgs {
+    float* state;
+    const void *q, *k, *v;
+    const float *log_alpha, *beta;
+    void* o;
+    int64_t N;
+    int32_t H, dk, dv;
+    bool bf16;
+};
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
+
+// One launch of the chunk kernel covers every (batch, head, segment, column block).
+//   mode 0: full evaluation of each segment from its start state; writes o and,
+//           for the last segment, the final state.
+//   mode 1: segment summaries (pass 1) for segments 0 .. n_seg-2: the state is
+//           widened to [S | M] (dv + dk columns) started from [0 | I] with value
+//           columns [v | 0]; writes S_loc (dk x dv) and M (dk x dk) per segment.
+struct ChunkArgs {
+    const void *q, *k, *v;
+    const float *log_alpha, *beta;
+    const float* s0;        // [B,H,dk,dv] or null (zeros): start state when n_seg == 1 (mode 0)
+    const float* starts;    // [B,H,P,dk,dv] start state of every segment (mode 0, n_seg > 1)
+    void* o;                // [B,T,H,dv] (mode 0)
+    float* s_final;         // [B,H,dk,dv] (mode 0)
+    float* s_loc;           // [B,H,P,dk,dv] (mode 1)
+    float* m_tr;            // [B,H,P,dk,dk] (mode 1)
+    int64_t B, T;
+    int32_t H, dk, dv, chunk;
+    int32_t n_seg;          // P
+    int64_t seg_len;        // tokens per segment, a multiple of chunk
+    int32_t dv_block;       // columns per workgroup (16 per wave)
+    int32_t mode;
+    bool bf16;
+};
+
+hipError_t launch_chunk(const ChunkArgs& a, hipStream_t st);
+
+// Prefix scan over segment pairs: starts[i+1] = M_i starts[i] + S_loc_i,
+// starts[0] = s0 (or zeros); writes starts[1 .. P-1].
+struct ScanArgs {
+    const float* s0;
+    const float* s_loc;
+    const float* m_tr;
+    float* starts;
+    int64_t B;
+    int32_t H, dk, dv, n_seg;
+};
+
+hipError_t launch_scan(const ScanArgs& a, hipStream_t st);
+
+// Bytes of dynamic LDS the chunk kernel needs (0 if the shape does not fit).
+size_t chunk_lds_bytes(bool bf16, int dk, int chunk, int dv_block);
+
+}  // namespace kda

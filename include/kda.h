@@ -1,0 +1,157 @@
+/*
+ * kda.h -- C ABI of the KDA (Kimi Delta Attention) hot-path library for
+ * AMD Instinct MI355X (gfx950).  Link with libkda.so.
+ *
+ * What the library computes.  Per (batch, head) a fixed-size state S with dk
+ * rows (key channels) and dv columns (value channels), float32, evolves token
+ * by token as
+ *
+ *     g_t = min(max(log_alpha_t, -5), 0)            per key channel
+ *     S_t = (I - beta_t k_t k_t^T) Diag(exp(g_t)) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = S_t^T q_t
+ *
+ * Sources: the state replaces the key/value cache and is updated per token,
+ * then multiplied by the query (llm-wiki.hwlabs.dev, "Kimi K3 ... linear
+ * attention", section "1. Limits of softmax attention and KDA's direction");
+ * one decay gate per feature channel where GatedDeltaNet has one per head
+ * (same page, "Difference between GatedDeltaNet and KDA"); log-decay floored
+ * so each step keeps at least 0.67 % (orkas.ai "Kimi K3 architecture",
+ * section "The floor that removed a GPU code path").  The pages do not print
+ * the formula; decay-then-delta order, the post-update read and the clamp at
+ * 0 are this library's reading.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - All tensor pointers are DEVICE pointers, owned by the caller; the library
+ *   never allocates, frees or synchronises.  Work is enqueued on `stream`
+ *   (a hipStream_t; NULL = the default stream).  KDA_OK means "enqueued".
+ * - Layouts are dense row-major (C order), base pointers 16-byte aligned.
+ * - Argument errors are detected before any HIP call: the call returns the
+ *   code, writes nothing and records a message for kda_last_error().  Input
+ *   values are not checked: NaN / Inf propagate.
+ * - A failed kernel launch returns KDA_ERR_HIP (text via kda_last_error()).
+ * - Supported sizes: dk, dv in {16, 32, 64, 128}; chunk in {16, 32, 64};
+ *   any T >= 0 (a partial last chunk is masked); B, N, H >= 1.  For float32
+ *   q/k/v the chunk must satisfy chunk * dk <= 4096 (LDS capacity).
+ * - Thread safety: calls are reentrant; concurrent calls on one stream run in
+ *   stream order, calls on different streams must not share output buffers.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+/* Storage type of q, k, v and o.  log_alpha, beta and every state are float32. */
+typedef enum { KDA_DTYPE_F32 = 0, KDA_DTYPE_BF16 = 1 } kda_dtype_t;
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_NULL = 1,          /* a required pointer is NULL                       */
+    KDA_ERR_SHAPE = 2,         /* a size is negative / zero where it must not be   */
+    KDA_ERR_DTYPE = 3,         /* unknown dtype enum                               */
+    KDA_ERR_ALIGN = 4,         /* a pointer is not 16-byte aligned                  */
+    KDA_ERR_UNSUPPORTED = 5,   /* dk / dv / chunk / plan outside the supported set  */
+    KDA_ERR_WORKSPACE = 6,     /* workspace missing or smaller than required        */
+    KDA_ERR_HIP = 7,           /* the HIP runtime reported an error                 */
+    KDA_ERR_ALIAS = 8          /* an output overlaps an input it must not alias     */
+} kda_status_t;
+
+/*
+ * Execution plan of kda_chunk_fwd.
+ *
+ * n_segments: split each sequence into this many token segments (each a whole
+ *   number of chunks).  1 = one sequential pass.  > 1 = the segment
+ *   decomposition of orkas.ai "Kimi K3 architecture", section "The cost comes
+ *   back in the serving stack": pass 1 builds every segment's (cumulative
+ *   transition, zero-start state) pair, a prefix scan gives each segment's
+ *   true start state, pass 2 reruns the segments in parallel from those.
+ * dv_block: value columns per workgroup, a multiple of 16 dividing dv.  The
+ *   recurrence is independent per state column, so column blocks run in
+ *   parallel; the shared per-chunk work (gates, WY transform) is repeated
+ *   per block.
+ * A zeroed plan (all fields 0) means "library default" for each field.
+ */
+typedef struct {
+    int32_t n_segments;
+    int32_t dv_block;
+} kda_plan_t;
+
+/* Fills *plan with the library's default for this problem on the current
+ * device (uses the device's compute-unit count).  Returns KDA_OK or an
+ * argument error.  Never launches work. */
+kda_status_t kda_chunk_fwd_default_plan(int64_t B, int64_t T, int32_t H, int32_t dk,
+                                        int32_t dv, int32_t chunk, kda_dtype_t dt,
+                                        kda_plan_t* plan);
+
+/* Device workspace, in bytes, that kda_chunk_fwd needs for this problem and
+ * plan (plan NULL = default plan).  0 when the plan has one segment. */
+kda_status_t kda_chunk_fwd_workspace_bytes(int64_t B, int64_t T, int32_t H, int32_t dk,
+                                           int32_t dv, int32_t chunk, kda_dtype_t dt,
+                                           const kda_plan_t* plan, size_t* bytes);
+
+/*
+ * Chunked prefill.
+ *
+ *   q, k       [B, T, H, dk]  dt
+ *   v          [B, T, H, dv]  dt
+ *   log_alpha  [B, T, H, dk]  float32 (values outside [-5, 0] are clamped)
+ *   beta       [B, T, H]      float32
+ *   S0         [B, H, dk, dv] float32 start state, or NULL for zeros
+ *   o          [B, T, H, dv]  dt, written
+ *   S_T        [B, H, dk, dv] float32 final state, written; may equal S0
+ *              (advance in place) but must not partially overlap it
+ *   chunk      tokens per chunk (16, 32 or 64); changes rounding, not the result
+ *   plan       NULL = default, else an explicit plan (see kda_plan_t)
+ *   workspace  device scratch of at least kda_chunk_fwd_workspace_bytes();
+ *              may be NULL when that size is 0.  Its contents are not needed
+ *              before or after the call.
+ *
+ * o must not overlap any input.  With T == 0 the call copies S0 (or zeros)
+ * into S_T and writes no o.
+ */
+kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v,
+                           const float* log_alpha, const float* beta, const float* S0,
+                           void* o, float* S_T,
+                           int64_t B, int64_t T, int32_t H, int32_t dk, int32_t dv,
+                           int32_t chunk, kda_dtype_t dt, const kda_plan_t* plan,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One recurrent decode step for N independent sequences, state updated in
+ * place (orkas.ai "Kimi K3 architecture", section "The cost comes back in the
+ * serving stack": the state is updated in place).  Equivalent to
+ * kda_chunk_fwd with T = 1 and S_T == S0.
+ *
+ *   state      [N, H, dk, dv] float32, read and overwritten
+ *   q, k       [N, H, dk]     dt
+ *   v          [N, H, dv]     dt
+ *   log_alpha  [N, H, dk]     float32
+ *   beta       [N, H]         float32
+ *   o          [N, H, dv]     dt, written; must not overlap state or inputs
+ */
+kda_status_t kda_decode_step(float* state, const void* q, const void* k, const void* v,
+                             const float* log_alpha, const float* beta, void* o,
+                             int64_t N, int32_t H, int32_t dk, int32_t dv, kda_dtype_t dt,
+                             void* stream);
+
+/* Static description of a status code. */
+const char* kda_status_str(kda_status_t status);
+
+/* Text of the last error recorded on the calling thread ("" if none). */
+const char* kda_last_error(void);
+
+/* KDA_ABI_VERSION of the loaded library. */
+int32_t kda_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

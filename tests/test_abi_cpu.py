@@ -1,0 +1,125 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects bad arguments with the documented codes before
+touching the HIP runtime (fake, never-dereferenced device addresses are used)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+LIBPATH = os.path.join(ROOT, "gated_delta_rule_107_amd", "libkda.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIBPATH), reason="libkda.so not built")
+
+OK, NULL, SHAPE, DTYPE, ALIGN, UNSUP, WS, HIP, ALIAS = range(9)
+F32, BF16 = 0, 1
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import gated_delta_rule_107_amd as g
+    return g.lib()
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert {"kda_chunk_fwd", "kda_decode_step", "kda_status_str", "kda_last_error"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.kda_abi_version() == 1
+    for code in range(9):
+        assert lib.kda_status_str(code).decode() not in ("", "unknown status")
+    assert lib.kda_status_str(99) == b"unknown status"
+
+
+# fake device addresses: 16-byte aligned, far apart, never dereferenced
+A = [0x10000000 * (i + 1) for i in range(12)]
+
+
+def call_chunk(lib, **kw):
+    import gated_delta_rule_107_amd as g
+    args = dict(q=A[0], k=A[1], v=A[2], la=A[3], beta=A[4], S0=None, o=A[6], S_T=A[7],
+                B=1, T=64, H=2, dk=16, dv=16, chunk=16, dt=F32, plan=g.Plan(1, 0), ws=None, wsb=0)
+    args.update(kw)
+    plan = ctypes.byref(args["plan"]) if args["plan"] is not None else None
+    return lib.kda_chunk_fwd(args["q"], args["k"], args["v"], args["la"], args["beta"], args["S0"], args["o"],
+                             args["S_T"], args["B"], args["T"], args["H"], args["dk"], args["dv"], args["chunk"],
+                             args["dt"], plan, args["ws"], args["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(o=None), NULL), (dict(S_T=None), NULL), (dict(beta=None), NULL),
+    (dict(B=0), SHAPE), (dict(H=0), SHAPE), (dict(T=-1), SHAPE),
+    (dict(dt=7), DTYPE),
+    (dict(dk=24), UNSUP), (dict(dv=256), UNSUP), (dict(chunk=128), UNSUP), (dict(chunk=8), UNSUP),
+    (dict(dk=128, chunk=64, dt=F32), UNSUP),
+    (dict(q=A[0] + 4), ALIGN), (dict(S_T=A[7] + 8), ALIGN),
+    (dict(o=A[0]), ALIAS), (dict(o=A[4] + 256), ALIAS), (dict(S_T=A[1]), ALIAS),
+    (dict(S0=A[7] + 16), ALIAS),
+])
+def test_chunk_fwd_rejects(lib, kw, code):
+    assert call_chunk(lib, **kw) == code
+    assert lib.kda_last_error().decode() != ""
+
+
+def test_chunk_fwd_plan_errors(lib):
+    import gated_delta_rule_107_amd as g
+    assert call_chunk(lib, plan=g.Plan(1, 24)) == UNSUP            # not a multiple of 16
+    assert call_chunk(lib, plan=g.Plan(1, 32)) == UNSUP            # does not divide dv=16
+    assert call_chunk(lib, plan=g.Plan(-1, 16)) == UNSUP
+    # segments need a workspace
+    r = call_chunk(lib, B=1, T=256, H=1, dk=32, dv=32, chunk=16, dt=BF16, plan=g.Plan(4, 32))
+    assert r == WS
+
+
+def test_plan_and_workspace_queries(lib):
+    import gated_delta_rule_107_amd as g
+    import torch
+    # one (b,h) per workgroup already covers 256 compute units: no segments
+    p = g.default_plan(8, 8192, 32, 128, 128, 64, torch.bfloat16)
+    assert p.n_segments == 1 and p.dv_block == 128
+    assert g.workspace_bytes(8, 8192, 32, 128, 128, 64, torch.bfloat16) == 0
+    # one long sequence: segments give the parallelism
+    p = g.default_plan(1, 1 << 20, 32, 128, 128, 64, torch.bfloat16)
+    assert p.n_segments >= 8
+    nb = g.workspace_bytes(1, 1 << 20, 32, 128, 128, 64, torch.bfloat16, p)
+    assert nb == 32 * p.n_segments * (2 * 128 * 128 + 128 * 128) * 4
+    # explicit plan is honoured; short sequences cap the number of segments
+    p = g.Plan(4, 64)
+    assert g.workspace_bytes(1, 1024, 2, 128, 128, 64, torch.bfloat16, p) == 2 * 4 * 3 * 128 * 128 * 4
+    p = g.default_plan(1, 64, 1, 128, 128, 64, torch.bfloat16)
+    assert p.n_segments == 1
+    with pytest.raises(g.KdaError) as e:
+        g.default_plan(1, 64, 1, 100, 128, 64, torch.bfloat16)
+    assert e.value.code == UNSUP
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(state=None), NULL), (dict(o=None), NULL), (dict(N=0), SHAPE), (dict(dt=3), DTYPE),
+    (dict(dk=48), UNSUP), (dict(q=A[1] + 2), ALIGN), (dict(o=A[0]), ALIAS), (dict(q=A[0] + 64), ALIAS),
+])
+def test_decode_step_rejects(lib, kw, code):
+    args = dict(state=A[0], q=A[1], k=A[2], v=A[3], la=A[4], beta=A[5], o=A[6], N=4, H=2, dk=16, dv=16, dt=BF16)
+    args.update(kw)
+    r = lib.kda_decode_step(args["state"], args["q"], args["k"], args["v"], args["la"], args["beta"], args["o"],
+                            args["N"], args["H"], args["dk"], args["dv"], args["dt"], None)
+    assert r == code
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import gated_delta_rule_107_amd as g
+    import torch
+    q = torch.zeros(1, 16, 1, 16)
+    with pytest.raises(g.KdaError):
+        g.chunk_fwd(q, q, q, q, torch.zeros(1, 16, 1))

@@ -1,0 +1,294 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 CPU oracle.
+
+Bar: relative Frobenius error (over the whole tensor, float64) <= 1e-4 for
+float32 inputs and <= 1.5e-2 for bf16 inputs, separately for o and S_T.
+Small cases are compared element by element over every output; the
+full-size workloads compare sampled (batch, head) slices the oracle can afford.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import kda_synth as ks
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 1.5e-2}
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def g():
+    import torch
+    assert torch.cuda.is_available()
+    import gated_delta_rule_107_amd as g
+    return g
+
+
+def dev_tensor(x, dtype):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x)).to(device="cuda", dtype=dtype)
+
+
+def to_np(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def run_prefill(g, x, dtype_name, chunk, plan=None, inplace=False):
+    import torch
+    dt = torch.bfloat16 if dtype_name == "bf16" else torch.float32
+    q, k, v = (dev_tensor(x[n], dt) for n in ("q", "k", "v"))
+    la = dev_tensor(x["log_alpha"], torch.float32)
+    beta = dev_tensor(x["beta"], torch.float32)
+    S0 = None if x["S0"] is None else dev_tensor(x["S0"], torch.float32)
+    if inplace:
+        assert S0 is not None
+        o, S_T = g.chunk_fwd(q, k, v, la, beta, S0, chunk=chunk, plan=plan, S_T=S0)
+    else:
+        o, S_T = g.chunk_fwd(q, k, v, la, beta, S0, chunk=chunk, plan=plan)
+    torch.cuda.synchronize()
+    return to_np(o), to_np(S_T)
+
+
+def check(o, S, o_ref, S_ref, tol, what):
+    eo, es = oracle.rel_fro(o, o_ref), oracle.rel_fro(S, S_ref)
+    _say(f"{what}: rel_fro o={eo:.3e} S_T={es:.3e} (tol {tol:g})")
+    assert np.isfinite(o).all() and np.isfinite(S).all()
+    assert eo <= tol and es <= tol, (what, eo, es)
+
+
+def small_recipe(dtype, B, T, H, dk, dv, chunk, **kw):
+    base = dict(loga="sig15", beta_std=1.0, s0_std=0.0, tag=ks.TAG_BASE + 100)
+    base.update(kw)
+    return ks.Recipe("test", B=B, T=T, H=H, dk=dk, dv=dv, chunk=chunk, dtype=dtype, **base)
+
+
+# ------------------------------------------------------------------ the tiny fp32 workload
+
+def test_tiny_fp32_workload(g):
+    r = ks.WORKLOADS[0]
+    _say("case: workload 0", r)
+    x = ks.make_prefill(r)
+    o, S = run_prefill(g, x, r.dtype, r.chunk, plan=g.Plan(1, 0))
+    o_ref, S_ref = oracle.kda_loop(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["S0"])
+    check(o, S, o_ref, S_ref, TOL["f32"], "workload 0 (one pass)")
+    o2, S2 = run_prefill(g, x, r.dtype, r.chunk)          # default plan (segments)
+    check(o2, S2, o_ref, S_ref, TOL["f32"], "workload 0 (default plan)")
+
+
+# ------------------------------------------------------------------ small shapes, every kernel variant
+
+SHAPES = [
+    # dtype, B, T, H, dk, dv, chunk
+    ("f32", 1, 100, 2, 16, 32, 16),
+    ("f32", 2, 77, 1, 32, 16, 32),
+    ("f32", 1, 130, 1, 64, 64, 64),
+    ("f32", 1, 90, 2, 128, 32, 32),
+    ("bf16", 1, 200, 2, 128, 128, 64),
+    ("bf16", 2, 150, 1, 64, 128, 64),
+    ("bf16", 1, 70, 3, 32, 64, 32),
+    ("bf16", 1, 45, 2, 16, 16, 16),
+    ("bf16", 1, 300, 1, 128, 64, 16),
+    ("bf16", 1, 129, 2, 128, 128, 32),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "-".join(map(str, s)))
+def test_small_shapes_one_pass(g, shape):
+    dtype, B, T, H, dk, dv, chunk = shape
+    r = small_recipe(dtype, B, T, H, dk, dv, chunk, s0_std=0.1)
+    _say("case:", shape)
+    x = ks.make_prefill(r)
+    o_ref, S_ref = oracle.kda_loop(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["S0"])
+    o, S = run_prefill(g, x, dtype, chunk, plan=g.Plan(1, 0))
+    check(o, S, o_ref, S_ref, TOL[dtype], f"{shape} one pass")
+    if dv >= 32:
+        o, S = run_prefill(g, x, dtype, chunk, plan=g.Plan(1, 16))      # 16-column blocks
+        check(o, S, o_ref, S_ref, TOL[dtype], f"{shape} dv_block=16")
+
+
+@pytest.mark.parametrize("shape", [("f32", 1, 200, 2, 32, 32, 16), ("bf16", 1, 500, 2, 128, 128, 64),
+                                   ("bf16", 2, 333, 1, 64, 64, 32), ("f32", 1, 64, 1, 16, 16, 16)],
+                         ids=lambda s: "-".join(map(str, s)))
+@pytest.mark.parametrize("nseg", [2, 3, 8])
+def test_segments(g, shape, nseg):
+    dtype, B, T, H, dk, dv, chunk = shape
+    r = small_recipe(dtype, B, T, H, dk, dv, chunk, s0_std=0.1)
+    _say("case: segments", nseg, shape)
+    x = ks.make_prefill(r)
+    o_ref, S_ref = oracle.kda_loop(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["S0"])
+    dvb = min(dv, dk)
+    o, S = run_prefill(g, x, dtype, chunk, plan=g.Plan(nseg, dvb))
+    check(o, S, o_ref, S_ref, TOL[dtype], f"{shape} {nseg} segments")
+
+
+def test_floor_stress_all_pinned(g):
+    """Every token at the floor: 16-token tiles at exactly -80, 64-token chunks at -320."""
+    r = small_recipe("bf16", 1, 256, 2, 128, 128, 64, loga="unif", pin_frac=1.0, beta_std=2.0)
+    x = ks.make_prefill(r)
+    assert (x["log_alpha"] == -5.0).all()
+    o_ref, S_ref = oracle.kda_loop(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["S0"])
+    o, S = run_prefill(g, x, "bf16", 64, plan=g.Plan(1, 0))
+    check(o, S, o_ref, S_ref, TOL["bf16"], "all tokens at the floor")
+    r32 = small_recipe("f32", 1, 128, 2, 64, 64, 64, loga="unif", pin_frac=1.0)
+    x = ks.make_prefill(r32)
+    o_ref, S_ref = oracle.kda_loop(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["S0"])
+    o, S = run_prefill(g, x, "f32", 64, plan=g.Plan(1, 0))
+    check(o, S, o_ref, S_ref, TOL["f32"], "all tokens at the floor (fp32)")
+
+
+def test_out_of_range_gates_are_clamped(g):
+    r = small_recipe("f32", 1, 96, 2, 32, 32, 32)
+    x = ks.make_prefill(r)
+    la = x["log_alpha"].copy()
+    la[:, ::3] = -9.0
+    la[:, 1::7] = 0.5
+    x["log_alpha"] = la
+    o_ref, S_ref = oracle.kda_loop(x["q"], x["k"], x["v"], la, x["beta"], x["S0"])
+    o, S = run_prefill(g, x, "f32", 32, plan=g.Plan(1, 0))
+    check(o, S, o_ref, S_ref, TOL["f32"], "clamped gates")
+
+
+def test_state_in_place_and_empty_sequence(g):
+    import torch
+    r = small_recipe("bf16", 2, 100, 2, 64, 64, 32, s0_std=0.2)
+    x = ks.make_prefill(r)
+    o_ref, S_ref = oracle.kda_loop(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["S0"])
+    for plan in (g.Plan(1, 0), g.Plan(3, 64)):
+        o, S = run_prefill(g, x, "bf16", 32, plan=plan, inplace=True)
+        check(o, S, o_ref, S_ref, TOL["bf16"], f"S_T aliases S0, {plan}")
+    # T = 0 copies the start state
+    S0 = dev_tensor(x["S0"], torch.float32)
+    e = torch.empty(2, 0, 2, 64, dtype=torch.bfloat16, device="cuda")
+    o, S_T = g.chunk_fwd(e, e, e, e.float(), torch.empty(2, 0, 2, device="cuda"), S0, chunk=32)
+    torch.cuda.synchronize()
+    assert o.shape == (2, 0, 2, 64) and torch.equal(S_T, S0)
+    o, S_T = g.chunk_fwd(e, e, e, e.float(), torch.empty(2, 0, 2, device="cuda"), None, chunk=32)
+    torch.cuda.synchronize()
+    assert (S_T == 0).all()
+
+
+def test_deterministic(g):
+    r = small_recipe("bf16", 1, 300, 4, 128, 128, 64, s0_std=0.1)
+    x = ks.make_prefill(r)
+    a = run_prefill(g, x, "bf16", 64, plan=g.Plan(3, 128))
+    b = run_prefill(g, x, "bf16", 64, plan=g.Plan(3, 128))
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# ------------------------------------------------------------------ decode
+
+@pytest.mark.parametrize("dtype,dk,dv", [("f32", 16, 16), ("f32", 32, 128), ("bf16", 128, 128),
+                                         ("bf16", 64, 32), ("bf16", 128, 16), ("f32", 128, 64)])
+def test_decode_small(g, dtype, dk, dv):
+    import torch
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    r = ks.Recipe("dec", B=5, T=1, H=3, dk=dk, dv=dv, chunk=16, dtype=dtype, loga="unif", s0_std=0.05,
+                  tag=ks.TAG_BASE + 200, steps=4)
+    d = ks.make_decode(r)
+    state = dev_tensor(d["state"], torch.float32)
+    S_ref = d["state"].astype(np.float64)
+    for s in range(r.steps):
+        o = g.decode_step(state, dev_tensor(d["q"][s], dt), dev_tensor(d["k"][s], dt), dev_tensor(d["v"][s], dt),
+                          dev_tensor(d["log_alpha"][s], torch.float32), dev_tensor(d["beta"][s], torch.float32))
+        o_ref, S_ref = oracle.kda_decode_step(S_ref, d["q"][s], d["k"][s], d["v"][s], d["log_alpha"][s], d["beta"][s])
+        torch.cuda.synchronize()
+        check(to_np(o), to_np(state), o_ref, S_ref, TOL[dtype] if dtype == "bf16" else 1e-5, f"decode step {s}")
+
+
+def test_decode_steps_equal_prefill(g):
+    """64 decode steps from a state == one prefill of the same 64 tokens from that state."""
+    import torch
+    r = ks.WORKLOADS[4].with_shape(B=8, H=4, steps=64)
+    d = ks.make_decode(r)
+    dt = torch.bfloat16
+    state = dev_tensor(d["state"], torch.float32)
+    outs = []
+    for s in range(64):
+        outs.append(g.decode_step(state, dev_tensor(d["q"][s], dt), dev_tensor(d["k"][s], dt),
+                                  dev_tensor(d["v"][s], dt), dev_tensor(d["log_alpha"][s], torch.float32),
+                                  dev_tensor(d["beta"][s], torch.float32)))
+    o_dec = torch.stack(outs, 1)
+    tr = lambda a: np.ascontiguousarray(np.swapaxes(a, 0, 1))  # noqa: E731
+    o_pre, S_pre = g.chunk_fwd(dev_tensor(tr(d["q"]), dt), dev_tensor(tr(d["k"]), dt), dev_tensor(tr(d["v"]), dt),
+                               dev_tensor(tr(d["log_alpha"]), torch.float32), dev_tensor(tr(d["beta"]), torch.float32),
+                               dev_tensor(d["state"], torch.float32), chunk=64)
+    torch.cuda.synchronize()
+    check(to_np(o_dec), to_np(state), to_np(o_pre), to_np(S_pre), 1e-2, "64 decode steps vs prefill(T=64)")
+
+
+# ------------------------------------------------------------------ full-size workloads
+
+def test_workload1_prefill_full(g):
+    """B=1 T=4096 H=16 dk=dv=128 chunk 64, bf16; default plan; every output checked."""
+    r = ks.WORKLOADS[1]
+    _say("case: workload 1 full", r)
+    x = ks.make_prefill(r)
+    o, S = run_prefill(g, x, "bf16", 64)
+    o_ref, S_ref = oracle.kda_chunked(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["S0"], chunk=64)
+    check(o, S, o_ref, S_ref, TOL["bf16"], "workload 1")
+
+
+def test_workload2_prefill_sampled(g):
+    """B=8 T=8192 H=32 with 25% of tokens pinned at the floor; GPU runs everything,
+    the oracle checks 6 sampled (batch, head) slices."""
+    import torch
+    r = ks.WORKLOADS[2]
+    _say("case: workload 2 full size", r)
+    x = ks.make_prefill(r)
+    o, S = run_prefill(g, x, "bf16", 64)
+    rng = np.random.default_rng(2)
+    for b, h in zip(rng.integers(0, r.B, 6), rng.integers(0, r.H, 6)):
+        sl = lambda a: a[b:b + 1, :, h:h + 1]  # noqa: E731
+        o_ref, S_ref = oracle.kda_chunked(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["log_alpha"]),
+                                          x["beta"][b:b + 1, :, h:h + 1], None, chunk=64)
+        check(o[b:b + 1, :, h:h + 1], S[b:b + 1, h:h + 1], o_ref, S_ref, TOL["bf16"], f"workload 2 (b={b}, h={h})")
+
+
+def test_workload4_decode_sampled(g):
+    """256 sequences x 32 heads, 64 steps in place; every o and the final state of
+    16 sampled sequences (all heads) checked against the oracle step by step."""
+    import torch
+    r = ks.WORKLOADS[4]
+    _say("case: workload 4 full size")
+    d = ks.make_decode(r)
+    dt = torch.bfloat16
+    state = dev_tensor(d["state"], torch.float32)
+    outs = []
+    for s in range(r.steps):
+        outs.append(to_np(g.decode_step(state, dev_tensor(d["q"][s], dt), dev_tensor(d["k"][s], dt),
+                                        dev_tensor(d["v"][s], dt), dev_tensor(d["log_alpha"][s], torch.float32),
+                                        dev_tensor(d["beta"][s], torch.float32))))
+    torch.cuda.synchronize()
+    o = np.stack(outs, 0)
+    sel = np.random.default_rng(4).choice(r.B, 16, replace=False)
+    S_ref = d["state"][sel].astype(np.float64)
+    o_ref = []
+    for s in range(r.steps):
+        os_, S_ref = oracle.kda_decode_step(S_ref, d["q"][s][sel], d["k"][s][sel], d["v"][s][sel],
+                                            d["log_alpha"][s][sel], d["beta"][s][sel])
+        o_ref.append(os_)
+    check(o[:, sel], to_np(state)[sel], np.stack(o_ref, 0), S_ref, TOL["bf16"], "workload 4 (16 sampled sequences)")
+
+
+def test_long_sequence_segments_sampled(g):
+    """The long-context shape (one sequence, 32 heads, dk=dv=128, chunk 64) at 1/16 of its
+    length: the default plan splits it into segments; 2 heads checked end to end."""
+    r = ks.WORKLOADS[3].with_shape(T=1 << 16)
+    _say("case: long sequence, T=65536")
+    x = ks.make_prefill(r)
+    p = g.default_plan(r.B, r.T, r.H, r.dk, r.dv, 64)
+    assert p.n_segments > 1
+    o, S = run_prefill(g, x, "bf16", 64)
+    for h in (0, 21):
+        sl = lambda a: a[:, :, h:h + 1]  # noqa: E731
+        o_ref, S_ref = oracle.kda_chunked(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["log_alpha"]),
+                                          x["beta"][:, :, h:h + 1], None, chunk=64)
+        check(o[:, :, h:h + 1], S[:, h:h + 1], o_ref, S_ref, TOL["bf16"], f"long sequence h={h} ({p})")
