@@ -1,0 +1,378 @@
+"""Benchmark of the KDA hot path on one MI355X (gfx950).
+
+    python bench.py [--steps K] [--warmup W] [--workload N] [--gpus 1]
+
+One step = one kda_chunk_fwd over the timed prefill workload with the
+library's default plan: gate prep, WY/UT transform, intra-chunk outputs and
+the inter-chunk state pass, plus the segment passes and prefix scan when the
+plan splits the sequence.  The default workload is the single-sequence
+prefill B=1, T=4096, H=16, dk=dv=128, chunk 64, bf16 q/k/v with float32 gates
+and state.  Inputs are seeded synthetic tensors already resident in HBM when
+the timed region starts.
+
+The same JSON line also carries the decode figure (256 sequences x 32 heads,
+128x128 float32 state, 64 consecutive in-place steps), the roofline of the
+dominant prefill kernel (algorithmic bytes per launch / its mean duration,
+taken from HIP events the library records around each launch on the stream
+the kernels run on), and the float64 CPU oracle timed on the host cores.
+
+Prints exactly one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import kda_synth as ks  # noqa: E402
+
+METRIC = "KDA prefill tokens/s (+% bf16 MFMA peak); decode steps/s (+% HBM GB/s)"
+PEAK_HBM_GBPS = 8000.0           # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2516.6        # MI355X dense bf16 MFMA
+PEAK_F32_MFMA_TFLOPS = 157.3     # MI355X dense fp32 MFMA
+DECODE_WORKLOAD = 4
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------- algorithmic work
+
+def prefill_flops_per_token_head(dk, dv, C):
+    """K~S, Q~S, K^T U (3 x 2 dk dv); causal A and M (~2 C dk); T V' and M U (2 (C+1) dv);
+    the triangular inverse (C^2 / 3).  Elementwise exps are not counted."""
+    return 6 * dk * dv + 2 * C * dk + 2 * (C + 1) * dv + C * C / 3.0
+
+
+def prefill_bytes_per_token_head(dk, dv, es):
+    """q, k, v, o in the storage dtype; log_alpha per channel and beta in float32."""
+    return 2 * dk * es + dv * es + 4 * dk + 4 + dv * es
+
+
+def launch_bytes(r, plan, es):
+    """Algorithmic HBM bytes of each kernel launch of one kda_chunk_fwd call, in launch order."""
+    B, T, H, dk, dv = r.B, r.T, r.H, r.dk, r.dv
+    st = B * H * dk * dv * 4
+    s0 = st if r.s0_std > 0 else 0
+    if plan.n_segments <= 1:
+        return [("chunk_kernel (one pass)", B * T * H * prefill_bytes_per_token_head(dk, dv, es) + s0 + st)]
+    P = plan.n_segments
+    seg_len = -(-(-(-T // r.chunk)) // P) * r.chunk
+    t1 = min(T, (P - 1) * seg_len)                                       # tokens pass 1 summarises
+    pair = B * H * (dk * dv + dk * dk) * 4
+    pass1 = B * t1 * H * (dk * es + dv * es + 4 * dk + 4) + (P - 1) * pair
+    scan = (P - 1) * pair + s0 + P * st
+    pass2 = B * T * H * prefill_bytes_per_token_head(dk, dv, es) + P * st + st
+    return [("chunk_kernel (segment pass 1)", pass1), ("scan_kernel", scan), ("chunk_kernel (pass 2)", pass2)]
+
+
+def decode_bytes_per_step(N, H, dk, dv, es):
+    """State read + write (float32), q, k, v, o in the storage dtype, log_alpha and beta float32."""
+    return N * H * (2 * dk * dv * 4 + 2 * dk * es + dv * es + 4 * dk + 4 + dv * es)
+
+
+# ----------------------------------------------------------------------------- CPU baseline (oracle)
+
+_CPU = {}
+
+
+def _oracle_prefill_head(h):
+    import oracle
+    x = _CPU["x"]
+    sl = lambda a: a[:, :, h:h + 1]  # noqa: E731
+    oracle.kda_chunked(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["log_alpha"]), x["beta"][:, :, h:h + 1],
+                       None if x["S0"] is None else x["S0"][:, h:h + 1], chunk=_CPU["chunk"])
+    return h
+
+
+def _oracle_decode_slice(i):
+    import oracle
+    d, sel = _CPU["d"], _CPU["slices"][i]
+    S = d["state"][sel].astype(np.float64)
+    for s in range(d["q"].shape[0]):
+        _, S = oracle.kda_decode_step(S, d["q"][s][sel], d["k"][s][sel], d["v"][s][sel],
+                                      d["log_alpha"][s][sel], d["beta"][s][sel])
+    return i
+
+
+def _pool_init():
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:
+        pass
+
+
+def _run_pool(fn, items, workers):
+    import multiprocessing as mp
+    ctx = mp.get_context("fork")
+    with ctx.Pool(workers, initializer=_pool_init) as pool:
+        t = time.perf_counter()
+        list(pool.imap_unordered(fn, items))
+        return time.perf_counter() - t
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.machine()
+
+
+def cpu_workers():
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def cpu_baseline_prefill(r, x):
+    """The oracle's chunked form over every head of the workload, repeated until about
+    10 s of CPU work; one process per core, BLAS single-threaded."""
+    _CPU.update(x=x, chunk=r.chunk)
+    workers = cpu_workers()
+    wall = _run_pool(_oracle_prefill_head, list(range(r.H)), workers)     # one full pass
+    reps = int(max(1, min(64, np.ceil(10.0 / max(wall * workers, 1e-3)))))
+    if reps > 1:
+        wall = _run_pool(_oracle_prefill_head, list(range(r.H)) * reps, workers)
+    tok = r.B * r.T * reps
+    return {"value": tok / wall, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "sample": f"whole workload (B={r.B} T={r.T} H={r.H}) x{reps}, float64 chunked form "
+                      f"(chunk {r.chunk}), one (b, h) per task", "seconds": wall,
+            "cpu_model": cpu_model()}
+
+
+def cpu_baseline_decode(rd, d, n_seq):
+    """The oracle's recurrent step over n_seq of the 256 sequences (all heads, all steps)."""
+    workers = cpu_workers()
+    seqs = np.arange(n_seq)
+    slices = [s for s in np.array_split(seqs, min(workers, n_seq)) if len(s)]
+    _CPU.update(d=d, slices=slices)
+    wall = _run_pool(_oracle_decode_slice, list(range(len(slices))), workers)
+    steps = d["q"].shape[0]
+    return {"value": steps * (n_seq / rd.B) / wall, "unit": "steps/s", "cores": workers, "kind": "oracle",
+            "sample": f"{n_seq} of {rd.B} sequences x {rd.H} heads x {steps} steps, scaled to the full batch",
+            "seconds": wall}
+
+
+# ----------------------------------------------------------------------------- GPU
+
+def make_events(torch, n):
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for e in evs:
+        e.record()          # creates the underlying hipEvent_t
+    torch.cuda.synchronize()
+    return evs
+
+
+def bench_prefill(g, torch, r, x, steps, warmup):
+    dev = torch.device("cuda:0")
+    dt = torch.bfloat16 if r.dtype == "bf16" else torch.float32
+    es = 2 if r.dtype == "bf16" else 4
+    T_ = lambda a, t: torch.from_numpy(np.ascontiguousarray(a)).to(dev, t)  # noqa: E731
+    q, k, v = T_(x["q"], dt), T_(x["k"], dt), T_(x["v"], dt)
+    la, beta = T_(x["log_alpha"], torch.float32), T_(x["beta"], torch.float32)
+    S0 = None if x["S0"] is None else T_(x["S0"], torch.float32)
+    plan = g.default_plan(r.B, r.T, r.H, r.dk, r.dv, r.chunk, dt)
+    nws = g.workspace_bytes(r.B, r.T, r.H, r.dk, r.dv, r.chunk, dt, plan)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    o = torch.empty((r.B, r.T, r.H, r.dv), dtype=dt, device=dev)
+    S_T = torch.empty((r.B, r.H, r.dk, r.dv), dtype=torch.float32, device=dev)
+    log(f"prefill {r.name}: plan {plan}, workspace {nws} B")
+
+    def step(p):
+        g.chunk_fwd(q, k, v, la, beta, S0, chunk=r.chunk, plan=p, o=o, S_T=S_T, workspace=ws)
+
+    for _ in range(warmup):
+        step(plan)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        step(plan)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+
+    # per-launch durations from events the library records around each launch
+    lb = launch_bytes(r, plan, es)
+    nl = len(lb)
+    evs = make_events(torch, 2 * nl * steps)
+    arrs = []
+    for i in range(steps):
+        arr = (ctypes.c_void_p * (2 * nl))(*[evs[2 * nl * i + j].cuda_event for j in range(2 * nl)])
+        arrs.append(arr)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        p = g.Plan(plan.n_segments, plan.dv_block, ctypes.cast(arrs[i], ctypes.POINTER(ctypes.c_void_p)), 2 * nl)
+        step(p)
+    torch.cuda.synchronize()
+    per_launch = []
+    for j, (name, nbytes) in enumerate(lb):
+        d = [evs[2 * nl * i + 2 * j].elapsed_time(evs[2 * nl * i + 2 * j + 1]) for i in range(steps)]
+        per_launch.append({"kernel": name, "ms": float(np.mean(d)), "bytes": int(nbytes),
+                           "GBps": nbytes / (np.mean(d) * 1e-3) / 1e9})
+    log("prefill per launch:", json.dumps(per_launch))
+    return ms, plan, per_launch
+
+
+def bench_decode(g, torch, rd, d, reps):
+    dev = torch.device("cuda:0")
+    dt = torch.bfloat16
+    T_ = lambda a, t: torch.from_numpy(np.ascontiguousarray(a)).to(dev, t)  # noqa: E731
+    pristine = T_(d["state"], torch.float32)
+    state = pristine.clone()
+    qs, ks_, vs = T_(d["q"], dt), T_(d["k"], dt), T_(d["v"], dt)
+    las, bs = T_(d["log_alpha"], torch.float32), T_(d["beta"], torch.float32)
+    o = torch.empty((rd.B, rd.H, rd.dv), dtype=dt, device=dev)
+    nsteps = qs.shape[0]
+
+    def run():
+        for s in range(nsteps):
+            g.decode_step(state, qs[s], ks_[s], vs[s], las[s], bs[s], o=o)
+
+    run()                                   # warm-up
+    times = []
+    for _ in range(reps):
+        state.copy_(pristine)               # restore (not timed)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        run()
+        t1.record()
+        torch.cuda.synchronize()
+        times.append(t0.elapsed_time(t1) / nsteps)
+    ms = float(np.median(times))
+    return ms, nsteps
+
+
+def copy_bandwidth(torch, nbytes=1 << 30, reps=10):
+    """Device-to-device copy of 1 GiB: the box's achievable-bandwidth reference (read + write)."""
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / reps
+    del a, b
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=1, choices=[0, 1, 2, 3],
+                    help="prefill workload (0 tiny fp32, 1 B1 T4096 H16, 2 B8 T8192 H32, 3 B1 T1M H32)")
+    ap.add_argument("--decode-reps", type=int, default=5)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: every workload runs on a single MI355X and no "
+              f"multi-GPU path is built (asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+
+    r = ks.WORKLOADS[args.workload]
+    rd = ks.WORKLOADS[DECODE_WORKLOAD]
+    t = time.perf_counter()
+    x = ks.make_prefill(r)
+    log(f"generated prefill inputs in {time.perf_counter() - t:.1f}s")
+    d = None
+    if not args.no_decode:
+        t = time.perf_counter()
+        d = ks.make_decode(rd)
+        log(f"generated decode inputs in {time.perf_counter() - t:.1f}s")
+
+    # CPU baseline first: the worker processes fork before the GPU is touched
+    cpu_pre = cpu_dec = None
+    if not args.no_cpu_baseline:
+        cpu_pre = cpu_baseline_prefill(r, x)
+        log("cpu baseline prefill:", json.dumps(cpu_pre))
+        if d is not None:
+            cpu_dec = cpu_baseline_decode(rd, d, 128)
+            log("cpu baseline decode:", json.dumps(cpu_dec))
+
+    import torch
+    import gated_delta_rule_107_amd as g
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    props = torch.cuda.get_device_properties(0)
+    log(f"device: {props.name} {getattr(props, 'gcnArchName', '')} CUs={props.multi_processor_count}")
+
+    ms, plan, per_launch = bench_prefill(g, torch, r, x, args.steps, args.warmup)
+    es = 2 if r.dtype == "bf16" else 4
+    token_heads = r.B * r.T * r.H
+    flops = token_heads * prefill_flops_per_token_head(r.dk, r.dv, r.chunk)
+    nbytes = token_heads * prefill_bytes_per_token_head(r.dk, r.dv, es)
+    sec = ms * 1e-3
+    peak_mf = PEAK_BF16_TFLOPS if r.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
+    dom = max(per_launch, key=lambda e: e["ms"])
+    roofline = {"bound": "hbm", "kernel": dom["kernel"], "achieved": round(dom["GBps"], 1),
+                "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(dom["GBps"] / PEAK_HBM_GBPS, 4),
+                "traffic": None, "launch_ms": round(dom["ms"], 5), "launch_bytes": dom["bytes"]}
+
+    dec = None
+    if d is not None:
+        dms, nsteps = bench_decode(g, torch, rd, d, args.decode_reps)
+        dbytes = decode_bytes_per_step(rd.B, rd.H, rd.dk, rd.dv, 2)
+        dgbps = dbytes / (dms * 1e-3) / 1e9
+        dec = {"workload": rd.name, "value": round(1e3 / dms, 2), "unit": "steps/s", "ms_per_step": round(dms, 5),
+               "steps_per_interval": nsteps,
+               "roofline": {"bound": "hbm", "kernel": "decode_kernel", "achieved": round(dgbps, 1),
+                            "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(dgbps / PEAK_HBM_GBPS, 4),
+                            "traffic": None, "launch_bytes": dbytes},
+               "cpu_baseline": cpu_dec}
+        log("decode:", json.dumps(dec))
+    copy_gbps = copy_bandwidth(torch)
+
+    out = {
+        "metric": METRIC,
+        "value": round(r.B * r.T / sec, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": r.dtype,
+        "data": "synthetic",
+        "config": {"workload": r.name, "B": r.B, "T": r.T, "H": r.H, "dk": r.dk, "dv": r.dv,
+                   "chunk": r.chunk, "plan": {"n_segments": plan.n_segments, "dv_block": plan.dv_block}},
+        "roofline": roofline,
+        "cpu_baseline": cpu_pre,
+        "prefill": {"mfma_frac_alg": round(flops / sec / (peak_mf * 1e12), 4),
+                    "hbm_frac_alg": round(nbytes / sec / (PEAK_HBM_GBPS * 1e9), 4),
+                    "roofline_frac": round(max(flops / (peak_mf * 1e12), nbytes / (PEAK_HBM_GBPS * 1e9)) / sec, 4),
+                    "alg_gflop": round(flops / 1e9, 3), "alg_mb": round(nbytes / 1e6, 2),
+                    "launches": per_launch},
+        "decode": dec,
+        "hbm_copy_GBps": round(copy_gbps, 1),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

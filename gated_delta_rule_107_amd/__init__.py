@@ -2,8 +2,9 @@
 
 Argument marshalling only: every step of the computation runs in the HIP
 kernels behind the C ABI declared in include/kda.h.  PyTorch supplies device
-memory and the current stream.  Importing this package loads libkda.so and
-fails loudly if it has not been built (``python -m gated_delta_rule_107_amd.build``).
+memory and the current stream.  libkda.so is loaded on the first call; every
+call raises ImportError if it has not been built
+(``python -m gated_delta_rule_107_amd.build``).  There is no fallback path.
 
     o, S_T = chunk_fwd(q, k, v, log_alpha, beta, S0=None, chunk=64)
     o      = decode_step(state, q, k, v, log_alpha, beta)      # state updated in place
@@ -33,7 +34,9 @@ class KdaError(RuntimeError):
 
 
 class Plan(ctypes.Structure):
-    _fields_ = [("n_segments", ctypes.c_int32), ("dv_block", ctypes.c_int32)]
+    """kda_plan_t: segmentation, column blocking and optional launch-timing events."""
+    _fields_ = [("n_segments", ctypes.c_int32), ("dv_block", ctypes.c_int32),
+                ("launch_events", ctypes.POINTER(ctypes.c_void_p)), ("n_launch_events", ctypes.c_int32)]
 
     def __repr__(self):
         return f"Plan(n_segments={self.n_segments}, dv_block={self.dv_block})"
@@ -63,7 +66,7 @@ def _load():
     return lib
 
 
-_lib = _load()
+_lib_handle = None
 
 
 def library_path() -> str:
@@ -71,13 +74,16 @@ def library_path() -> str:
 
 
 def lib() -> ctypes.CDLL:
-    """The loaded libkda.so (ctypes handle)."""
-    return _lib
+    """The loaded libkda.so (ctypes handle), loaded on first use; raises ImportError if it is not built."""
+    global _lib_handle
+    if _lib_handle is None:
+        _lib_handle = _load()
+    return _lib_handle
 
 
 def _check(code: int):
     if code != 0:
-        raise KdaError(code, _lib.kda_last_error().decode())
+        raise KdaError(code, lib().kda_last_error().decode())
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -112,14 +118,14 @@ def _stream(device) -> ctypes.c_void_p:
 def default_plan(B, T, H, dk, dv, chunk=64, dtype=torch.bfloat16) -> Plan:
     plan = Plan()
     code = DTYPE_BF16 if dtype == torch.bfloat16 else DTYPE_F32
-    _check(_lib.kda_chunk_fwd_default_plan(B, T, H, dk, dv, chunk, code, ctypes.byref(plan)))
+    _check(lib().kda_chunk_fwd_default_plan(B, T, H, dk, dv, chunk, code, ctypes.byref(plan)))
     return plan
 
 
 def workspace_bytes(B, T, H, dk, dv, chunk=64, dtype=torch.bfloat16, plan: Plan | None = None) -> int:
     n = ctypes.c_size_t(0)
     code = DTYPE_BF16 if dtype == torch.bfloat16 else DTYPE_F32
-    _check(_lib.kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk, code,
+    _check(lib().kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk, code,
                                               ctypes.byref(plan) if plan is not None else None,
                                               ctypes.byref(n)))
     return n.value
@@ -161,7 +167,7 @@ def chunk_fwd(q, k, v, log_alpha, beta, S0=None, chunk: int = 64, plan: Plan | N
             workspace = torch.empty(nws, dtype=torch.uint8, device=dev)
     else:
         workspace = None
-    code = _lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0),
+    code = lib().kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0),
                               _ptr(o), _ptr(S_T), B, T, H, dk, dv, chunk, dt,
                               ctypes.byref(plan) if plan is not None else None,
                               _ptr(workspace), nws, _stream(dev))
@@ -190,6 +196,6 @@ def decode_step(state, q, k, v, log_alpha, beta, o=None):
         o = torch.empty((N, H, dv), dtype=q.dtype, device=dev)
     else:
         _require(o, "o", q.dtype, (N, H, dv), dev)
-    _check(_lib.kda_decode_step(_ptr(state), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+    _check(lib().kda_decode_step(_ptr(state), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
                                 _ptr(o), N, H, dk, dv, dt, _stream(dev)))
     return o

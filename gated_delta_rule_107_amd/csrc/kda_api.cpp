@@ -74,7 +74,7 @@ struct Resolved {
 
 kda_status_t resolve_plan(int64_t B, int64_t T, int32_t H, int32_t dk, int32_t dv, int32_t chunk,
                           kda_dtype_t dt, const kda_plan_t* plan, Resolved* out) {
-    kda_plan_t p = plan ? *plan : kda_plan_t{0, 0};
+    kda_plan_t p = plan ? *plan : kda_plan_t{0, 0, nullptr, 0};
     int32_t dvb = p.dv_block;
     if (dvb == 0) dvb = dv;                                   // one column block per (b, h)
     if (dvb < 16 || dvb > 128 || dvb % 16 != 0 || dv % dvb != 0)
@@ -111,6 +111,21 @@ size_t workspace_for(int64_t B, int32_t H, int32_t dk, int32_t dv, const Resolve
     if (r.n_seg <= 1) return 0;
     return (size_t)B * H * r.n_seg * ((size_t)2 * dk * dv + (size_t)dk * dk) * sizeof(float);
 }
+
+// Records the caller's timing events around each kernel launch of one call.
+struct LaunchEvents {
+    void* const* ev;
+    int32_t n;
+    int32_t i;
+    hipStream_t st;
+    void before() {
+        if (ev && 2 * i + 1 < n) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(ev[2 * i]), st);
+    }
+    void after() {
+        if (ev && 2 * i + 1 < n) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(ev[2 * i + 1]), st);
+        ++i;
+    }
+};
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     if (!a || !b || na == 0 || nb == 0) return false;
@@ -206,6 +221,9 @@ kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v, const fl
     }
 
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (plan && plan->launch_events && plan->n_launch_events < 0)
+        return fail(KDA_ERR_UNSUPPORTED, "n_launch_events must be >= 0");
+    LaunchEvents tm{plan ? plan->launch_events : nullptr, plan ? plan->n_launch_events : 0, 0, st};
     kda::ChunkArgs a{};
     a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta;
     a.o = o; a.s_final = S_T;
@@ -216,7 +234,9 @@ kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v, const fl
     if (r.n_seg == 1) {
         a.mode = 0;
         a.s0 = S0;
+        tm.before();
         e = kda::launch_chunk(a, st);
+        tm.after();
         if (e != hipSuccess) return hip_fail(e, "chunk kernel launch");
         return KDA_OK;
     }
@@ -229,17 +249,23 @@ kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v, const fl
     a.mode = 1;
     a.s_loc = s_loc;
     a.m_tr = m_tr;
+    tm.before();
     e = kda::launch_chunk(a, st);
+    tm.after();
     if (e != hipSuccess) return hip_fail(e, "segment pass-1 launch");
     // prefix scan over the pairs
     kda::ScanArgs sc{S0, s_loc, m_tr, starts, B, H, dk, dv, r.n_seg};
+    tm.before();
     e = kda::launch_scan(sc, st);
+    tm.after();
     if (e != hipSuccess) return hip_fail(e, "segment scan launch");
     // pass 2: every segment from its true start state
     a.mode = 0;
     a.s0 = nullptr;
     a.starts = starts;
+    tm.before();
     e = kda::launch_chunk(a, st);
+    tm.after();
     if (e != hipSuccess) return hip_fail(e, "segment pass-2 launch");
     return KDA_OK;
 }

@@ -193,7 +193,8 @@ __device__ __forceinline__ void store_pair(float* p, float x, float y) {
 }
 
 // ---------------------------------------------------------------- the kernel
-template <typename OpT, int DK, int C>
+// MODE 0: outputs and final states; MODE 1: segment summaries (see ChunkArgs).
+template <typename OpT, int DK, int C, int MODE>
 __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
     using MF = Mf<OpT>;
     using frag = typename MF::frag;
@@ -237,9 +238,9 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
 
     // ---- which (batch, head, segment, column block) this workgroup owns
     const int H = a.H, dv = a.dv;
-    const int ncols = a.mode == 0 ? dv : dv + DK;
+    const int ncols = MODE == 0 ? dv : dv + DK;
     const int ncb = ncols / DVB;
-    const int nseg_grid = a.mode == 0 ? a.n_seg : a.n_seg - 1;
+    const int nseg_grid = MODE == 0 ? a.n_seg : a.n_seg - 1;
     int64_t bid = blockIdx.x;
     const int cb = (int)(bid % ncb);
     bid /= ncb;
@@ -253,9 +254,9 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
     const int64_t t_end = t_begin + a.seg_len < T ? t_begin + a.seg_len : T;
 
     const int colw = cb * DVB + 16 * wave;           // first (virtual) column of this wave
-    const bool mcols = a.mode == 1 && colw >= dv;    // wave holds transition columns
-    const bool blk_mcols = a.mode == 1 && cb * DVB >= dv;
-    const bool want_o = a.mode == 0;
+    const bool mcols = MODE == 1 && colw >= dv;    // wave holds transition columns
+    const bool blk_mcols = MODE == 1 && cb * DVB >= dv;
+    const bool want_o = MODE == 0;
     const int g4 = 4 * (lane >> 4), jl = lane & 15;
 
     const OpT* gq = reinterpret_cast<const OpT*>(a.q);
@@ -273,7 +274,7 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
         const float* src = nullptr;
         int64_t ld = dv;
         int col = colw + jl;
-        if (a.mode == 0) {
+        if (MODE == 0) {
             // with segments every start (segment 0's included) comes from the scan's
             // output, so S0 is never read here while another workgroup writes S_T
             if (a.n_seg == 1) src = a.s0 ? a.s0 + bh * DK * dv : nullptr;
@@ -552,7 +553,7 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
         float* dst = nullptr;
         int64_t ld = 0;
         int col = colw + jl;
-        if (a.mode == 0) {
+        if (MODE == 0) {
             if (seg == a.n_seg - 1) { dst = a.s_final + bh * DK * dv; ld = dv; }
         } else if (!mcols) {
             dst = a.s_loc + (bh * a.n_seg + seg) * DK * dv; ld = dv;
@@ -574,10 +575,10 @@ size_t chunk_lds_bytes(bool bf16_, int dk, int chunk, int dv_block) {
     return (size_t)lds_layout(E, KS, dk, chunk, dv_block).total;
 }
 
-template <typename OpT, int DK, int C>
-static hipError_t launch_chunk_t(const ChunkArgs& a, hipStream_t st) {
+template <typename OpT, int DK, int C, int MODE>
+static hipError_t launch_chunk_m(const ChunkArgs& a, hipStream_t st) {
     const size_t lds = chunk_lds_bytes(sizeof(OpT) == 2, DK, C, a.dv_block);
-    auto kern = chunk_kernel<OpT, DK, C>;
+    auto kern = chunk_kernel<OpT, DK, C, MODE>;
     static bool attr_set = false;   // per instantiation; the attribute is device-independent
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds > 65536 ? 163840 : 65536);
@@ -590,6 +591,11 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, hipStream_t st) {
     if (nblk <= 0) return hipSuccess;
     hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(64 * (a.dv_block / 16)), lds, st, a);
     return hipGetLastError();
+}
+
+template <typename OpT, int DK, int C>
+static hipError_t launch_chunk_t(const ChunkArgs& a, hipStream_t st) {
+    return a.mode == 0 ? launch_chunk_m<OpT, DK, C, 0>(a, st) : launch_chunk_m<OpT, DK, C, 1>(a, st);
 }
 
 template <typename OpT, int DK>

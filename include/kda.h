@@ -76,11 +76,19 @@ typedef enum {
  *   recurrence is independent per state column, so column blocks run in
  *   parallel; the shared per-chunk work (gates, WY transform) is repeated
  *   per block.
- * A zeroed plan (all fields 0) means "library default" for each field.
+ * A zeroed plan (all fields 0 / NULL) means "library default" for each field.
  */
 typedef struct {
     int32_t n_segments;
     int32_t dv_block;
+    /* Optional launch timing, for profilers and benchmarks (NULL = off).  An
+     * array of n_launch_events hipEvent_t handles, created by the caller.
+     * Kernel launch i of the call (i = 0, 1, ... in launch order: one launch
+     * with one segment; pass 1, scan, pass 2 with several) records
+     * launch_events[2i] just before it and launch_events[2i+1] just after it
+     * on `stream`; launches beyond the array's capacity record nothing. */
+    void* const* launch_events;
+    int32_t n_launch_events;
 } kda_plan_t;
 
 /* Fills *plan with the library's default for this problem on the current
