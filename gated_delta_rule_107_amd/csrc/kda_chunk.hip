@@ -2,278 +2,349 @@
 //
 // Each workgroup owns one (batch, head, segment, column block) and walks its
 // chunks of C tokens in order.  Per chunk, with Gamma the inclusive cumulative
-// sum of the floored log-decay g and S the start state:
+// sum of the floored log-decay g from the chunk start and S the start state:
 //
+//   A[t,s] = sum_c k_tc k_sc e^(Gamma_tc - Gamma_sc)   (s <  t)
+//   M[t,s] = sum_c q_tc k_sc e^(Gamma_tc - Gamma_sc)   (s <= t)
 //   U  = (I + Diag(beta) A)^-1 Diag(beta) (V - (k e^Gamma) S)          (WY/UT form)
 //   O  = (q e^Gamma) S + M U
 //   S' = Diag(e^Gamma_C) S + (k e^(Gamma_C - Gamma))^T U
-//   A[t,s] = sum_c k_tc k_sc e^(Gamma_tc - Gamma_sc)  (s < t),  M likewise with q (s <= t)
 //
 // Chunked evaluation has to divide by a cumulative decay; the floor on the
 // log-decay bounds a 16-token tile's cumulative log-decay to [-80, 0], so its
 // reciprocal stays below e^80 ~ 5.5e34, inside bf16, and the diagonal tiles
-// can run as the same dense matrix products as every other tile (orkas.ai
-// "Kimi K3 architecture", section "The floor that removed a GPU code path").
+// run as the same dense matrix products as every other tile (orkas.ai "Kimi
+// K3 architecture", section "The floor that removed a GPU code path").
 //
-// Sub-tile factorisation used here.  Let t lie in 16-token sub-tile p of the
-// chunk, gamma_t the inclusive cumulative log-decay inside that sub-tile
-// (in [-80, 0]), tot_p its total and r_p = tot_0 + ... + tot_{p-1}.  Then
-//   k_t e^Gamma_t           = [k_t e^gamma_t] e^r_p                (KL, <= 1)
-//   e^(Gamma_t - Gamma_s)   = [e^gamma_t] f_pp' [e^(tot_p' - gamma_s)]
-// with f_pp = e^-tot_p (<= e^80, the diagonal tile) and f_pp' = e^(r_p -
-// r_p'+1) (<= 1) for p' < p.  So A and M tiles are (KL or QL) Diag(f) RH^T
-// with both stored operands bounded by 1; the per-channel factor f is applied
-// to the left operand in registers.  e^r_p is folded into the state operand:
-// (k e^Gamma) S = KL (Diag(e^r_p) S).
+// Reference points.  Let t lie in 16-token sub-tile p of the chunk, gamma_t
+// the inclusive cumulative log-decay inside that sub-tile, tot_p its total,
+// r_p = tot_0 + ... + tot_{p-1}, so Gamma_t = r_p + gamma_t.  Stored operands:
+//   KL = k e^gamma, QL = q e^gamma, RH = k e^(tot_p - gamma)       (all <= 1)
+//   Kt = KL e^(r_p) = k e^Gamma, Qt = q e^Gamma                    (<= 1, may flush to 0)
+//   KhT = (k e^(Gamma_C - Gamma))^T                                (<= 1)
+// A and M tiles are (KL or QL) Diag(f) RH^T with f = e^-tot_p (<= e^80, the
+// diagonal tile), f = 1 for adjacent sub-tiles and f = e^(r_p - r_pp+1) (<= 1)
+// further below; f is applied to the left operand in registers.
 //
-// Matrix products run on MFMA: v_mfma_f32_16x16x32_bf16 for bf16 inputs,
-// v_mfma_f32_16x16x4_f32 for float32 inputs.  The state stays in fp32 MFMA
-// accumulators for the whole sequence; each wave owns 16 state columns
-// (the recurrence is independent per column).  MFMA outputs (V - X, U) feed
-// the next MFMA straight from registers: the contraction index of the next
-// product is taken in the order the accumulator layout holds it, and the
-// other operand is loaded from LDS in that same order ("chained" order).
-// The triangular solve runs in fp32 (diagonal 16x16 blocks by forward
-// substitution, off-diagonal blocks level by level).
+// Per chunk: (1) gate prep from registers prefetched one chunk ahead, writing
+// the operands above to LDS; (2) A / M tiles on MFMA and X = Kt S, QS = Qt S;
+// (3) the four 16x16 diagonal blocks of (I + Diag(beta) A) inverted by fp32
+// forward substitution; (4) the state chain, per wave on its 16 state columns:
+// the block triangular solve for U runs on MFMA straight from registers
+// (U_p = N_pp (R_p - sum_q Ab_pq U_q)), then O and the state update.  The
+// fp32 state stays in MFMA accumulators for the whole sequence; accumulator
+// tiles feed the next product's B operand directly (the contraction index is
+// taken in the order the accumulator layout holds it, and the LDS operand is
+// read in that same order).
+//
+// bf16 inputs use v_mfma_f32_16x16x32_bf16 / v_mfma_f32_16x16x16_bf16 with
+// fp32 accumulation; float32 inputs use v_mfma_f32_16x16x4_f32 throughout.
 #include "kda_device.h"
 #include "kda_internal.h"
 
 namespace kda {
 
-// ---------------------------------------------------------------- MFMA operand policies
-// Accumulator layout (both instructions): lane l holds C[4*(l/16) + r][l % 16], r = 0..3.
-template <typename OpT> struct Mf;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
 
-template <> struct Mf<bf16> {
-    static constexpr int KS = 32;          // contraction length per instruction
-    typedef bf16x8 frag;
-    static __device__ __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-    }
-    // natural order: lane (m = l%16, g = l/16) holds X[r0 + m][k0 + 8g + j], j < 8
-    static __device__ __forceinline__ frag ld_nat(const bf16* X, int ld, int r0, int k0, int lane) {
-        return *reinterpret_cast<const frag*>(X + (r0 + (lane & 15)) * ld + k0 + 8 * (lane >> 4));
-    }
-    // chained order for step s: slot j<4 -> k = 32s + 4g + j, slot 4+j -> k = 32s + 16 + 4g + j,
-    // i.e. rows 4g..4g+3 of accumulator tiles 2s and 2s+1
-    static __device__ __forceinline__ frag ld_chain(const bf16* X, int ld, int r0, int s, int lane) {
-        const bf16* p = X + (r0 + (lane & 15)) * ld + 32 * s + 4 * (lane >> 4);
-        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(p);
-        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 16);
-        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    }
-    template <int NTILE>
-    static __device__ __forceinline__ frag b_chain(const f32x4 (&t)[NTILE], int s) {
-        frag f;
+// ---------------------------------------------------------------- MFMA policies
+// Accumulator layout (every 16x16 instruction here): lane l holds C[4*(l/16) + r][l % 16].
+template <typename OpT> struct MM;
+
+template <> struct MM<bf16> {
+    static constexpr int KS = 32;                  // contraction per natural-order instruction
+    typedef bf16x4 B16;                            // B operand for a 16-deep contraction
+    static __device__ __forceinline__ B16 b16(const f32x4& x) {
+        B16 r;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            f[j] = (bf16)(2 * s < NTILE ? t[2 * s][j] : 0.f);
-            f[4 + j] = (bf16)(2 * s + 1 < NTILE ? t[2 * s + 1][j] : 0.f);
-        }
-        return f;
-    }
-    // scale a natural-order fragment by per-k factors fac[k0 + 8g + j]
-    static __device__ __forceinline__ frag scale_nat(frag a, const float* fac, int k0, int lane) {
-        const f32x4* f4 = reinterpret_cast<const f32x4*>(fac + k0 + 8 * (lane >> 4));
-        const f32x4 lo = f4[0], hi = f4[1];
-        frag r;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            r[j] = (bf16)((float)a[j] * lo[j]);
-            r[4 + j] = (bf16)((float)a[4 + j] * hi[j]);
-        }
+        for (int j = 0; j < 4; ++j) r[j] = (bf16)x[j];
         return r;
     }
-    static constexpr int steps(int K) { return (K + KS - 1) / KS; }
+    // acc += A[r0 + m][c0 + kk] * B[kk][n] over kk < 16, B given as an accumulator-layout
+    // tile (rows kk = 4g + j held by lane group g)
+    static __device__ __forceinline__ f32x4 k16(const bf16* A, int ld, int r0, int c0, B16 b, f32x4 acc,
+                                                int lane) {
+        const bf16x4 a = *reinterpret_cast<const bf16x4*>(A + (r0 + (lane & 15)) * ld + c0 + 4 * (lane >> 4));
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
+                                                         __builtin_bit_cast(i16x4, b), acc, 0, 0, 0);
+    }
+    // the same over 32 contraction rows given as two tiles (rows c0.. and c0+16..)
+    static __device__ __forceinline__ f32x4 k32(const bf16* A, int ld, int r0, int c0, B16 b0, B16 b1,
+                                                f32x4 acc, int lane) {
+        const bf16* p = A + (r0 + (lane & 15)) * ld + c0 + 4 * (lane >> 4);
+        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(p);
+        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 16);
+        const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8 b = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+    }
+    // natural order, both operands in LDS:
+    // acc += (A[ra + m][k0 + kk] * fac[k0 + kk]) * Bm[rb + n][k0 + kk] over kk < 32
+    static __device__ __forceinline__ f32x4 nat(const bf16* A, int lda, int ra, const bf16* Bm, int ldb,
+                                                int rb, int k0, const float* fac, f32x4 acc, int lane) {
+        bf16x8 a = *reinterpret_cast<const bf16x8*>(A + (ra + (lane & 15)) * lda + k0 + 8 * (lane >> 4));
+        if (fac) {
+            const f32x4* f4 = reinterpret_cast<const f32x4*>(fac + k0 + 8 * (lane >> 4));
+            const f32x4 lo = f4[0], hi = f4[1];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                a[j] = (bf16)((float)a[j] * lo[j]);
+                a[4 + j] = (bf16)((float)a[4 + j] * hi[j]);
+            }
+        }
+        const bf16x8 b = *reinterpret_cast<const bf16x8*>(Bm + (rb + (lane & 15)) * ldb + k0 + 8 * (lane >> 4));
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+    }
 };
 
-template <> struct Mf<float> {
+template <> struct MM<float> {
     static constexpr int KS = 4;
-    typedef float frag;
-    static __device__ __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
-        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    typedef f32x4 B16;
+    static __device__ __forceinline__ B16 b16(const f32x4& x) { return x; }
+    // four v_mfma_f32_16x16x4_f32: step s contracts rows 4g + s (g = lane group)
+    static __device__ __forceinline__ f32x4 k16(const float* A, int ld, int r0, int c0, B16 b, f32x4 acc,
+                                                int lane) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(A + (r0 + (lane & 15)) * ld + c0 + 4 * (lane >> 4));
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc, 0, 0, 0);
+        return acc;
     }
-    // natural order: lane (m, g) holds X[r0 + m][k0 + g]
-    static __device__ __forceinline__ frag ld_nat(const float* X, int ld, int r0, int k0, int lane) {
-        return X[(r0 + (lane & 15)) * ld + k0 + (lane >> 4)];
+    static __device__ __forceinline__ f32x4 k32(const float* A, int ld, int r0, int c0, B16 b0, B16 b1,
+                                                f32x4 acc, int lane) {
+        acc = k16(A, ld, r0, c0, b0, acc, lane);
+        return k16(A, ld, r0, c0 + 16, b1, acc, lane);
     }
-    // chained order for step s: k = 16*(s/4) + 4g + s%4, i.e. row 4g + s%4 of accumulator tile s/4
-    static __device__ __forceinline__ frag ld_chain(const float* X, int ld, int r0, int s, int lane) {
-        return X[(r0 + (lane & 15)) * ld + 16 * (s >> 2) + 4 * (lane >> 4) + (s & 3)];
+    static __device__ __forceinline__ f32x4 nat(const float* A, int lda, int ra, const float* Bm, int ldb,
+                                                int rb, int k0, const float* fac, f32x4 acc, int lane) {
+        float a = A[(ra + (lane & 15)) * lda + k0 + (lane >> 4)];
+        if (fac) a *= fac[k0 + (lane >> 4)];
+        const float b = Bm[(rb + (lane & 15)) * ldb + k0 + (lane >> 4)];
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
     }
-    template <int NTILE>
-    static __device__ __forceinline__ frag b_chain(const f32x4 (&t)[NTILE], int s) {
-        return t[s >> 2][s & 3];
+};
+
+// ---------------------------------------------------------------- cross-lane helpers
+// Within 16-lane rows: value of lane (i - N) (0 for the first N lanes of the row).
+template <int N> __device__ __forceinline__ float row_shr(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x110 | N, 0xF, 0xF, true));
+}
+// Within 16-lane rows: value of lane (i + N) (0 for the last N lanes of the row).
+template <int N> __device__ __forceinline__ float row_shl(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x100 | N, 0xF, 0xF, true));
+}
+// Within groups of 4 lanes: lane selector pattern (2 bits per lane).
+template <int PAT> __device__ __forceinline__ float quad_perm(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), PAT, 0xF, 0xF, true));
+}
+
+// ---------------------------------------------------------------- element access
+template <typename OpT> struct Ld4;             // 4 consecutive elements <-> float[4]
+template <> struct Ld4<bf16> {
+    typedef bf16x4 V;
+    static __device__ __forceinline__ void to_f(const V& v, float (&x)[4]) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = (float)v[e];
     }
-    static __device__ __forceinline__ frag scale_nat(frag a, const float* fac, int k0, int lane) {
-        return a * fac[k0 + (lane >> 4)];
+    static __device__ __forceinline__ V from_f(const float (&x)[4]) {
+        V v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (bf16)x[e];
+        return v;
     }
-    static constexpr int steps(int K) { return K / KS; }
+    static __device__ __forceinline__ V zero() { return from_f({0.f, 0.f, 0.f, 0.f}); }
+};
+template <> struct Ld4<float> {
+    typedef f32x4 V;
+    static __device__ __forceinline__ void to_f(const V& v, float (&x)[4]) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = v[e];
+    }
+    static __device__ __forceinline__ V from_f(const float (&x)[4]) { return V{x[0], x[1], x[2], x[3]}; }
+    static __device__ __forceinline__ V zero() { return V{0.f, 0.f, 0.f, 0.f}; }
 };
 
 // ---------------------------------------------------------------- LDS layout
+// bf16 operands (RV): the A / M tiles take their decay factors on the right operand, which
+// is stored in one variant per distance between the sub-tiles (RD for the diagonal, RH for
+// adjacent sub-tiles, RF for two and three apart).  float32 operands instead scale the left
+// operand in registers by per-channel factors (fd, fo), which keeps their LDS footprint small.
 struct Lds {
-    int kl, ql, rh, tinv, kht, abuf, tb, mb, vb, lp;
-    int tot, rr, er, fp, fd, fo, egc, beta, total;
+    int kt, qt, kl, ql, rh, rd, rf, kht, an, mm, ad, fd, fo, egc, beta, total;
 };
 
 __host__ __device__ constexpr int align16(int x) { return (x + 15) & ~15; }
 
-// E: bytes per operand element; KS: MFMA contraction length
-__host__ __device__ constexpr Lds lds_layout(int E, int KS, int DK, int C, int DVB) {
+// E: bytes per operand element
+__host__ __device__ constexpr Lds lds_layout(int E, int DK, int C) {
+    const bool RV = E == 2;
     const int PADE = 16 / E;
     const int NT = C / 16;
-    const int LDK = (DK > KS ? DK : KS) + PADE;
-    const int LC = (C > KS ? C : KS) + PADE;
-    const int LCA = C + 4;
-    const int LV = DVB + PADE;
-    const int FK = DK > KS ? DK : KS;          // factor row length (padded for DK < KS)
-    const int NPAIR = NT * (NT - 1) / 2;
+    const int DKP = DK < 32 ? 32 : DK;            // bf16 natural loads read 32 channels at a time
+    const int LDK = DKP + PADE;
+    const int LC = C + PADE;
     Lds L{};
     int off = 0;
+    L.kt = off;   off += align16(C * LDK * E);
+    L.qt = off;   off += align16(C * LDK * E);
     L.kl = off;   off += align16(C * LDK * E);
     L.ql = off;   off += align16(C * LDK * E);
-    L.rh = off;   L.tinv = off;
-    {
-        const int a = align16(C * LDK * E), b = align16(C * LCA * 4);
-        off += a > b ? a : b;
-    }
-    L.kht = off;  off += align16(FK * LC * E);
-    L.abuf = off; off += align16(C * LCA * 4);
-    L.tb = off;   off += align16(C * LC * E);
-    L.mb = off;   off += align16(C * LC * E);
-    L.vb = off;   off += align16(C * LV * E);
-    L.lp = off;   off += align16((NPAIR > 0 ? NPAIR : 1) * 256 * 4);
-    L.tot = off;  off += align16(NT * FK * 4);
-    L.rr = off;   off += align16((NT + 1) * FK * 4);
-    L.er = off;   off += align16(NT * FK * 4);
-    L.fp = off;   off += align16(NT * FK * 4);
-    L.fd = off;   off += align16(NT * FK * 4);
-    L.fo = off;   off += align16((NPAIR > 0 ? NPAIR : 1) * FK * 4);
-    L.egc = off;  off += align16(FK * 4);
+    L.rh = off;   off += align16(C * LDK * E);
+    L.rd = off;   off += RV ? align16(C * LDK * E) : 0;
+    L.rf = off;   off += (RV && NT == 4) ? align16(48 * LDK * E) : 0;
+    L.kht = off;  off += align16(DK * LC * E);
+    L.an = off;   off += align16(C * LC * E);
+    L.mm = off;   off += align16(C * LC * E);
+    L.ad = off;   off += align16(NT * 16 * 16 * 4);
+    L.fd = off;   off += RV ? 0 : align16(NT * DKP * 4);
+    L.fo = off;   off += RV ? 0 : align16(3 * DKP * 4);
+    L.egc = off;  off += align16(DKP * 4);
     L.beta = off; off += align16(C * 4);
     L.total = off;
     return L;
 }
 
-__device__ __forceinline__ int pair_index(int p, int pp) { return p * (p - 1) / 2 + pp; }   // pp < p
-
-// store 16 consecutive values (converted) at dst (16-byte aligned)
-__device__ __forceinline__ void store16(bf16* dst, const float (&x)[16]) {
-    bf16x8 a, b;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        a[j] = (bf16)x[j];
-        b[j] = (bf16)x[8 + j];
-    }
-    reinterpret_cast<bf16x8*>(dst)[0] = a;
-    reinterpret_cast<bf16x8*>(dst)[1] = b;
-}
-__device__ __forceinline__ void store16(float* dst, const float (&x)[16]) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        reinterpret_cast<f32x4*>(dst)[j] = f32x4{x[4 * j], x[4 * j + 1], x[4 * j + 2], x[4 * j + 3]};
-}
-
-__device__ __forceinline__ void load_pair(const bf16* p, float& x, float& y) {
-    const bf16x2 v = *reinterpret_cast<const bf16x2*>(p);
-    x = (float)v[0];
-    y = (float)v[1];
-}
-__device__ __forceinline__ void load_pair(const float* p, float& x, float& y) {
-    const float2 v = *reinterpret_cast<const float2*>(p);
-    x = v.x;
-    y = v.y;
-}
-__device__ __forceinline__ void store_pair(bf16* p, float x, float y) {
-    *reinterpret_cast<bf16x2*>(p) = bf16x2{(bf16)x, (bf16)y};
-}
-__device__ __forceinline__ void store_pair(float* p, float x, float y) {
-    *reinterpret_cast<float2*>(p) = make_float2(x, y);
+__host__ __device__ constexpr int pair_fo_index(int p, int pp) {   // p - pp >= 2, p <= 3
+    return p == 2 ? 0 : (pp == 0 ? 1 : 2);                          // (2,0) (3,0) (3,1)
 }
 
 // ---------------------------------------------------------------- the kernel
 // MODE 0: outputs and final states; MODE 1: segment summaries (see ChunkArgs).
 template <typename OpT, int DK, int C, int MODE>
 __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
-    using MF = Mf<OpT>;
-    using frag = typename MF::frag;
+    using MF = MM<OpT>;
+    using B16 = typename MF::B16;
+    using L4 = Ld4<OpT>;
+    using V4 = typename L4::V;
     constexpr int E = sizeof(OpT);
-    constexpr int KS = MF::KS;
+    constexpr bool RV = E == 2;
     constexpr int PADE = 16 / E;
     constexpr int NT = C / 16;                       // 16-token sub-tiles per chunk
     constexpr int NCT = DK / 16;                     // 16-row tiles of the state
-    constexpr int LDK = (DK > KS ? DK : KS) + PADE;
-    constexpr int LC = (C > KS ? C : KS) + PADE;
-    constexpr int LCA = C + 4;
-    constexpr int FK = DK > KS ? DK : KS;
-    constexpr int NPAIR = NT * (NT - 1) / 2;
-    constexpr int SK_DK = MF::steps(DK);             // MFMA steps over the key dimension
-    constexpr int SK_C = MF::steps(C);               // MFMA steps over the chunk
+    constexpr int DKP = DK < 32 ? 32 : DK;
+    constexpr int LDK = DKP + PADE;
+    constexpr int LC = C + PADE;
+    constexpr int KNAT = (E == 2) ? (DK + 31) / 32 : DK / 4;   // natural-order steps over channels
+    constexpr bool want_o = MODE == 0;
+    constexpr Lds L = lds_layout(E, DK, C);
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int NTH = blockDim.x;
-    const int DVB = a.dv_block;
-    const int LV = DVB + PADE;
-    const Lds L = lds_layout(E, KS, DK, C, DVB);
+    OpT* s_kt = reinterpret_cast<OpT*>(smem + L.kt);
+    OpT* s_qt = reinterpret_cast<OpT*>(smem + L.qt);
     OpT* s_kl = reinterpret_cast<OpT*>(smem + L.kl);
     OpT* s_ql = reinterpret_cast<OpT*>(smem + L.ql);
     OpT* s_rh = reinterpret_cast<OpT*>(smem + L.rh);
-    float* s_tinv = reinterpret_cast<float*>(smem + L.tinv);
+    OpT* s_rd = reinterpret_cast<OpT*>(smem + L.rd);
+    OpT* s_rf = reinterpret_cast<OpT*>(smem + L.rf);
     OpT* s_kht = reinterpret_cast<OpT*>(smem + L.kht);
-    float* s_abuf = reinterpret_cast<float*>(smem + L.abuf);
-    OpT* s_tb = reinterpret_cast<OpT*>(smem + L.tb);
-    OpT* s_mb = reinterpret_cast<OpT*>(smem + L.mb);
-    OpT* s_vb = reinterpret_cast<OpT*>(smem + L.vb);
-    float* s_lp = reinterpret_cast<float*>(smem + L.lp);
-    float* s_tot = reinterpret_cast<float*>(smem + L.tot);
-    float* s_rr = reinterpret_cast<float*>(smem + L.rr);
-    float* s_er = reinterpret_cast<float*>(smem + L.er);
-    float* s_fp = reinterpret_cast<float*>(smem + L.fp);
+    OpT* s_an = reinterpret_cast<OpT*>(smem + L.an);
+    OpT* s_mm = reinterpret_cast<OpT*>(smem + L.mm);
+    float* s_ad = reinterpret_cast<float*>(smem + L.ad);    // [p][s][t]: transposed diagonal blocks
     float* s_fd = reinterpret_cast<float*>(smem + L.fd);
     float* s_fo = reinterpret_cast<float*>(smem + L.fo);
     float* s_egc = reinterpret_cast<float*>(smem + L.egc);
     float* s_beta = reinterpret_cast<float*>(smem + L.beta);
 
-    // ---- which (batch, head, segment, column block) this workgroup owns
-    const int H = a.H, dv = a.dv;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    __builtin_assume(wave >= 0 && wave < 8);
+
+    // ---- which (batch, head, segment, column block) this workgroup owns.  Column blocks of
+    // one unit are 8 block indices apart, so they share an XCD (blocks go round-robin over 8).
+    const int H = a.H, dv = a.dv, DVB = a.dv_block;
     const int ncols = MODE == 0 ? dv : dv + DK;
     const int ncb = ncols / DVB;
     const int nseg_grid = MODE == 0 ? a.n_seg : a.n_seg - 1;
-    int64_t bid = blockIdx.x;
-    const int cb = (int)(bid % ncb);
-    bid /= ncb;
-    const int seg = (int)(bid % nseg_grid);
-    bid /= nseg_grid;
-    const int h = (int)(bid % H);
-    const int64_t b = bid / H;
-    const int64_t bh = b * H + h;
+    int64_t unit, cb;
+    {
+        const int64_t bid = blockIdx.x;
+        const int64_t grp = bid / (8 * ncb), rem = bid % (8 * ncb);
+        unit = grp * 8 + rem % 8;
+        cb = rem / 8;
+        const int64_t nunits = a.B * H * (int64_t)nseg_grid;
+        const int64_t tail0 = (nunits / 8) * 8;            // last, partial group of 8 units
+        if (grp * 8 >= tail0) {
+            const int64_t ntail = nunits - tail0, r2 = bid - tail0 * ncb;
+            unit = tail0 + r2 % ntail;
+            cb = r2 / ntail;
+        }
+    }
+    const int seg = (int)(unit % nseg_grid);
+    const int64_t bh = unit / nseg_grid;
+    const int h = (int)(bh % H);
+    const int64_t b = bh / H;
     const int64_t T = a.T;
     const int64_t t_begin = (int64_t)seg * a.seg_len;
     const int64_t t_end = t_begin + a.seg_len < T ? t_begin + a.seg_len : T;
 
-    const int colw = cb * DVB + 16 * wave;           // first (virtual) column of this wave
-    const bool mcols = MODE == 1 && colw >= dv;    // wave holds transition columns
-    const bool blk_mcols = MODE == 1 && cb * DVB >= dv;
-    const bool want_o = MODE == 0;
-    const int g4 = 4 * (lane >> 4), jl = lane & 15;
+    const int colw = (int)cb * DVB + 16 * wave;      // first (virtual) column of this wave
+    const bool chain = 16 * wave < DVB;              // this wave owns state columns
+    const bool mcols = MODE == 1 && colw >= dv;      // ... transition columns (start I, V = 0)
+    const bool vcols = chain && !mcols;              // ... value columns (read v, write o)
 
     const OpT* gq = reinterpret_cast<const OpT*>(a.q);
     const OpT* gk = reinterpret_cast<const OpT*>(a.k);
     const OpT* gv = reinterpret_cast<const OpT*>(a.v);
     OpT* go = reinterpret_cast<OpT*>(a.o);
+    const int tok_k = H * DK;                        // elements between tokens in q, k, log_alpha
+    const int tok_v = H * dv;                        // ... in v and o
 
-    // ---- zero all LDS once: padding columns and the upper blocks of T and M stay zero
-    for (int i = tid * 16; i < L.total; i += NTH * 16)
+    // ---- zero LDS once: padding channels (DK < 32) stay zero for the natural-order loads
+    for (int i = threadIdx.x * 16; i < L.total; i += 512 * 16)
         *reinterpret_cast<f32x4*>(smem + i) = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // Thread maps.  Gate prep: wave w holds channels 16w..16w+15; lane = 16 x + tq covers
+    // the channel quad c0 = 16w + 4x and the token quad 4tq..4tq+3 (sub-tile p = tq / 4).
+    // Chain: wave w holds state columns colw..colw+15; lane (g, jl) holds rows 4g..4g+3 of
+    // each 16-row tile in column jl (the accumulator layout), and v / o in that layout.
+    // Lane-derived indices are recomputed from an opaque copy of the thread id inside the
+    // chunk loop, so the compiler does not hoist dozens of per-lane addresses out of the
+    // loop and hold them in registers for its whole length.
+
+    // prefetch registers (one chunk ahead)
+    f32x4 pla[4];
+    V4 pk[4], pq[4];
+    float pv[NT][4] = {};
+    float pbeta = 0.f;
+
+    // Loads are unconditional, from addresses clamped into the tensors: tokens past the end
+    // are masked where they are used, one chunk later, so no instruction here waits for the
+    // data.  beta is loaded under exactly the predicate of its consumer, so no path reaches
+    // the next prefetch with that load unconsumed.
+    auto prefetch_gates = [&](int64_t t0, int tid) {
+        const int lane = tid & 63;
+        const int tq = lane & 15;
+        const int gc0 = min(16 * wave + 4 * (lane >> 4), DK - 4);
+        const int tlim = (int)(t_end - 1 - t0 < C - 1 ? t_end - 1 - t0 : C - 1);
+        const int64_t base = ((b * T + t0) * H + h) * (int64_t)DK;       // uniform
+        const float* la_b = a.log_alpha + base;
+        const OpT* k_b = gk + base;
+        const OpT* q_b = gq + base;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const unsigned off = (unsigned)(min(4 * tq + j, tlim) * tok_k + gc0);
+            pla[j] = *reinterpret_cast<const f32x4*>(la_b + off);
+            pk[j] = *reinterpret_cast<const V4*>(k_b + off);
+            if (want_o) pq[j] = *reinterpret_cast<const V4*>(q_b + off);
+        }
+        if (tid < C) pbeta = a.beta[(b * T + t0 + min(tid, tlim)) * H + h];
+    };
+    // v for the chain, in the accumulator layout; rows past the end are multiplied by beta = 0
+    auto prefetch_v = [&](int64_t t0, int tid) {
+        if (vcols) {
+            const int lane = tid & 63;
+            const int tlim = (int)(t_end - 1 - t0 < C - 1 ? t_end - 1 - t0 : C - 1);
+            const OpT* v_b = gv + ((b * T + t0) * H + h) * (int64_t)dv + colw + (lane & 15);
+#pragma unroll
+            for (int p = 0; p < NT; ++p)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    pv[p][r] = to_f32(v_b[(unsigned)(min(16 * p + 4 * (lane >> 4) + r, tlim) * tok_v)]);
+        }
+    };
 
     // ---- start state into accumulator layout: Sacc[tau][r] = S[16 tau + g4 + r][colw + jl]
     f32x4 Sacc[NCT];
     {
+        const int lane = threadIdx.x & 63, g4 = 4 * (lane >> 4), jl = lane & 15;
         const float* src = nullptr;
-        int64_t ld = dv;
-        int col = colw + jl;
         if (MODE == 0) {
             // with segments every start (segment 0's included) comes from the scan's
             // output, so S0 is never read here while another workgroup writes S_T
@@ -286,270 +357,319 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
             for (int r = 0; r < 4; ++r) {
                 const int row = 16 * tau + g4 + r;
                 float x = 0.f;
-                if (src) x = src[row * ld + col];
-                else if (mcols) x = (row == col - dv) ? 1.f : 0.f;
+                if (chain) {
+                    if (src) x = src[row * dv + colw + jl];
+                    else if (mcols) x = (row == colw + jl - dv) ? 1.f : 0.f;
+                }
                 Sacc[tau][r] = x;
             }
     }
 
+    __builtin_amdgcn_s_waitcnt(0x0F70);              // vmcnt(0): the start state is in registers
+    if (t_begin < t_end) {
+        prefetch_gates(t_begin, threadIdx.x);
+        prefetch_v(t_begin, threadIdx.x);
+    }
+
     for (int64_t t0 = t_begin; t0 < t_end; t0 += C) {
         const int Tc = (int)(t_end - t0 < C ? t_end - t0 : C);
+        int tid_opaque = threadIdx.x;
+        asm volatile("" : "+v"(tid_opaque));
+        const int tid = tid_opaque, lane = tid & 63;
+        const int g4 = 4 * (lane >> 4), jl = lane & 15;
+        const int gx = lane >> 4, tq = lane & 15;
+        const int gc0 = 16 * wave + 4 * gx;
+        const bool gact = gc0 < DK && tq < 4 * NT;
+        const int gp = tq >> 2, gi = tq & 3;
         __syncthreads();   // previous chunk's readers of LDS are done
 
-        // ---- V block and beta into LDS (zeros past the end and for transition columns)
+        // ================= (1) gate prep (log-decays in log2 units from here on)
+        if (tid < C) s_beta[tid] = tid < Tc ? pbeta : 0.f;
         {
-            constexpr int VE = 16 / E;                 // elements per 16-byte vector
-            const int vpr = DVB / VE;                  // vectors per row
-            for (int i = tid; i < C * vpr; i += NTH) {
-                const int t = i / vpr, cv = (i % vpr) * VE;
-                f32x4 val = {0.f, 0.f, 0.f, 0.f};
-                if (t < Tc && !blk_mcols)
-                    val = *reinterpret_cast<const f32x4*>(gv + ((b * T + t0 + t) * H + h) * dv + cb * DVB + cv);
-                *reinterpret_cast<f32x4*>(s_vb + t * LV + cv) = val;
-            }
-            for (int t = tid; t < C; t += NTH)
-                s_beta[t] = t < Tc ? a.beta[(b * T + t0 + t) * H + h] : 0.f;
-        }
-
-        // ---- gate prep: one item = (channel pair, sub-tile); cumulative log-decay inside
-        // the sub-tile, scaled operands KL = k e^gamma, QL = q e^gamma, RH = k e^(tot-gamma)
-        for (int it = tid; it < (DK / 2) * NT; it += NTH) {
-            const int c = 2 * (it % (DK / 2)), p = it / (DK / 2);
-            float ga[16][2], kk[16][2], qq[16][2];
-            float g0 = 0.f, g1 = 0.f;
+            // Every lane runs the cross-lane scans; only stores are guarded.  Tokens past the
+            // end (and lanes past the last sub-tile) read clamped addresses: zero them.  Full
+            // chunks of 4 sub-tiles need no mask (idle channel lanes of DK < 128 only feed
+            // their own 16-lane rows, whose stores are skipped).
+            float k[4][4], q[4][4], g2[4][4];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int t = 16 * p + i;
-                float la0 = 0.f, la1 = 0.f;
-                kk[i][0] = kk[i][1] = qq[i][0] = qq[i][1] = 0.f;
-                if (t < Tc) {
-                    const int64_t base = ((b * T + t0 + t) * H + h) * DK + c;
-                    load_pair(a.log_alpha + base, la0, la1);
-                    load_pair(gk + base, kk[i][0], kk[i][1]);
-                    load_pair(gq + base, qq[i][0], qq[i][1]);
+            for (int j = 0; j < 4; ++j) {
+                L4::to_f(pk[j], k[j]);
+                if (want_o) L4::to_f(pq[j], q[j]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    g2[j][e] = clamp_log_alpha(pla[j][e]) * LOG2E;
+                    if (!want_o) q[j][e] = 0.f;
                 }
-                g0 += clamp_log_alpha(la0);
-                g1 += clamp_log_alpha(la1);
-                ga[i][0] = g0;
-                ga[i][1] = g1;
             }
-            float h0[16], h1[16];
+            if (NT < 4 || Tc < C) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int t = 16 * p + i;
-                const float a0 = fast_exp(ga[i][0]), a1 = fast_exp(ga[i][1]);
-                const float c0 = fast_exp(g0 - ga[i][0]), c1 = fast_exp(g1 - ga[i][1]);
-                store_pair(s_kl + t * LDK + c, kk[i][0] * a0, kk[i][1] * a1);
-                store_pair(s_ql + t * LDK + c, qq[i][0] * a0, qq[i][1] * a1);
-                store_pair(s_rh + t * LDK + c, kk[i][0] * c0, kk[i][1] * c1);
-                h0[i] = kk[i][0] * c0;
-                h1[i] = kk[i][1] * c1;
-            }
-            store16(s_kht + c * LC + 16 * p, h0);
-            store16(s_kht + (c + 1) * LC + 16 * p, h1);
-            s_tot[p * FK + c] = g0;
-            s_tot[p * FK + c + 1] = g1;
-        }
-        __syncthreads();
-
-        // ---- per-channel factors
-        for (int c = tid; c < DK; c += NTH) {
-            float r = 0.f;
-            s_rr[c] = 0.f;
+                for (int j = 0; j < 4; ++j) {
+                    const bool ok = 4 * tq + j < Tc;
 #pragma unroll
-            for (int p = 0; p < NT; ++p) {
-                const float tot = s_tot[p * FK + c];
-                s_er[p * FK + c] = fast_exp(r);
-                s_fd[p * FK + c] = fast_exp(-tot);
-                r += tot;
-                s_rr[(p + 1) * FK + c] = r;
-            }
-            s_egc[c] = fast_exp(r);
-#pragma unroll
-            for (int p = 0; p < NT; ++p) {
-                s_fp[p * FK + c] = fast_exp(r - s_rr[(p + 1) * FK + c]);
-#pragma unroll
-                for (int pp = 0; pp < p; ++pp)
-                    s_fo[pair_index(p, pp) * FK + c] = fast_exp(s_rr[p * FK + c] - s_rr[(pp + 1) * FK + c]);
-            }
-        }
-        __syncthreads();
-
-        // ---- K-hat^T = (k e^(tot_p - gamma))^T scaled by e^(Gamma_C - r_{p+1})
-        for (int i = tid; i < DK * C; i += NTH) {
-            const int c = i / C, t = i % C;
-            OpT* p = s_kht + c * LC + t;
-            *p = from_f32<OpT>(to_f32(*p) * s_fp[(t / 16) * FK + c]);
-        }
-        // ---- A (beta-scaled, strictly lower) and M (lower) tiles on MFMA
-        {
-            constexpr int NTASK = NT * (NT + 1);
-            for (int task = wave; task < NTASK; task += NTH / 64) {
-                if (!want_o && (task & 1)) continue;            // M only needed for outputs
-                const bool isM = task & 1;
-                int pr = task >> 1, p = 0;
-                while (pr > p) { pr -= p + 1; ++p; }
-                const int pp = pr;                                // pp <= p
-                const OpT* left = isM ? s_ql : s_kl;
-                const float* fac = p == pp ? s_fd + p * FK
-                                 : (p > pp + 1 ? s_fo + pair_index(p, pp) * FK : nullptr);
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < SK_DK; ++ks) {
-                    frag af = MF::ld_nat(left, LDK, 16 * p, ks * KS, lane);
-                    if (fac) af = MF::scale_nat(af, fac, ks * KS, lane);
-                    const frag bf = MF::ld_nat(s_rh, LDK, 16 * pp, ks * KS, lane);
-                    acc = MF::mma(af, bf, acc);
-                }
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int tr = g4 + r;                        // row within tile
-                    const int t = 16 * p + tr, s = 16 * pp + jl;
-                    if (!isM) {
-                        float val = acc[r] * s_beta[t];
-                        if (p == pp && jl >= tr) val = 0.f;
-                        s_abuf[t * LCA + s] = val;
-                    } else {
-                        float val = acc[r];
-                        if (p == pp && jl > tr) val = 0.f;
-                        s_mb[t * LC + s] = from_f32<OpT>(val);
+                    for (int e = 0; e < 4; ++e) {
+                        g2[j][e] = ok ? g2[j][e] : 0.f;
+                        k[j][e] = ok ? k[j][e] : 0.f;
+                        q[j][e] = ok ? q[j][e] : 0.f;
                     }
                 }
             }
-        }
-        __syncthreads();
-
-        // ---- T = (I + Diag(beta) A)^-1 Diag(beta), fp32.  Diagonal blocks first.
-        if (tid < NT * 16) {
-            const int p = tid >> 4, j = tid & 15;
-            float x[16];
+            float pre[4], tot[4], rp[4], after[4], gcs[4], tn1[4], tn2[4], tm1[4], tm2[4];
 #pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                float acc = (t == j) ? 1.f : 0.f;
-                const float* row = s_abuf + (16 * p + t) * LCA + 16 * p;
-#pragma unroll
-                for (int s = 0; s < t; ++s) acc -= row[s] * x[s];
-                x[t] = acc;
+            for (int e = 0; e < 4; ++e) {
+                const float loc = g2[0][e] + g2[1][e] + g2[2][e] + g2[3][e];
+                // inclusive scan of the 4 lane totals of this sub-tile (lanes 4p .. 4p+3)
+                float inc = loc;
+                float sh = quad_perm<0x90>(inc);                      // lane i <- lane i-1 (0,0,1,2)
+                inc += gi >= 1 ? sh : 0.f;
+                sh = quad_perm<0x40>(inc);                            // lane i <- lane i-2 (0,0,0,1)
+                inc += gi >= 2 ? sh : 0.f;
+                const float exc = quad_perm<0x90>(inc);
+                pre[e] = gi >= 1 ? exc : 0.f;
+                tot[e] = quad_perm<0xFF>(inc);                        // lane 3 of the quad: sub-tile total
+                // prefix over sub-tiles (groups of 4 lanes in the 16-lane row)
+                float z = tot[e];
+                z += row_shr<4>(z);
+                z += row_shr<8>(z);                                   // inclusive: r_{p+1}
+                rp[e] = row_shr<4>(z);                                // exclusive: r_p
+                // suffix over sub-tiles
+                float u = tot[e];
+                u += row_shl<4>(u);
+                u += row_shl<8>(u);                                   // sum over p' >= p
+                after[e] = row_shl<4>(u);                             // sum over p' > p
+                gcs[e] = u;                                           // at p = 0: Gamma_C
+                tn1[e] = row_shl<4>(tot[e]);                          // total of sub-tile p+1
+                tn2[e] = row_shl<8>(tot[e]);                          // total of sub-tile p+2
+                tm1[e] = row_shr<4>(tot[e]);                          // total of sub-tile p-1
+                tm2[e] = row_shr<8>(tot[e]);                          // total of sub-tile p-2
             }
+            if (gact && gi == 0) {
 #pragma unroll
-            for (int t = 0; t < 16; ++t) s_tinv[(16 * p + t) * LCA + 16 * p + j] = x[t];
-        }
-        __syncthreads();
-        if constexpr (NT > 1) {
-            // L'_pq = N_pp L_pq for p > q (N_pp = inverse of the diagonal block)
-            for (int it = tid; it < NPAIR * 256; it += NTH) {
-                const int pr = it >> 8, i = (it >> 4) & 15, j = it & 15;
-                int p = 1, q = pr;
-                while (q >= p) { q -= p; ++p; }
-                const float* nrow = s_tinv + (16 * p + i) * LCA + 16 * p;
-                const float* lcol = s_abuf + (16 * p) * LCA + 16 * q + j;
-                float acc = 0.f;
-#pragma unroll
-                for (int u = 0; u < 16; ++u) acc += nrow[u] * lcol[u * LCA];
-                s_lp[it] = acc;
-            }
-            __syncthreads();
-            // X_pq = -sum_{m=q}^{p-1} L'_pm X_mq, level by level (X_qq = N_qq)
-#pragma unroll
-            for (int d = 1; d < NT; ++d) {
-                for (int it = tid; it < (NT - d) * 256; it += NTH) {
-                    const int q = it >> 8, i = (it >> 4) & 15, j = it & 15;
-                    const int p = q + d;
-                    float acc = 0.f;
-                    for (int m = q; m < p; ++m) {
-                        const float* lrow = s_lp + pair_index(p, m) * 256 + i * 16;
-                        const float* xcol = s_tinv + (16 * m) * LCA + 16 * q + j;
-#pragma unroll
-                        for (int u = 0; u < 16; ++u) acc += lrow[u] * xcol[u * LCA];
+                for (int e = 0; e < 4; ++e) {
+                    if (gp == 0) s_egc[gc0 + e] = fast_exp2(gcs[e]);
+                    if (!RV) {
+                        s_fd[gp * DKP + gc0 + e] = fast_exp2(-tot[e]);                               // e^-tot_p
+                        if (NT == 4 && gp == 2) s_fo[0 * DKP + gc0 + e] = fast_exp2(tm1[e]);          // (2,0)
+                        if (NT == 4 && gp == 3) {
+                            s_fo[1 * DKP + gc0 + e] = fast_exp2(tm1[e] + tm2[e]);                     // (3,0)
+                            s_fo[2 * DKP + gc0 + e] = fast_exp2(tm1[e]);                              // (3,1)
+                        }
                     }
-                    s_tinv[(16 * p + i) * LCA + 16 * q + j] = -acc;
                 }
-                __syncthreads();
+            }
+            if (gact) {
+                float er[4], eh[4], ed[4], ef1[4], ef2[4], gam[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    er[e] = fast_exp2(rp[e]);
+                    eh[e] = fast_exp2(after[e]);
+                    gam[e] = pre[e];
+                    if (RV) {
+                        ed[e] = fast_exp2(-tot[e]);
+                        ef1[e] = fast_exp2(tn1[e]);
+                        ef2[e] = fast_exp2(tn1[e] + tn2[e]);
+                    }
+                }
+                float kht[4][4];                          // [channel][token]
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int t = 4 * tq + j;
+                    float kl[4], ql[4], rh[4], kt[4], qt[4], rd[4], rf1[4], rf2[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        gam[e] += g2[j][e];
+                        const float e1 = fast_exp2(gam[e]), e2 = fast_exp2(tot[e] - gam[e]);
+                        kl[e] = k[j][e] * e1;
+                        ql[e] = q[j][e] * e1;
+                        rh[e] = k[j][e] * e2;
+                        kt[e] = kl[e] * er[e];
+                        qt[e] = ql[e] * er[e];
+                        kht[e][j] = rh[e] * eh[e];
+                        if (RV) {
+                            rd[e] = rh[e] * ed[e];                    // k e^-gamma, <= e^80
+                            rf1[e] = rh[e] * ef1[e];                  // referenced at the end of p+1
+                            rf2[e] = rh[e] * ef2[e];                  // ... of p+2
+                        }
+                    }
+                    *reinterpret_cast<V4*>(s_kt + t * LDK + gc0) = L4::from_f(kt);
+                    *reinterpret_cast<V4*>(s_kl + t * LDK + gc0) = L4::from_f(kl);
+                    *reinterpret_cast<V4*>(s_rh + t * LDK + gc0) = L4::from_f(rh);
+                    if (want_o) {
+                        *reinterpret_cast<V4*>(s_qt + t * LDK + gc0) = L4::from_f(qt);
+                        *reinterpret_cast<V4*>(s_ql + t * LDK + gc0) = L4::from_f(ql);
+                    }
+                    if (RV) {
+                        *reinterpret_cast<V4*>(s_rd + t * LDK + gc0) = L4::from_f(rd);
+                        if (NT == 4 && gp <= 1) *reinterpret_cast<V4*>(s_rf + t * LDK + gc0) = L4::from_f(rf1);
+                        if (NT == 4 && gp == 0) *reinterpret_cast<V4*>(s_rf + (32 + t) * LDK + gc0) = L4::from_f(rf2);
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    *reinterpret_cast<V4*>(s_kht + (gc0 + e) * LC + 4 * tq) = L4::from_f(kht[e]);
             }
         }
-        // T = Tinv Diag(beta) on the lower block triangle (upper blocks stay zero)
-        for (int i = tid; i < C * C; i += NTH) {
-            const int t = i / C, s = i % C;
-            if (s < 16 * (t / 16 + 1)) s_tb[t * LC + s] = from_f32<OpT>(s_tinv[t * LCA + s] * s_beta[s]);
-        }
+        // next chunk's gates, keys and queries load while this chunk computes
+        if (t0 + C < t_end) prefetch_gates(t0 + C, tid);
         __syncthreads();
 
-        // ---- the state chain, per wave on its 16 columns
-        {
-            f32x4 X[NT], QS[NT];
+        // ================= (2) X = Kt S and QS = Qt S, then the A / M tiles
+        f32x4 X[NT], QS[NT];
+        if (chain) {
+            B16 sb[NCT];
+#pragma unroll
+            for (int tau = 0; tau < NCT; ++tau) sb[tau] = MF::b16(Sacc[tau]);
 #pragma unroll
             for (int p = 0; p < NT; ++p) {
-                f32x4 sc[NCT];
-#pragma unroll
-                for (int tau = 0; tau < NCT; ++tau)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) sc[tau][r] = Sacc[tau][r] * s_er[p * FK + 16 * tau + g4 + r];
                 X[p] = f32x4{0.f, 0.f, 0.f, 0.f};
                 QS[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if constexpr (NCT == 1) {
+                    X[p] = MF::k16(s_kt, LDK, 16 * p, 0, sb[0], X[p], lane);
+                    if (want_o) QS[p] = MF::k16(s_qt, LDK, 16 * p, 0, sb[0], QS[p], lane);
+                } else {
 #pragma unroll
-                for (int s = 0; s < SK_DK; ++s) {
-                    const frag sf = MF::b_chain(sc, s);
-                    X[p] = MF::mma(MF::ld_chain(s_kl, LDK, 16 * p, s, lane), sf, X[p]);
-                    if (want_o) QS[p] = MF::mma(MF::ld_chain(s_ql, LDK, 16 * p, s, lane), sf, QS[p]);
+                    for (int s2 = 0; s2 < NCT / 2; ++s2) {
+                        X[p] = MF::k32(s_kt, LDK, 16 * p, 32 * s2, sb[2 * s2], sb[2 * s2 + 1], X[p], lane);
+                        if (want_o)
+                            QS[p] = MF::k32(s_qt, LDK, 16 * p, 32 * s2, sb[2 * s2], sb[2 * s2 + 1], QS[p], lane);
+                    }
                 }
             }
-            // V' = V - X
-            f32x4 Vp[NT];
+        }
+        {
+            // up to 3 tile tasks per wave; every task's loads and products come before any
+            // of the wave's stores
+            constexpr int NPAIR = NT * (NT + 1) / 2;
+            constexpr int NTASK = want_o ? 2 * NPAIR : NPAIR;
+            constexpr int NSLOT = (NTASK + 7) / 8;
+            f32x4 acc[NSLOT];
 #pragma unroll
-            for (int p = 0; p < NT; ++p)
+            for (int sl = 0; sl < NSLOT; ++sl) {
+                const int task = wave + 8 * sl;
+                acc[sl] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (task < NTASK) {
+                    const bool isM = task >= NPAIR;
+                    int pr = isM ? task - NPAIR : task, p = 0;
+                    while (pr > p) { pr -= p + 1; ++p; }
+                    const int pp = pr;                                // pp <= p
+                    const OpT* left = isM ? s_ql : s_kl;
+                    const OpT* right = s_rh;
+                    int rrow = 16 * pp;
+                    const float* fac = nullptr;
+                    if (RV) {
+                        if (p == pp) right = s_rd;
+                        else if (p - pp == 2) right = s_rf;                           // rows 16 pp
+                        else if (p - pp == 3) { right = s_rf; rrow = 32 + 16 * pp; }
+                    } else {
+                        fac = p == pp ? s_fd + p * DKP : (p - pp >= 2 ? s_fo + pair_fo_index(p, pp) * DKP : nullptr);
+                    }
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float vv = mcols ? 0.f : to_f32(s_vb[(16 * p + g4 + r) * LV + 16 * wave + jl]);
-                    Vp[p][r] = vv - X[p][r];
+                    for (int ks = 0; ks < KNAT; ++ks)
+                        acc[sl] = MF::nat(left, LDK, 16 * p, right, LDK, rrow, ks * MF::KS, fac, acc[sl], lane);
                 }
-            // U = T V'
-            f32x4 U[NT];
-#pragma unroll
-            for (int p = 0; p < NT; ++p) {
-                U[p] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s = 0; s < SK_C; ++s)
-                    U[p] = MF::mma(MF::ld_chain(s_tb, LC, 16 * p, s, lane), MF::b_chain(Vp, s), U[p]);
             }
-            // O = Q~ S + M U, staged in the V buffer (same wave, same columns)
-            if (want_o) {
 #pragma unroll
-                for (int p = 0; p < NT; ++p) {
-                    f32x4 O = QS[p];
+            for (int sl = 0; sl < NSLOT; ++sl) {
+                const int task = wave + 8 * sl;
+                if (task < NTASK) {
+                    const bool isM = task >= NPAIR;
+                    int pr = isM ? task - NPAIR : task, p = 0;
+                    while (pr > p) { pr -= p + 1; ++p; }
+                    const int pp = pr;
+                    if (!isM && p == pp) {
+                        // diagonal block of beta A, strictly lower, stored transposed: [p][s][t]
+                        f32x4 col;
 #pragma unroll
-                    for (int s = 0; s < SK_C; ++s)
-                        O = MF::mma(MF::ld_chain(s_mb, LC, 16 * p, s, lane), MF::b_chain(U, s), O);
+                        for (int r = 0; r < 4; ++r) col[r] = (jl < g4 + r) ? acc[sl][r] * s_beta[16 * p + g4 + r] : 0.f;
+                        *reinterpret_cast<f32x4*>(s_ad + (p * 16 + jl) * 16 + g4) = col;
+                    } else {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        s_vb[(16 * p + g4 + r) * LV + 16 * wave + jl] = from_f32<OpT>(O[r]);
+                        for (int r = 0; r < 4; ++r) {
+                            const int tr = g4 + r;
+                            const int t = 16 * p + tr, s = 16 * pp + jl;
+                            if (!isM) s_an[t * LC + s] = from_f32<OpT>(-acc[sl][r] * s_beta[t]);
+                            else s_mm[t * LC + s] = from_f32<OpT>((p == pp && jl > tr) ? 0.f : acc[sl][r]);
+                        }
+                    }
                 }
-            }
-            // S <- Diag(e^Gamma_C) S + K-hat^T U
-#pragma unroll
-            for (int tau = 0; tau < NCT; ++tau) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) Sacc[tau][r] *= s_egc[16 * tau + g4 + r];
-#pragma unroll
-                for (int s = 0; s < SK_C; ++s)
-                    Sacc[tau] = MF::mma(MF::ld_chain(s_kht, LC, 16 * tau, s, lane), MF::b_chain(U, s), Sacc[tau]);
             }
         }
         __syncthreads();
 
-        // ---- write the chunk's outputs
-        if (want_o) {
-            constexpr int VE = 16 / E;
-            const int vpr = DVB / VE;
-            for (int i = tid; i < Tc * vpr; i += NTH) {
-                const int t = i / vpr, cv = (i % vpr) * VE;
-                *reinterpret_cast<f32x4*>(go + ((b * T + t0 + t) * H + h) * dv + cb * DVB + cv) =
-                    *reinterpret_cast<const f32x4*>(s_vb + t * LV + cv);
+        // ================= (3) inverses of the diagonal blocks of I + Diag(beta) A (fp32),
+        // right-looking: once x_s is final it is subtracted from every later row
+        if (wave == 0 && (lane >> 4) < NT) {
+            const int p = lane >> 4, j = lane & 15;
+            const float* Ab = s_ad + p * 256;                // column s at Ab[16 s .. 16 s + 15]
+            float x[16];
+#pragma unroll
+            for (int t = 0; t < 16; ++t) x[t] = (t == j) ? 1.f : 0.f;
+#pragma unroll
+            for (int s = 0; s < 15; ++s) {
+                float col[16];
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const f32x4 c4 = *reinterpret_cast<const f32x4*>(Ab + 16 * s + 4 * q4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) col[4 * q4 + e] = c4[e];
+                }
+#pragma unroll
+                for (int t = s + 1; t < 16; ++t) x[t] -= col[t] * x[s];
+            }
+#pragma unroll
+            for (int t = 0; t < 16; ++t) s_an[(16 * p + t) * LC + 16 * p + j] = from_f32<OpT>(x[t]);
+        }
+        __syncthreads();
+
+        // ================= (4) the state chain on this wave's 16 columns
+        if (chain) {
+            // R_p = beta (V - X);  U_p = N_pp (R_p - sum_{q<p} Ab_pq U_q)
+            B16 ub[NT];
+#pragma unroll
+            for (int p = 0; p < NT; ++p) {
+                f32x4 R;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) R[r] = s_beta[16 * p + g4 + r] * (pv[p][r] - X[p][r]);
+#pragma unroll
+                for (int q = 0; q < p; ++q) R = MF::k16(s_an, LC, 16 * p, 16 * q, ub[q], R, lane);
+                const f32x4 U = MF::k16(s_an, LC, 16 * p, 16 * p, MF::b16(R), f32x4{0.f, 0.f, 0.f, 0.f}, lane);
+                ub[p] = MF::b16(U);
+            }
+            // O = QS + M U, stored straight from the accumulators (rows past the end skipped)
+            if (want_o) {
+                OpT* o_b = go + ((b * T + t0) * H + h) * (int64_t)dv + colw + jl;
+#pragma unroll
+                for (int p = 0; p < NT; ++p) {
+#pragma unroll
+                    for (int q = 0; q <= p; ++q) QS[p] = MF::k16(s_mm, LC, 16 * p, 16 * q, ub[q], QS[p], lane);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int t = 16 * p + g4 + r;
+                        if (t < Tc) o_b[(unsigned)(t * tok_v)] = from_f32<OpT>(QS[p][r]);
+                    }
+                }
+            }
+            // next chunk's v loads once this chunk's are consumed
+            if (t0 + C < t_end) prefetch_v(t0 + C, tid);
+            // S <- Diag(e^Gamma_C) S + Khat^T U
+#pragma unroll
+            for (int tau = 0; tau < NCT; ++tau) {
+                const f32x4 eg = *reinterpret_cast<const f32x4*>(s_egc + 16 * tau + g4);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Sacc[tau][r] *= eg[r];
+                if constexpr (NT == 1) {
+                    Sacc[tau] = MF::k16(s_kht, LC, 16 * tau, 0, ub[0], Sacc[tau], lane);
+                } else {
+#pragma unroll
+                    for (int s2 = 0; s2 < NT / 2; ++s2)
+                        Sacc[tau] = MF::k32(s_kht, LC, 16 * tau, 32 * s2, ub[2 * s2], ub[2 * s2 + 1], Sacc[tau], lane);
+                }
             }
         }
     }
 
     // ---- final state of this unit
-    {
+    if (chain) {
+        const int lane = threadIdx.x & 63, g4 = 4 * (lane >> 4), jl = lane & 15;
         float* dst = nullptr;
         int64_t ld = 0;
         int col = colw + jl;
@@ -570,26 +690,25 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
 }
 
 // ---------------------------------------------------------------- launch
-size_t chunk_lds_bytes(bool bf16_, int dk, int chunk, int dv_block) {
-    const int E = bf16_ ? 2 : 4, KS = bf16_ ? 32 : 4;
-    return (size_t)lds_layout(E, KS, dk, chunk, dv_block).total;
+size_t chunk_lds_bytes(bool bf16_, int dk, int chunk, int /*dv_block*/) {
+    return (size_t)lds_layout(bf16_ ? 2 : 4, dk, chunk).total;
 }
 
 template <typename OpT, int DK, int C, int MODE>
 static hipError_t launch_chunk_m(const ChunkArgs& a, hipStream_t st) {
-    const size_t lds = chunk_lds_bytes(sizeof(OpT) == 2, DK, C, a.dv_block);
+    constexpr size_t lds = (size_t)lds_layout(sizeof(OpT), DK, C).total;
     auto kern = chunk_kernel<OpT, DK, C, MODE>;
     static bool attr_set = false;   // per instantiation; the attribute is device-independent
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds > 65536 ? 163840 : 65536);
+        hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 163840);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    const int ncols = a.mode == 0 ? a.dv : a.dv + DK;
-    const int nseg_grid = a.mode == 0 ? a.n_seg : a.n_seg - 1;
+    const int ncols = MODE == 0 ? a.dv : a.dv + DK;
+    const int nseg_grid = MODE == 0 ? a.n_seg : a.n_seg - 1;
     const int64_t nblk = a.B * a.H * (int64_t)nseg_grid * (ncols / a.dv_block);
     if (nblk <= 0) return hipSuccess;
-    hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(64 * (a.dv_block / 16)), lds, st, a);
+    hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(512), lds, st, a);
     return hipGetLastError();
 }
 
