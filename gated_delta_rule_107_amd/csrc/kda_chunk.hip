@@ -127,13 +127,14 @@ template <> struct MM<float> {
 template <int N> __device__ __forceinline__ float row_shr(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x110 | N, 0xF, 0xF, true));
 }
-// Within 16-lane rows: value of lane (i + N) (0 for the last N lanes of the row).
-template <int N> __device__ __forceinline__ float row_shl(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x100 | N, 0xF, 0xF, true));
+// ---------------------------------------------------------------- global addressing
+// base (wave-uniform, in scalar registers) + a 32-bit byte offset per lane: the form the
+// hardware's scalar-base addressing takes, with no 64-bit arithmetic per access
+template <typename T> __device__ __forceinline__ T* at_bytes(T* base, unsigned byte_off) {
+    return reinterpret_cast<T*>(reinterpret_cast<char*>(base) + byte_off);
 }
-// Within groups of 4 lanes: lane selector pattern (2 bits per lane).
-template <int PAT> __device__ __forceinline__ float quad_perm(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), PAT, 0xF, 0xF, true));
+template <typename T> __device__ __forceinline__ const T* at_bytes(const T* base, unsigned byte_off) {
+    return reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + byte_off);
 }
 
 // ---------------------------------------------------------------- element access
@@ -180,11 +181,12 @@ __host__ __device__ constexpr Lds lds_layout(int E, int DK, int C) {
     const int NT = C / 16;
     const int DKP = DK < 32 ? 32 : DK;            // bf16 natural loads read 32 channels at a time
     const int LDK = DKP + PADE;
-    const int LC = C + PADE;
+    const int LKQ = DKP + 16 / E / (E == 2 ? 2 : 1);
+    const int LC = C + 16 / E / (E == 2 ? 2 : 1);
     Lds L{};
     int off = 0;
-    L.kt = off;   off += align16(C * LDK * E);
-    L.qt = off;   off += align16(C * LDK * E);
+    L.kt = off;   off += align16(C * LKQ * E);
+    L.qt = off;   off += align16(C * LKQ * E);
     L.kl = off;   off += align16(C * LDK * E);
     L.ql = off;   off += align16(C * LDK * E);
     L.rh = off;   off += align16(C * LDK * E);
@@ -220,8 +222,15 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
     constexpr int NT = C / 16;                       // 16-token sub-tiles per chunk
     constexpr int NCT = DK / 16;                     // 16-row tiles of the state
     constexpr int DKP = DK < 32 ? 32 : DK;
+    // Row pitches (LDS has 32 4-byte banks; 16 lanes of a b64 access and 8 lanes of a b128
+    // access share a cycle).  Tiles read 16 B per lane (the natural-order A / M operands):
+    // pitch = 4 banks mod 32, so 8 consecutive rows hit 8 distinct bank quads.  Tiles read
+    // 8 B per lane (the chained operands Kt, Qt, Khat^T, the solve and M blocks): pitch = 2
+    // banks mod 32, so 16 consecutive rows hit 16 distinct bank pairs.  (bf16; float32 keeps
+    // 16-byte pitches so its 16-byte chained loads stay aligned.)
     constexpr int LDK = DKP + PADE;
-    constexpr int LC = C + PADE;
+    constexpr int LKQ = DKP + (E == 2 ? 4 : 4);
+    constexpr int LC = C + (E == 2 ? 4 : 4);
     constexpr int KNAT = (E == 2) ? (DK + 31) / 32 : DK / 4;   // natural-order steps over channels
     constexpr bool want_o = MODE == 0;
     constexpr Lds L = lds_layout(E, DK, C);
@@ -290,8 +299,10 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
     for (int i = threadIdx.x * 16; i < L.total; i += 512 * 16)
         *reinterpret_cast<f32x4*>(smem + i) = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Thread maps.  Gate prep: wave w holds channels 16w..16w+15; lane = 16 x + tq covers
-    // the channel quad c0 = 16w + 4x and the token quad 4tq..4tq+3 (sub-tile p = tq / 4).
+    // Thread maps.  Gate prep: wave w holds channels 16w..16w+15; lane = 16 p + 4 i + x
+    // covers the channel quad c0 = 16w + 4x and the token quad tq = 4p + i (tokens
+    // 4tq..4tq+3 of sub-tile p), so a 16-lane DPP row is one sub-tile and a 16-lane store
+    // pass spans 4 token quads x 4 channel quads.
     // Chain: wave w holds state columns colw..colw+15; lane (g, jl) holds rows 4g..4g+3 of
     // each 16-row tile in column jl (the accumulator layout), and v / o in that layout.
     // Lane-derived indices are recomputed from an opaque copy of the thread id inside the
@@ -310,8 +321,8 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
     // the next prefetch with that load unconsumed.
     auto prefetch_gates = [&](int64_t t0, int tid) {
         const int lane = tid & 63;
-        const int tq = lane & 15;
-        const int gc0 = min(16 * wave + 4 * (lane >> 4), DK - 4);
+        const int tq = 4 * (lane >> 4) + ((lane >> 2) & 3);
+        const int gc0 = min(16 * wave + 4 * (lane & 3), DK - 4);
         const int tlim = (int)(t_end - 1 - t0 < C - 1 ? t_end - 1 - t0 : C - 1);
         const int64_t base = ((b * T + t0) * H + h) * (int64_t)DK;       // uniform
         const float* la_b = a.log_alpha + base;
@@ -320,23 +331,23 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const unsigned off = (unsigned)(min(4 * tq + j, tlim) * tok_k + gc0);
-            pla[j] = *reinterpret_cast<const f32x4*>(la_b + off);
-            pk[j] = *reinterpret_cast<const V4*>(k_b + off);
-            if (want_o) pq[j] = *reinterpret_cast<const V4*>(q_b + off);
+            pla[j] = *at_bytes(reinterpret_cast<const f32x4*>(la_b), off * 4u);
+            pk[j] = *at_bytes(reinterpret_cast<const V4*>(k_b), off * (unsigned)E);
+            if (want_o) pq[j] = *at_bytes(reinterpret_cast<const V4*>(q_b), off * (unsigned)E);
         }
-        if (tid < C) pbeta = a.beta[(b * T + t0 + min(tid, tlim)) * H + h];
+        if (tid < C) pbeta = *at_bytes(a.beta + (b * T + t0) * H + h, (unsigned)(min(tid, tlim) * H) * 4u);
     };
     // v for the chain, in the accumulator layout; rows past the end are multiplied by beta = 0
     auto prefetch_v = [&](int64_t t0, int tid) {
         if (vcols) {
             const int lane = tid & 63;
             const int tlim = (int)(t_end - 1 - t0 < C - 1 ? t_end - 1 - t0 : C - 1);
-            const OpT* v_b = gv + ((b * T + t0) * H + h) * (int64_t)dv + colw + (lane & 15);
+            const OpT* v_b = gv + ((b * T + t0) * H + h) * (int64_t)dv + colw;      // wave-uniform
 #pragma unroll
             for (int p = 0; p < NT; ++p)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    pv[p][r] = to_f32(v_b[(unsigned)(min(16 * p + 4 * (lane >> 4) + r, tlim) * tok_v)]);
+                    pv[p][r] = to_f32(*at_bytes(v_b, (unsigned)(min(16 * p + 4 * (lane >> 4) + r, tlim) * tok_v + (lane & 15)) * (unsigned)E));
         }
     };
 
@@ -377,10 +388,10 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
         asm volatile("" : "+v"(tid_opaque));
         const int tid = tid_opaque, lane = tid & 63;
         const int g4 = 4 * (lane >> 4), jl = lane & 15;
-        const int gx = lane >> 4, tq = lane & 15;
+        const int gx = lane & 3, gi = (lane >> 2) & 3, gp = lane >> 4;
+        const int tq = 4 * gp + gi;
         const int gc0 = 16 * wave + 4 * gx;
-        const bool gact = gc0 < DK && tq < 4 * NT;
-        const int gp = tq >> 2, gi = tq & 3;
+        const bool gact = gc0 < DK && gp < NT;
         __syncthreads();   // previous chunk's readers of LDS are done
 
         // ================= (1) gate prep (log-decays in log2 units from here on)
@@ -417,30 +428,23 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float loc = g2[0][e] + g2[1][e] + g2[2][e] + g2[3][e];
-                // inclusive scan of the 4 lane totals of this sub-tile (lanes 4p .. 4p+3)
+                // inclusive scan over the 4 token quads of this sub-tile (lanes 4 apart)
                 float inc = loc;
-                float sh = quad_perm<0x90>(inc);                      // lane i <- lane i-1 (0,0,1,2)
-                inc += gi >= 1 ? sh : 0.f;
-                sh = quad_perm<0x40>(inc);                            // lane i <- lane i-2 (0,0,0,1)
-                inc += gi >= 2 ? sh : 0.f;
-                const float exc = quad_perm<0x90>(inc);
-                pre[e] = gi >= 1 ? exc : 0.f;
-                tot[e] = quad_perm<0xFF>(inc);                        // lane 3 of the quad: sub-tile total
-                // prefix over sub-tiles (groups of 4 lanes in the 16-lane row)
-                float z = tot[e];
-                z += row_shr<4>(z);
-                z += row_shr<8>(z);                                   // inclusive: r_{p+1}
-                rp[e] = row_shr<4>(z);                                // exclusive: r_p
-                // suffix over sub-tiles
-                float u = tot[e];
-                u += row_shl<4>(u);
-                u += row_shl<8>(u);                                   // sum over p' >= p
-                after[e] = row_shl<4>(u);                             // sum over p' > p
-                gcs[e] = u;                                           // at p = 0: Gamma_C
-                tn1[e] = row_shl<4>(tot[e]);                          // total of sub-tile p+1
-                tn2[e] = row_shl<8>(tot[e]);                          // total of sub-tile p+2
-                tm1[e] = row_shr<4>(tot[e]);                          // total of sub-tile p-1
-                tm2[e] = row_shr<8>(tot[e]);                          // total of sub-tile p-2
+                inc += row_shr<4>(inc);
+                inc += row_shr<8>(inc);
+                pre[e] = row_shr<4>(inc);                             // exclusive
+                // sub-tile totals from lane 12 + x of every row
+                float tp[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) tp[q] = q < NT ? __shfl(inc, 16 * q + 12 + gx, 64) : 0.f;
+                tot[e] = gp == 0 ? tp[0] : gp == 1 ? tp[1] : gp == 2 ? tp[2] : tp[3];
+                rp[e] = (gp > 0 ? tp[0] : 0.f) + (gp > 1 ? tp[1] : 0.f) + (gp > 2 ? tp[2] : 0.f);  // r_p
+                after[e] = (gp < 1 ? tp[1] : 0.f) + (gp < 2 ? tp[2] : 0.f) + (gp < 3 ? tp[3] : 0.f);
+                gcs[e] = tp[0] + tp[1] + tp[2] + tp[3];               // Gamma_C
+                tn1[e] = gp == 0 ? tp[1] : gp == 1 ? tp[2] : gp == 2 ? tp[3] : 0.f;   // sub-tile p+1
+                tn2[e] = gp == 0 ? tp[2] : gp == 1 ? tp[3] : 0.f;                      // p+2
+                tm1[e] = gp == 1 ? tp[0] : gp == 2 ? tp[1] : gp == 3 ? tp[2] : 0.f;   // p-1
+                tm2[e] = gp == 2 ? tp[0] : gp == 3 ? tp[1] : 0.f;                      // p-2
             }
             if (gact && gi == 0) {
 #pragma unroll
@@ -490,11 +494,11 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
                             rf2[e] = rh[e] * ef2[e];                  // ... of p+2
                         }
                     }
-                    *reinterpret_cast<V4*>(s_kt + t * LDK + gc0) = L4::from_f(kt);
+                    *reinterpret_cast<V4*>(s_kt + t * LKQ + gc0) = L4::from_f(kt);
                     *reinterpret_cast<V4*>(s_kl + t * LDK + gc0) = L4::from_f(kl);
                     *reinterpret_cast<V4*>(s_rh + t * LDK + gc0) = L4::from_f(rh);
                     if (want_o) {
-                        *reinterpret_cast<V4*>(s_qt + t * LDK + gc0) = L4::from_f(qt);
+                        *reinterpret_cast<V4*>(s_qt + t * LKQ + gc0) = L4::from_f(qt);
                         *reinterpret_cast<V4*>(s_ql + t * LDK + gc0) = L4::from_f(ql);
                     }
                     if (RV) {
@@ -523,14 +527,14 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
                 X[p] = f32x4{0.f, 0.f, 0.f, 0.f};
                 QS[p] = f32x4{0.f, 0.f, 0.f, 0.f};
                 if constexpr (NCT == 1) {
-                    X[p] = MF::k16(s_kt, LDK, 16 * p, 0, sb[0], X[p], lane);
-                    if (want_o) QS[p] = MF::k16(s_qt, LDK, 16 * p, 0, sb[0], QS[p], lane);
+                    X[p] = MF::k16(s_kt, LKQ, 16 * p, 0, sb[0], X[p], lane);
+                    if (want_o) QS[p] = MF::k16(s_qt, LKQ, 16 * p, 0, sb[0], QS[p], lane);
                 } else {
 #pragma unroll
                     for (int s2 = 0; s2 < NCT / 2; ++s2) {
-                        X[p] = MF::k32(s_kt, LDK, 16 * p, 32 * s2, sb[2 * s2], sb[2 * s2 + 1], X[p], lane);
+                        X[p] = MF::k32(s_kt, LKQ, 16 * p, 32 * s2, sb[2 * s2], sb[2 * s2 + 1], X[p], lane);
                         if (want_o)
-                            QS[p] = MF::k32(s_qt, LDK, 16 * p, 32 * s2, sb[2 * s2], sb[2 * s2 + 1], QS[p], lane);
+                            QS[p] = MF::k32(s_qt, LKQ, 16 * p, 32 * s2, sb[2 * s2], sb[2 * s2 + 1], QS[p], lane);
                     }
                 }
             }
@@ -636,7 +640,8 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
             }
             // O = QS + M U, stored straight from the accumulators (rows past the end skipped)
             if (want_o) {
-                OpT* o_b = go + ((b * T + t0) * H + h) * (int64_t)dv + colw + jl;
+                OpT* o_b = go + ((b * T + t0) * H + h) * (int64_t)dv + colw;          // wave-uniform
+                const unsigned o_lane = (unsigned)(g4 * tok_v + jl);
 #pragma unroll
                 for (int p = 0; p < NT; ++p) {
 #pragma unroll
@@ -644,7 +649,7 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int t = 16 * p + g4 + r;
-                        if (t < Tc) o_b[(unsigned)(t * tok_v)] = from_f32<OpT>(QS[p][r]);
+                        if (t < Tc) *at_bytes(o_b, (o_lane + (unsigned)((16 * p + r) * tok_v)) * (unsigned)E) = from_f32<OpT>(QS[p][r]);
                     }
                 }
             }
