@@ -312,7 +312,11 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
     // prefetch registers (one chunk ahead)
     f32x4 pla[4];
     V4 pk[4], pq[4];
-    float pv[NT][4] = {};
+    // v granules of 16 bytes: thread tid holds granules tid, tid + 512, ... of the chunk's
+    // [C][DVB] value block (row = granule / GPR, granule column = granule % GPR)
+    typedef __attribute__((__vector_size__(16))) float g16;
+    constexpr int NGV = C * (128 * E / 16) / 512 > 0 ? C * (128 * E / 16) / 512 : 1;
+    g16 pv[NGV];
     float pbeta = 0.f;
 
     // Loads are unconditional, from addresses clamped into the tensors: tokens past the end
@@ -337,19 +341,28 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
         }
         if (tid < C) pbeta = *at_bytes(a.beta + (b * T + t0) * H + h, (unsigned)(min(tid, tlim) * H) * 4u);
     };
-    // v for the chain, in the accumulator layout; rows past the end are multiplied by beta = 0
+    // v for the chain as 16-byte granules (GPR per row); rows past the end read a clamped row
+    // and are multiplied by beta = 0 later, transition columns are zeroed when staged
+    constexpr int VG = 16 / E;                       // elements per granule
+    const int GPR = DVB / VG;                        // granules per row of the value block
+    const bool vblk = MODE == 0 || (int)cb * DVB < dv;   // the block holds value columns
     auto prefetch_v = [&](int64_t t0, int tid) {
-        if (vcols) {
-            const int lane = tid & 63;
-            const int tlim = (int)(t_end - 1 - t0 < C - 1 ? t_end - 1 - t0 : C - 1);
-            const OpT* v_b = gv + ((b * T + t0) * H + h) * (int64_t)dv + colw;      // wave-uniform
+        if (!vblk) return;
+        const int tlim = (int)(t_end - 1 - t0 < C - 1 ? t_end - 1 - t0 : C - 1);
+        const OpT* v_b = gv + ((b * T + t0) * H + h) * (int64_t)dv + (int)cb * DVB;   // uniform
 #pragma unroll
-            for (int p = 0; p < NT; ++p)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    pv[p][r] = to_f32(*at_bytes(v_b, (unsigned)(min(16 * p + 4 * (lane >> 4) + r, tlim) * tok_v + (lane & 15)) * (unsigned)E));
+        for (int u = 0; u < NGV; ++u) {
+            const int gi2 = tid + 512 * u;
+            const int row = gi2 / GPR, gc = gi2 % GPR;
+            const int col = min(gc * VG, dv - (int)cb * DVB - VG);
+            if (row < C) pv[u] = *at_bytes(reinterpret_cast<const g16*>(v_b), (unsigned)(min(row, tlim) * tok_v + col) * (unsigned)E);
         }
     };
+    // staging tile for v (before the chain) and o (after it), over the Kt..QL region, which
+    // is dead between the A / M tiles and the next gate prep
+    OpT* s_vo = s_kt;
+    constexpr int LVO = 128 + PADE;                  // pitch: up to 128 columns
+    static_assert(C * LVO * E <= L.kht - L.kt, "v / o staging tile exceeds the dead operand region");
 
     // ---- start state into accumulator layout: Sacc[tau][r] = S[16 tau + g4 + r][colw + jl]
     f32x4 Sacc[NCT];
@@ -599,6 +612,17 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
         }
         __syncthreads();
 
+        // stage this chunk's v (the A / M operands under it are dead) and load the next chunk's
+        {
+#pragma unroll
+            for (int u = 0; u < NGV; ++u) {
+                const int gi2 = tid + 512 * u;
+                const int row = gi2 / GPR, gc = gi2 % GPR;
+                if (row < C) *reinterpret_cast<g16*>(s_vo + row * LVO + gc * VG) = vblk ? pv[u] : g16{0.f, 0.f, 0.f, 0.f};
+            }
+            if (t0 + C < t_end) prefetch_v(t0 + C, tid);
+        }
+
         // ================= (3) inverses of the diagonal blocks of I + Diag(beta) A (fp32),
         // right-looking: once x_s is final it is subtracted from every later row
         if (wave == 0 && (lane >> 4) < NT) {
@@ -632,29 +656,25 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
             for (int p = 0; p < NT; ++p) {
                 f32x4 R;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) R[r] = s_beta[16 * p + g4 + r] * (pv[p][r] - X[p][r]);
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 16 * p + g4 + r;
+                    R[r] = s_beta[t] * (to_f32(s_vo[t * LVO + 16 * wave + jl]) - X[p][r]);
+                }
 #pragma unroll
                 for (int q = 0; q < p; ++q) R = MF::k16(s_an, LC, 16 * p, 16 * q, ub[q], R, lane);
                 const f32x4 U = MF::k16(s_an, LC, 16 * p, 16 * p, MF::b16(R), f32x4{0.f, 0.f, 0.f, 0.f}, lane);
                 ub[p] = MF::b16(U);
             }
-            // O = QS + M U, stored straight from the accumulators (rows past the end skipped)
+            // O = QS + M U, staged over this wave's own v columns (already consumed)
             if (want_o) {
-                OpT* o_b = go + ((b * T + t0) * H + h) * (int64_t)dv + colw;          // wave-uniform
-                const unsigned o_lane = (unsigned)(g4 * tok_v + jl);
 #pragma unroll
                 for (int p = 0; p < NT; ++p) {
 #pragma unroll
                     for (int q = 0; q <= p; ++q) QS[p] = MF::k16(s_mm, LC, 16 * p, 16 * q, ub[q], QS[p], lane);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int t = 16 * p + g4 + r;
-                        if (t < Tc) *at_bytes(o_b, (o_lane + (unsigned)((16 * p + r) * tok_v)) * (unsigned)E) = from_f32<OpT>(QS[p][r]);
-                    }
+                    for (int r = 0; r < 4; ++r) s_vo[(16 * p + g4 + r) * LVO + 16 * wave + jl] = from_f32<OpT>(QS[p][r]);
                 }
             }
-            // next chunk's v loads once this chunk's are consumed
-            if (t0 + C < t_end) prefetch_v(t0 + C, tid);
             // S <- Diag(e^Gamma_C) S + Khat^T U
 #pragma unroll
             for (int tau = 0; tau < NCT; ++tau) {
@@ -668,6 +688,18 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
                     for (int s2 = 0; s2 < NT / 2; ++s2)
                         Sacc[tau] = MF::k32(s_kht, LC, 16 * tau, 32 * s2, ub[2 * s2], ub[2 * s2 + 1], Sacc[tau], lane);
                 }
+            }
+        }
+        if (want_o) {
+            __syncthreads();                         // every wave's o columns are staged
+            OpT* o_b = go + ((b * T + t0) * H + h) * (int64_t)dv + (int)cb * DVB;   // uniform
+#pragma unroll
+            for (int u = 0; u < NGV; ++u) {
+                const int gi2 = tid + 512 * u;
+                const int row = gi2 / GPR, gc = gi2 % GPR;
+                if (row < Tc)
+                    *at_bytes(reinterpret_cast<g16*>(o_b), (unsigned)(row * tok_v + gc * VG) * (unsigned)E) =
+                        *reinterpret_cast<const g16*>(s_vo + row * LVO + gc * VG);
             }
         }
     }
