@@ -143,10 +143,12 @@ def cpu_baseline_prefill(r, x):
     10 s of CPU work; one process per core, BLAS single-threaded."""
     _CPU.update(x=x, chunk=r.chunk)
     workers = cpu_workers()
-    wall = _run_pool(_oracle_prefill_head, list(range(r.H)), workers)     # one full pass
-    reps = int(max(1, min(64, np.ceil(10.0 / max(wall * workers, 1e-3)))))
-    if reps > 1:
+    reps = 1
+    while True:
         wall = _run_pool(_oracle_prefill_head, list(range(r.H)) * reps, workers)
+        if wall * workers >= 10.0 or reps >= 512:
+            break
+        reps = int(min(512, max(2 * reps, np.ceil(reps * 12.0 / max(wall * workers, 1e-3)))))
     tok = r.B * r.T * reps
     return {"value": tok / wall, "unit": "tokens/s", "cores": workers, "kind": "oracle",
             "sample": f"whole workload (B={r.B} T={r.T} H={r.H}) x{reps}, float64 chunked form "
@@ -258,6 +260,52 @@ def bench_decode(g, torch, rd, d, reps):
     return ms, nsteps
 
 
+# ----------------------------------------------------------------------------- measured HBM traffic
+
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "gated_delta_rule_107_amd", "csrc")
+
+
+def library_source_digest():
+    """sha256 over the library's kernel and ABI sources: a counter table measured on other
+    sources no longer describes the kernels that run."""
+    import hashlib
+    h = hashlib.sha256()
+    files = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".h", ".cpp")))
+    for f in files + ["../../include/kda.h"]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of ``kernel`` from the committed rocprofv3 counter table of
+    ``workload`` (FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by what the same counter
+    reads for a 1 GiB device copy), or None when there is no table for it or the library
+    sources changed since it was taken."""
+    path = os.path.join(PROFILES, f"hbm_traffic__{workload}.md")
+    if not os.path.exists(path):
+        return None
+    digest, fetch_f, write_f, rows = None, None, None, {}
+    for line in open(path):
+        line = line.strip()
+        if line.startswith("source digest:"):
+            digest = line.split(":", 1)[1].strip().strip("`")
+        elif line.startswith("| scale |"):
+            cells = [c.strip() for c in line.strip("|").split("|")]
+            fetch_f, write_f = float(cells[1]), float(cells[2])
+        elif line.startswith("| ") and line.count("|") >= 6 and not line.startswith(("| kernel", "| scale")):
+            cells = [c.strip() for c in line.strip("|").split("|")]
+            try:
+                rows[cells[0]] = (float(cells[2].replace(",", "")), float(cells[3].replace(",", "")))
+            except ValueError:
+                pass
+    if digest != library_source_digest() or fetch_f is None or kernel not in rows:
+        return None
+    fk, wk = rows[kernel]
+    return int(round((fk * fetch_f + wk * write_f) * 1024))
+
+
 def copy_bandwidth(torch, nbytes=1 << 30, reps=10):
     """Device-to-device copy of 1 GiB: the box's achievable-bandwidth reference (read + write)."""
     a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
@@ -330,7 +378,8 @@ def main():
     dom = max(per_launch, key=lambda e: e["ms"])
     roofline = {"bound": "hbm", "kernel": dom["kernel"], "achieved": round(dom["GBps"], 1),
                 "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(dom["GBps"] / PEAK_HBM_GBPS, 4),
-                "traffic": None, "launch_ms": round(dom["ms"], 5), "launch_bytes": dom["bytes"]}
+                "traffic": measured_traffic(r.name, dom["kernel"]), "launch_ms": round(dom["ms"], 5),
+                "launch_bytes": dom["bytes"]}
 
     dec = None
     if d is not None:
@@ -341,7 +390,7 @@ def main():
                "steps_per_interval": nsteps,
                "roofline": {"bound": "hbm", "kernel": "decode_kernel", "achieved": round(dgbps, 1),
                             "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(dgbps / PEAK_HBM_GBPS, 4),
-                            "traffic": None, "launch_bytes": dbytes},
+                            "traffic": measured_traffic(rd.name, "decode_kernel"), "launch_bytes": dbytes},
                "cpu_baseline": cpu_dec}
         log("decode:", json.dumps(dec))
     copy_gbps = copy_bandwidth(torch)
