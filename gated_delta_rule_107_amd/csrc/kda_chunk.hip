@@ -709,13 +709,23 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
         const int lane = threadIdx.x & 63, g4 = 4 * (lane >> 4), jl = lane & 15;
         float* dst = nullptr;
         int64_t ld = 0;
-        int col = colw + jl;
+        const int col = colw + jl;
         if (MODE == 0) {
             if (seg == a.n_seg - 1) { dst = a.s_final + bh * DK * dv; ld = dv; }
         } else if (!mcols) {
             dst = a.s_loc + (bh * a.n_seg + seg) * DK * dv; ld = dv;
         } else {
-            dst = a.m_tr + (bh * a.n_seg + seg) * DK * DK; ld = DK; col -= dv;
+            // the transition goes to the scan already split into bf16 high and low planes
+            bf16* mh = reinterpret_cast<bf16*>(a.m_tr) + (bh * a.n_seg + seg) * 2 * DK * DK + (col - dv);
+#pragma unroll
+            for (int tau = 0; tau < NCT; ++tau)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float x = Sacc[tau][r];
+                    const bf16 hi = (bf16)x;
+                    mh[(16 * tau + g4 + r) * DK] = hi;
+                    mh[DK * DK + (16 * tau + g4 + r) * DK] = (bf16)(x - (float)hi);
+                }
         }
         if (dst) {
 #pragma unroll

@@ -34,7 +34,7 @@ struct ChunkArgs {
     void* o;                // [B,T,H,dv] (mode 0)
     float* s_final;         // [B,H,dk,dv] (mode 0)
     float* s_loc;           // [B,H,P,dk,dv] (mode 1)
-    float* m_tr;            // [B,H,P,dk,dk] (mode 1)
+    void* m_tr;             // [B,H,P][2][dk][dk] bf16 (mode 1): M split into high and low parts
     int64_t B, T;
     int32_t H, dk, dv, chunk;
     int32_t n_seg;          // P
@@ -51,7 +51,7 @@ hipError_t launch_chunk(const ChunkArgs& a, hipStream_t st);
 struct ScanArgs {
     const float* s0;
     const float* s_loc;
-    const float* m_tr;
+    const void* m_tr;       // [B,H,P][2][dk][dk] bf16: high and low parts of M (hi + lo ~ M)
     float* starts;
     int64_t B;
     int32_t H, dk, dv, n_seg;

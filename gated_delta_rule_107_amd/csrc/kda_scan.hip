@@ -5,46 +5,44 @@
 // order recovers each segment's true start state (orkas.ai "Kimi K3
 // architecture", section "The cost comes back in the serving stack").
 //
-// One workgroup per (batch*head, 16-column tile of the state); wave w owns
-// state rows 16w..16w+15.  Each step is a dk x dk by dk x 16
-// product per tile on v_mfma_f32_16x16x32_bf16 with both operands split into
-// bf16 high and low parts (hi*hi + hi*lo + lo*hi, fp32 accumulation: about 16
-// mantissa bits), started from S_loc_i in the accumulator.  The running start
-// state sits in LDS transposed (column-major), so each lane reads its 8
-// contraction values with two 16-byte loads; the next segment's transition rows
-// are loaded into registers while the current step runs.  One extra wave copies
-// each start state from LDS to HBM: the product waves issue only loads, so their
-// in-order memory counter never makes a step wait for the previous step's stores.
-// starts[0] receives a copy of S0 (or zeros), so the pass that follows never
-// reads S0 itself (S0 may alias the final state).
+// One workgroup per (batch*head, 16-column tile of the state); wave w owns state
+// rows 16w..16w+15.  Each step is a dk x dk by dk x 16 product on
+// v_mfma_f32_16x16x32_bf16 with both operands split into bf16 high and low parts
+// (hi*hi + hi*lo + lo*hi, fp32 accumulation: about 16 mantissa bits), started from
+// S_loc_i in the accumulator.
+//
+// The step chain is latency-bound, so nothing but the product sits on it:
+//   * M_i arrives already split (the segment pass writes its high and low bf16
+//     planes) and each wave keeps the rows of the next SCAN_DEPTH transitions in
+//     flight in registers;
+//   * the new start state is split once, by the wave that produced it, into
+//     transposed bf16 high / low copies in LDS that every wave reads as its MFMA
+//     B operand with 16-byte loads;
+//   * one extra wave copies each start state (an fp32 copy in LDS) to HBM, so the
+//     product waves issue only loads.
+// starts[0] receives a copy of S0 (or zeros), so the pass that follows never reads
+// S0 itself (S0 may alias the final state).
 #include "kda_device.h"
 #include "kda_internal.h"
 
 namespace kda {
 
-namespace {
+constexpr int SCAN_DEPTH = 3;   // transitions in flight per wave
 
-__device__ __forceinline__ void split8(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        hi[j] = (bf16)x[j];
-        lo[j] = (bf16)(x[j] - (float)hi[j]);
-    }
-}
-
-}  // namespace
-
-// CT: 16-column tiles per workgroup
-template <int DK, int CT>
-__global__ __launch_bounds__(576) void scan_kernel(ScanArgs a) {
-    constexpr int NW = DK / 16;                   // waves: one 16-row tile of the state each
+template <int DK>
+__global__ __launch_bounds__(64 * (DK / 16 + 1)) void scan_kernel(ScanArgs a) {
+    constexpr int NW = DK / 16;                   // product waves: one 16-row tile of the state each
     constexpr int KSTEP = (DK + 31) / 32;         // 32-deep MFMA steps over the contraction
-    constexpr int LDT = 32 * KSTEP + 4;           // transposed row length (zero padded)
-    __shared__ __attribute__((aligned(16))) float curT[16 * CT * LDT];
+    constexpr int LDB = 32 * KSTEP + 8;           // bf16 pitch of the transposed split copies
+    constexpr int LDF = DK + 4;                   // fp32 pitch of the transposed copy (store wave)
+    constexpr int D = SCAN_DEPTH;
+    __shared__ __attribute__((aligned(16))) bf16 s_hi[16 * LDB];
+    __shared__ __attribute__((aligned(16))) bf16 s_lo[16 * LDB];
+    __shared__ __attribute__((aligned(16))) float s_f[16 * LDF];
 
-    // The column blocks of one (batch, head) are 8 block indices apart, so they run on one
+    // The column tiles of one (batch, head) are 8 block indices apart, so they run on one
     // XCD (workgroups go round-robin over the 8 XCDs) and share its L2 copy of M_i.
-    const int nblk = a.dv / (16 * CT);
+    const int nblk = a.dv / 16;
     int64_t bh;
     int jb;
     {
@@ -60,127 +58,129 @@ __global__ __launch_bounds__(576) void scan_kernel(ScanArgs a) {
         }
     }
     const int P = a.n_seg, dv = a.dv;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int m = lane & 15, g = lane >> 4;
-    const int col0 = 16 * CT * jb + m;            // column of this lane in tile 0 (B / C layouts)
+    const int col = 16 * jb + m;                  // state column of this lane (B / C layouts)
     const int row0 = 16 * w;
+    const bool storer = w == NW;
 
-    const bool storer = w == NW;                  // the extra wave: LDS -> HBM copies only
-
-    for (int i = threadIdx.x; i < 16 * CT * LDT; i += 64 * (NW + 1)) curT[i] = 0.f;
+    // contraction rows past DK (DK = 16) must read as zeros
+    for (int i = threadIdx.x; i < 16 * LDB; i += 64 * (NW + 1)) {
+        s_hi[i] = (bf16)0.f;
+        s_lo[i] = (bf16)0.f;
+    }
     __syncthreads();
 
-    // the store wave writes start state i (in curT) to starts[i]; rows are spread over lanes
+    // publish rows row0 + 4g .. +3 of column m: fp32 for the store wave, split bf16 for the products
+    auto put = [&](const f32x4& x) {
+        *reinterpret_cast<f32x4*>(s_f + m * LDF + row0 + 4 * g) = x;
+        bf16x4 hi, lo;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            hi[j] = (bf16)x[j];
+            lo[j] = (bf16)(x[j] - (float)hi[j]);
+        }
+        *reinterpret_cast<bf16x4*>(s_hi + m * LDB + row0 + 4 * g) = hi;
+        *reinterpret_cast<bf16x4*>(s_lo + m * LDB + row0 + 4 * g) = lo;
+    };
+
+    // the store wave writes start state i (in s_f) to starts[i]; rows spread over lanes
     auto store_start = [&](int i) {
-        float* dst = a.starts + (bh * P + i) * DK * dv + 16 * CT * jb;
-        for (int e = lane; e < DK * CT * 4; e += 64) {            // (row, column quad)
-            const int row = e / (CT * 4), cq = e % (CT * 4);
+        float* dst = a.starts + (bh * P + i) * DK * dv + 16 * jb;
+#pragma unroll
+        for (int it = 0; it < DK / 16; ++it) {                    // (row, column quad) pairs
+            const int e = lane + 64 * it, row = e >> 2, cq = e & 3;
             f32x4 v;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) v[j] = curT[(4 * cq + j) * LDT + row];
+            for (int j = 0; j < 4; ++j) v[j] = s_f[(4 * cq + j) * LDF + row];
             *reinterpret_cast<f32x4*>(dst + (int64_t)row * dv + 4 * cq) = v;
         }
     };
 
-    // start state: rows row0 + 4g + r of each tile's column
     if (!storer) {
+        f32x4 cur;
 #pragma unroll
-        for (int c = 0; c < CT; ++c) {
-            f32x4 cur;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int64_t idx = (int64_t)(row0 + 4 * g + r) * dv + col0 + 16 * c;
-                cur[r] = a.s0 ? a.s0[bh * DK * dv + idx] : 0.f;
-            }
-            *reinterpret_cast<f32x4*>(curT + (16 * c + m) * LDT + row0 + 4 * g) = cur;
-        }
+        for (int r = 0; r < 4; ++r)
+            cur[r] = a.s0 ? a.s0[bh * DK * dv + (int64_t)(row0 + 4 * g + r) * dv + col] : 0.f;
+        put(cur);
     }
 
-    // transition rows of step i: lane (m, g) holds M_i[row0 + m][32 s + 8 g + j]
-    float mrow[KSTEP][8];
-    f32x4 sl[CT];
-    auto load_step = [&](int i) {
-        const float* M = a.m_tr + (bh * P + i) * DK * DK + (int64_t)(row0 + m) * DK;
+    // transition rows of step i into slot u: lane (m, g) holds the high and low parts of
+    // M_i[row0 + m][32 s + 8 g .. + 7]; S_loc_i rows row0 + 4 g + r of column col
+    const bf16* mt = reinterpret_cast<const bf16*>(a.m_tr);    // [B*H][P][2][DK][DK]
+    bf16x8 mh[D][KSTEP], ml[D][KSTEP];
+    f32x4 sl[D];
+    auto load_step = [&](int i, bf16x8 (&h)[KSTEP], bf16x8 (&l)[KSTEP], f32x4& s) {
+        const bf16* Mh = mt + ((bh * P + i) * 2) * DK * DK + (int64_t)(row0 + m) * DK;
+        const bf16* Ml = Mh + DK * DK;
 #pragma unroll
-        for (int s = 0; s < KSTEP; ++s) {
-            const int k0 = 32 * s + 8 * g;
+        for (int t = 0; t < KSTEP; ++t) {
+            const int k0 = 32 * t + 8 * g;
             if (k0 < DK) {
-                const f32x4 lo4 = *reinterpret_cast<const f32x4*>(M + k0);
-                const f32x4 hi4 = *reinterpret_cast<const f32x4*>(M + k0 + 4);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    mrow[s][j] = lo4[j];
-                    mrow[s][4 + j] = hi4[j];
-                }
+                h[t] = *reinterpret_cast<const bf16x8*>(Mh + k0);
+                l[t] = *reinterpret_cast<const bf16x8*>(Ml + k0);
             } else {
 #pragma unroll
-                for (int j = 0; j < 8; ++j) mrow[s][j] = 0.f;
+                for (int j = 0; j < 8; ++j) h[t][j] = l[t][j] = (bf16)0.f;
             }
         }
         const float* L = a.s_loc + (bh * P + i) * DK * dv;
 #pragma unroll
-        for (int c = 0; c < CT; ++c)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sl[c][r] = L[(int64_t)(row0 + 4 * g + r) * dv + col0 + 16 * c];
+        for (int r = 0; r < 4; ++r) s[r] = L[(int64_t)(row0 + 4 * g + r) * dv + col];
     };
-    if (P > 1 && !storer) load_step(0);
+    const int nsteps = P - 1;
+    if (nsteps > 0 && !storer) {
+#pragma unroll
+        for (int u = 0; u < D; ++u) load_step(min(u, nsteps - 1), mh[u], ml[u], sl[u]);
+    }
 
-    for (int i = 0; i + 1 < P; ++i) {
-        __syncthreads();                          // curT holds the start of segment i
-        if (storer) {
+    // The store wave and the product waves run separate loops with the same barriers, so the
+    // product loop holds loads only and its memory counter waits cover exactly one slot.
+    if (storer) {
+        for (int i = 0; i < nsteps; ++i) {
+            __syncthreads();                      // LDS holds the start of segment i
             store_start(i);
             __syncthreads();
-            continue;
         }
-        bf16x8 ahi[KSTEP], alo[KSTEP];
-#pragma unroll
-        for (int s = 0; s < KSTEP; ++s) split8(mrow[s], ahi[s], alo[s]);
-        f32x4 acc[CT], acc2[CT];
-#pragma unroll
-        for (int c = 0; c < CT; ++c) {
-            acc[c] = sl[c];
-            acc2[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-        if (i + 2 < P) load_step(i + 1);          // next transition loads during this step
-#pragma unroll
-        for (int c = 0; c < CT; ++c)
-#pragma unroll
-            for (int s = 0; s < KSTEP; ++s) {
-                const float* src = curT + (16 * c + m) * LDT + 32 * s + 8 * g;
-                const f32x4 b0 = *reinterpret_cast<const f32x4*>(src);
-                const f32x4 b1 = *reinterpret_cast<const f32x4*>(src + 4);
-                float x[8];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    x[j] = b0[j];
-                    x[4 + j] = b1[j];
-                }
-                bf16x8 bhi, blo;
-                split8(x, bhi, blo);
-                acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[s], bhi, acc[c], 0, 0, 0);
-                acc2[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[s], blo, acc2[c], 0, 0, 0);
-                acc2[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[s], bhi, acc2[c], 0, 0, 0);
-            }
-        __syncthreads();                          // every wave has read curT
-#pragma unroll
-        for (int c = 0; c < CT; ++c)
-            *reinterpret_cast<f32x4*>(curT + (16 * c + m) * LDT + row0 + 4 * g) = acc[c] + acc2[c];
+        __syncthreads();
+        store_start(P - 1);
+        return;
     }
+    // one step: the start of segment i (in LDS) times M_i plus S_loc_i, from slot u
+    auto step = [&](int i, int u, bool refill) {
+        __syncthreads();                          // LDS holds the start of segment i
+        f32x4 acc = sl[u], acc2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < KSTEP; ++t) {
+            const bf16x8 bh8 = *reinterpret_cast<const bf16x8*>(s_hi + m * LDB + 32 * t + 8 * g);
+            const bf16x8 bl8 = *reinterpret_cast<const bf16x8*>(s_lo + m * LDB + 32 * t + 8 * g);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mh[u][t], bh8, acc, 0, 0, 0);
+            acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mh[u][t], bl8, acc2, 0, 0, 0);
+            acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ml[u][t], bh8, acc2, 0, 0, 0);
+        }
+        // the slot's registers are consumed: refill it with step i + D (clamped)
+        if (refill) load_step(min(i + D, nsteps - 1), mh[u], ml[u], sl[u]);
+        __syncthreads();                          // every wave has read the start of segment i
+        put(acc + acc2);
+    };
+    // Whole groups of D steps per iteration, so every slot keeps its registers across the
+    // back edge and the loop is entered only with the slots in load order; the last
+    // nsteps % D steps follow it.
+    int i = 0;
+    for (; i + D <= nsteps; i += D) {
+#pragma unroll
+        for (int u = 0; u < D; ++u) step(i + u, u, true);
+    }
+#pragma unroll
+    for (int u = 0; u < D - 1; ++u)
+        if (i + u < nsteps) step(i + u, u, false);
     __syncthreads();
-    if (storer) store_start(P - 1);
 }
 
 template <int DK>
 static hipError_t launch_scan_dk(const ScanArgs& a, hipStream_t st) {
-    const int ct = 1;
-    const unsigned nblk = (unsigned)(a.B * a.H * (a.dv / (16 * ct)));
-    const dim3 block(64 * (DK / 16 + 1));
-    switch (ct) {
-        case 1: hipLaunchKernelGGL((scan_kernel<DK, 1>), dim3(nblk), block, 0, st, a); break;
-        case 2: hipLaunchKernelGGL((scan_kernel<DK, 2>), dim3(nblk), block, 0, st, a); break;
-        case 4: hipLaunchKernelGGL((scan_kernel<DK, 4>), dim3(nblk), block, 0, st, a); break;
-        default: return hipErrorInvalidValue;
-    }
+    const unsigned nblk = (unsigned)(a.B * a.H * (a.dv / 16));
+    hipLaunchKernelGGL((scan_kernel<DK>), dim3(nblk), dim3(64 * (DK / 16 + 1)), 0, st, a);
     return hipGetLastError();
 }
 
