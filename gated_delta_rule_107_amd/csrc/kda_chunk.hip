@@ -26,16 +26,17 @@
 // diagonal tile), f = 1 for adjacent sub-tiles and f = e^(r_p - r_pp+1) (<= 1)
 // further below; f is applied to the left operand in registers.
 //
-// Per chunk: (1) gate prep from registers prefetched one chunk ahead, writing
-// the operands above to LDS; (2) A / M tiles on MFMA and X = Kt S, QS = Qt S;
-// (3) the four 16x16 diagonal blocks of (I + Diag(beta) A) inverted by fp32
-// forward substitution; (4) the state chain, per wave on its 16 state columns:
-// the block triangular solve for U runs on MFMA straight from registers
-// (U_p = N_pp (R_p - sum_q Ab_pq U_q)), then O and the state update.  The
-// fp32 state stays in MFMA accumulators for the whole sequence; accumulator
-// tiles feed the next product's B operand directly (the contraction index is
-// taken in the order the accumulator layout holds it, and the LDS operand is
-// read in that same order).
+// Per chunk: gate prep from registers prefetched a chunk ahead writes the operands
+// above to LDS; A / M tiles run on MFMA together with X = Kt S, QS = Qt S; the four
+// 16x16 diagonal blocks of (I + Diag(beta) A) are inverted by fp32 forward
+// substitution; then the state chain runs per wave on its 16 state columns: the
+// block triangular solve for U on MFMA straight from registers
+// (U_p = N_pp (R_p - sum_q Ab_pq U_q)), O, and the state update.  The loop is
+// software-pipelined by one chunk: the chain of chunk n (MFMA latency) shares its
+// barrier interval with the gate prep of chunk n+1 (VALU work).  The fp32 state
+// stays in MFMA accumulators for the whole sequence; accumulator tiles feed the next
+// product's B operand directly (the contraction index is taken in the order the
+// accumulator layout holds it, and the LDS operand is read in that same order).
 //
 // bf16 inputs use v_mfma_f32_16x16x32_bf16 / v_mfma_f32_16x16x16_bf16 with
 // fp32 accumulation; float32 inputs use v_mfma_f32_16x16x4_f32 throughout.
@@ -137,6 +138,8 @@ template <typename T> __device__ __forceinline__ const T* at_bytes(const T* base
     return reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + byte_off);
 }
 
+template <bool V> struct BoolC { static constexpr bool value = V; };
+
 // ---------------------------------------------------------------- element access
 template <typename OpT> struct Ld4;             // 4 consecutive elements <-> float[4]
 template <> struct Ld4<bf16> {
@@ -192,14 +195,16 @@ __host__ __device__ constexpr Lds lds_layout(int E, int DK, int C) {
     L.rh = off;   off += align16(C * LDK * E);
     L.rd = off;   off += RV ? align16(C * LDK * E) : 0;
     L.rf = off;   off += (RV && NT == 4) ? align16(48 * LDK * E) : 0;
+    // the Kt..RF region also holds the v and o staging tiles (C rows, up to 128 columns each)
+    if (off - L.kt < 2 * C * (128 + PADE) * E) off = L.kt + align16(2 * C * (128 + PADE) * E);
     L.kht = off;  off += align16(DK * LC * E);
     L.an = off;   off += align16(C * LC * E);
     L.mm = off;   off += align16(C * LC * E);
     L.ad = off;   off += align16(NT * 16 * 16 * 4);
     L.fd = off;   off += RV ? 0 : align16(NT * DKP * 4);
     L.fo = off;   off += RV ? 0 : align16(3 * DKP * 4);
-    L.egc = off;  off += align16(DKP * 4);
-    L.beta = off; off += align16(C * 4);
+    L.egc = off;  off += align16(2 * DKP * 4);   // two slots: chunk n and chunk n+1
+    L.beta = off; off += align16(2 * C * 4);
     L.total = off;
     return L;
 }
@@ -295,7 +300,7 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
     const int tok_k = H * DK;                        // elements between tokens in q, k, log_alpha
     const int tok_v = H * dv;                        // ... in v and o
 
-    // ---- zero LDS once: padding channels (DK < 32) stay zero for the natural-order loads
+    // ---- zero LDS once (gate prep clears the padding channels of DK < 32 with every chunk)
     for (int i = threadIdx.x * 16; i < L.total; i += 512 * 16)
         *reinterpret_cast<f32x4*>(smem + i) = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -345,6 +350,13 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
     // and are multiplied by beta = 0 later, transition columns are zeroed when staged
     constexpr int VG = 16 / E;                       // elements per granule
     const int GPR = DVB / VG;                        // granules per row of the value block
+    // granule index -> (row, granule column) without a division per use: multiply by the
+    // rounded-up reciprocal 2^32 / GPR and keep the high word (exact for indices < 2^16)
+    const unsigned gpr_magic = 0xFFFFFFFFu / (unsigned)GPR + 1u;
+    auto granule = [&](int gi2, int& row, int& gc) {
+        row = (int)__umulhi((unsigned)gi2, gpr_magic);
+        gc = gi2 - row * GPR;
+    };
     const bool vblk = MODE == 0 || (int)cb * DVB < dv;   // the block holds value columns
     auto prefetch_v = [&](int64_t t0, int tid) {
         if (!vblk) return;
@@ -353,16 +365,18 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
 #pragma unroll
         for (int u = 0; u < NGV; ++u) {
             const int gi2 = tid + 512 * u;
-            const int row = gi2 / GPR, gc = gi2 % GPR;
+            int row, gc;
+            granule(gi2, row, gc);
             const int col = min(gc * VG, dv - (int)cb * DVB - VG);
             if (row < C) pv[u] = *at_bytes(reinterpret_cast<const g16*>(v_b), (unsigned)(min(row, tlim) * tok_v + col) * (unsigned)E);
         }
     };
-    // staging tile for v (before the chain) and o (after it), over the Kt..QL region, which
-    // is dead between the A / M tiles and the next gate prep
-    OpT* s_vo = s_kt;
+    // staging tiles for v (the next chunk's, before its chain) and o (this chunk's, after its
+    // chain) over the Kt..RF region, which is dead between the A / M tiles and the next gate prep
     constexpr int LVO = 128 + PADE;                  // pitch: up to 128 columns
-    static_assert(C * LVO * E <= L.kht - L.kt, "v / o staging tile exceeds the dead operand region");
+    OpT* s_v = s_kt;
+    OpT* s_o = s_kt + C * LVO;
+    static_assert(2 * C * LVO * E <= L.kht - L.kt, "v / o staging tiles exceed the dead operand region");
 
     // ---- start state into accumulator layout: Sacc[tau][r] = S[16 tau + g4 + r][colw + jl]
     f32x4 Sacc[NCT];
@@ -390,13 +404,34 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
     }
 
     __builtin_amdgcn_s_waitcnt(0x0F70);              // vmcnt(0): the start state is in registers
-    if (t_begin < t_end) {
+    const int64_t nchunks = t_end > t_begin ? (t_end - t_begin + C - 1) / C : 0;
+    if (nchunks > 0) {
         prefetch_gates(t_begin, threadIdx.x);
         prefetch_v(t_begin, threadIdx.x);
     }
 
-    for (int64_t t0 = t_begin; t0 < t_end; t0 += C) {
-        const int Tc = (int)(t_end - t0 < C ? t_end - t0 : C);
+    // Software pipeline over chunks.  Iteration n runs the state chain of chunk n and prepares
+    // chunk n+1; its four barriers separate
+    //   (1) chain(n) [R, U, O, S update]  +  gate prep(n+1)    (MFMA latency next to VALU work)
+    //   (2) Khat^T(n+1) to LDS, X / QS(n+1) from the updated state, A / M tiles(n+1)
+    //   (3) diagonal-block inverses(n+1), v(n+1) and o(n) into the staging tiles
+    //   (4) o(n) to HBM, v(n+1) into registers in the accumulator layout.
+    // beta and e^Gamma_C of chunk n are read in (1) while gate prep writes chunk n+1's, so
+    // they have two slots (chunk n uses slot n & 1); Khat^T(n+1) waits in registers until (2).
+    f32x4 X[NT], QS[NT];                             // Kt S, Qt S of the chunk chained next
+    B16 vr[NT], orr[NT];                             // its v, and o of the chunk just chained
+    V4 khr[4];                                       // Khat^T(n+1): 4 channels x 4 tokens
+
+    auto body = [&](auto cur_c, auto nxt_c, int64_t n) {
+        constexpr bool cur = decltype(cur_c)::value;  // a chain runs (chunk n exists)
+        constexpr bool nxt = decltype(nxt_c)::value;  // chunk n+1 exists
+        const int64_t t0 = t_begin + n * C, t1 = t0 + C;
+        const int Tc = cur ? (int)(t_end - t0 < C ? t_end - t0 : C) : 0;
+        const int Tn = nxt ? (int)(t_end - t1 < C ? t_end - t1 : C) : 0;
+        float* sb_c = s_beta + (int)(n & 1) * C;
+        float* eg_c = s_egc + (int)(n & 1) * DKP;
+        float* sb_n = s_beta + (int)((n + 1) & 1) * C;
+        float* eg_n = s_egc + (int)((n + 1) & 1) * DKP;
         int tid_opaque = threadIdx.x;
         asm volatile("" : "+v"(tid_opaque));
         const int tid = tid_opaque, lane = tid & 63;
@@ -405,39 +440,50 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
         const int tq = 4 * gp + gi;
         const int gc0 = 16 * wave + 4 * gx;
         const bool gact = gc0 < DK && gp < NT;
-        __syncthreads();   // previous chunk's readers of LDS are done
+        __syncthreads();   // the previous iteration's readers of the staging tiles are done
 
-        // ================= (1) gate prep (log-decays in log2 units from here on)
-        if (tid < C) s_beta[tid] = tid < Tc ? pbeta : 0.f;
-        {
+        // ================= (1a) chain of chunk n: R_p = beta (V - X); U_p = N_pp (R_p - sum_{q<p} Ab_pq U_q)
+        B16 ub[NT];
+        if constexpr (cur) {
+#pragma unroll
+            for (int p = 0; p < NT; ++p) {
+                f32x4 R;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) R[r] = sb_c[16 * p + g4 + r] * ((float)vr[p][r] - X[p][r]);
+#pragma unroll
+                for (int q = 0; q < p; ++q) R = MF::k16(s_an, LC, 16 * p, 16 * q, ub[q], R, lane);
+                const f32x4 U = MF::k16(s_an, LC, 16 * p, 16 * p, MF::b16(R), f32x4{0.f, 0.f, 0.f, 0.f}, lane);
+                ub[p] = MF::b16(U);
+            }
+        }
+
+        // ================= (1c) O = QS + M U of chunk n, kept in registers until (3)
+        if constexpr (cur && want_o) {
+#pragma unroll
+            for (int p = 0; p < NT; ++p) {
+#pragma unroll
+                for (int qq = 0; qq <= p; ++qq) QS[p] = MF::k16(s_mm, LC, 16 * p, 16 * qq, ub[qq], QS[p], lane);
+                orr[p] = MF::b16(QS[p]);
+            }
+        }
+
+        // ================= (1b) gate prep of chunk n+1 (log-decays in log2 units from here on)
+        float g2[4][4];
+        float pre[4], tot[4], rp[4], after[4], gcs[4], tn1[4], tn2[4], tm1[4], tm2[4];
+        const bool full = !(NT < 4 || Tn < C);
+        if constexpr (nxt) {
+            if (tid < C) sb_n[tid] = tid < Tn ? pbeta : 0.f;
             // Every lane runs the cross-lane scans; only stores are guarded.  Tokens past the
             // end (and lanes past the last sub-tile) read clamped addresses: zero them.  Full
             // chunks of 4 sub-tiles need no mask (idle channel lanes of DK < 128 only feed
-            // their own 16-lane rows, whose stores are skipped).
-            float k[4][4], q[4][4], g2[4][4];
+            // their own 16-lane rows, whose stores are skipped).  k and q stay in their packed
+            // prefetch registers until they are used.
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                L4::to_f(pk[j], k[j]);
-                if (want_o) L4::to_f(pq[j], q[j]);
+                const bool ok = full || 4 * tq + j < Tn;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    g2[j][e] = clamp_log_alpha(pla[j][e]) * LOG2E;
-                    if (!want_o) q[j][e] = 0.f;
-                }
+                for (int e = 0; e < 4; ++e) g2[j][e] = ok ? clamp_log_alpha(pla[j][e]) * LOG2E : 0.f;
             }
-            if (NT < 4 || Tc < C) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const bool ok = 4 * tq + j < Tc;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        g2[j][e] = ok ? g2[j][e] : 0.f;
-                        k[j][e] = ok ? k[j][e] : 0.f;
-                        q[j][e] = ok ? q[j][e] : 0.f;
-                    }
-                }
-            }
-            float pre[4], tot[4], rp[4], after[4], gcs[4], tn1[4], tn2[4], tm1[4], tm2[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float loc = g2[0][e] + g2[1][e] + g2[2][e] + g2[3][e];
@@ -449,7 +495,7 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
                 // sub-tile totals from lane 12 + x of every row
                 float tp[4];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) tp[q] = q < NT ? __shfl(inc, 16 * q + 12 + gx, 64) : 0.f;
+                for (int qq = 0; qq < 4; ++qq) tp[qq] = qq < NT ? __shfl(inc, 16 * qq + 12 + gx, 64) : 0.f;
                 tot[e] = gp == 0 ? tp[0] : gp == 1 ? tp[1] : gp == 2 ? tp[2] : tp[3];
                 rp[e] = (gp > 0 ? tp[0] : 0.f) + (gp > 1 ? tp[1] : 0.f) + (gp > 2 ? tp[2] : 0.f);  // r_p
                 after[e] = (gp < 1 ? tp[1] : 0.f) + (gp < 2 ? tp[2] : 0.f) + (gp < 3 ? tp[3] : 0.f);
@@ -459,10 +505,14 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
                 tm1[e] = gp == 1 ? tp[0] : gp == 2 ? tp[1] : gp == 3 ? tp[2] : 0.f;   // p-1
                 tm2[e] = gp == 2 ? tp[0] : gp == 3 ? tp[1] : 0.f;                      // p-2
             }
+        }
+
+        // ================= (1d) gate prep of chunk n+1: operands to LDS
+        if constexpr (nxt) {
             if (gact && gi == 0) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    if (gp == 0) s_egc[gc0 + e] = fast_exp2(gcs[e]);
+                    if (gp == 0) eg_n[gc0 + e] = fast_exp2(gcs[e]);
                     if (!RV) {
                         s_fd[gp * DKP + gc0 + e] = fast_exp2(-tot[e]);                               // e^-tot_p
                         if (NT == 4 && gp == 2) s_fo[0 * DKP + gc0 + e] = fast_exp2(tm1[e]);          // (2,0)
@@ -486,10 +536,18 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
                         ef2[e] = fast_exp2(tn1[e] + tn2[e]);
                     }
                 }
-                float kht[4][4];                          // [channel][token]
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int t = 4 * tq + j;
+                    const bool ok = full || t < Tn;
+                    float k[4][4], q[4][4];
+                    L4::to_f(pk[j], k[j]);
+                    if (want_o) L4::to_f(pq[j], q[j]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        k[j][e] = ok ? k[j][e] : 0.f;
+                        q[j][e] = (want_o && ok) ? q[j][e] : 0.f;
+                    }
                     float kl[4], ql[4], rh[4], kt[4], qt[4], rd[4], rf1[4], rf2[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
@@ -500,7 +558,7 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
                         rh[e] = k[j][e] * e2;
                         kt[e] = kl[e] * er[e];
                         qt[e] = ql[e] * er[e];
-                        kht[e][j] = rh[e] * eh[e];
+                        khr[e][j] = from_f32<OpT>(rh[e] * eh[e]);    // Khat^T: [channel][token]
                         if (RV) {
                             rd[e] = rh[e] * ed[e];                    // k e^-gamma, <= e^80
                             rf1[e] = rh[e] * ef1[e];                  // referenced at the end of p+1
@@ -520,39 +578,76 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
                         if (NT == 4 && gp == 0) *reinterpret_cast<V4*>(s_rf + (32 + t) * LDK + gc0) = L4::from_f(rf2);
                     }
                 }
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    *reinterpret_cast<V4*>(s_kht + (gc0 + e) * LC + 4 * tq) = L4::from_f(kht[e]);
             }
         }
-        // next chunk's gates, keys and queries load while this chunk computes
-        if (t0 + C < t_end) prefetch_gates(t0 + C, tid);
-        __syncthreads();
 
-        // ================= (2) X = Kt S and QS = Qt S, then the A / M tiles
-        f32x4 X[NT], QS[NT];
-        if (chain) {
-            B16 sb[NCT];
+        if constexpr (nxt && DK < DKP) {
+            // channels DK..DKP-1 pad the 32-deep natural-order products; the staging tiles
+            // overwrite them, so they are cleared with every chunk's operands
+            if (gc0 >= DK && gc0 < DKP && gp < NT) {
 #pragma unroll
-            for (int tau = 0; tau < NCT; ++tau) sb[tau] = MF::b16(Sacc[tau]);
-#pragma unroll
-            for (int p = 0; p < NT; ++p) {
-                X[p] = f32x4{0.f, 0.f, 0.f, 0.f};
-                QS[p] = f32x4{0.f, 0.f, 0.f, 0.f};
-                if constexpr (NCT == 1) {
-                    X[p] = MF::k16(s_kt, LKQ, 16 * p, 0, sb[0], X[p], lane);
-                    if (want_o) QS[p] = MF::k16(s_qt, LKQ, 16 * p, 0, sb[0], QS[p], lane);
-                } else {
-#pragma unroll
-                    for (int s2 = 0; s2 < NCT / 2; ++s2) {
-                        X[p] = MF::k32(s_kt, LKQ, 16 * p, 32 * s2, sb[2 * s2], sb[2 * s2 + 1], X[p], lane);
-                        if (want_o)
-                            QS[p] = MF::k32(s_qt, LKQ, 16 * p, 32 * s2, sb[2 * s2], sb[2 * s2 + 1], QS[p], lane);
+                for (int j = 0; j < 4; ++j) {
+                    const int t = 4 * tq + j;
+                    const V4 z = L4::zero();
+                    *reinterpret_cast<V4*>(s_kl + t * LDK + gc0) = z;
+                    *reinterpret_cast<V4*>(s_ql + t * LDK + gc0) = z;
+                    *reinterpret_cast<V4*>(s_rh + t * LDK + gc0) = z;
+                    if (RV) {
+                        *reinterpret_cast<V4*>(s_rd + t * LDK + gc0) = z;
+                        if (NT == 4 && gp <= 1) *reinterpret_cast<V4*>(s_rf + t * LDK + gc0) = z;
+                        if (NT == 4 && gp == 0) *reinterpret_cast<V4*>(s_rf + (32 + t) * LDK + gc0) = z;
                     }
                 }
             }
         }
-        {
+
+        // ================= (1e) S <- Diag(e^Gamma_C) S + Khat^T U for chunk n
+        if constexpr (cur) {
+#pragma unroll
+            for (int tau = 0; tau < NCT; ++tau) {
+                const f32x4 eg = *reinterpret_cast<const f32x4*>(eg_c + 16 * tau + g4);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Sacc[tau][r] *= eg[r];
+                if constexpr (NT == 1) {
+                    Sacc[tau] = MF::k16(s_kht, LC, 16 * tau, 0, ub[0], Sacc[tau], lane);
+                } else {
+#pragma unroll
+                    for (int s2 = 0; s2 < NT / 2; ++s2)
+                        Sacc[tau] = MF::k32(s_kht, LC, 16 * tau, 32 * s2, ub[2 * s2], ub[2 * s2 + 1], Sacc[tau], lane);
+                }
+            }
+        }
+        // chunk n+2's gates, keys and queries load while chunk n+1 is processed
+        if (nxt && n + 2 < nchunks) prefetch_gates(t1 + C, tid);
+        __syncthreads();
+
+        // ================= (2) Khat^T(n+1) to LDS; X = Kt S and QS = Qt S; the A / M tiles
+        if constexpr (nxt) {
+            if (gact) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) *reinterpret_cast<V4*>(s_kht + (gc0 + e) * LC + 4 * tq) = khr[e];
+            }
+            {
+                B16 sb[NCT];
+#pragma unroll
+                for (int tau = 0; tau < NCT; ++tau) sb[tau] = MF::b16(Sacc[tau]);
+#pragma unroll
+                for (int p = 0; p < NT; ++p) {
+                    X[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    QS[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    if constexpr (NCT == 1) {
+                        X[p] = MF::k16(s_kt, LKQ, 16 * p, 0, sb[0], X[p], lane);
+                        if (want_o) QS[p] = MF::k16(s_qt, LKQ, 16 * p, 0, sb[0], QS[p], lane);
+                    } else {
+#pragma unroll
+                        for (int s2 = 0; s2 < NCT / 2; ++s2) {
+                            X[p] = MF::k32(s_kt, LKQ, 16 * p, 32 * s2, sb[2 * s2], sb[2 * s2 + 1], X[p], lane);
+                            if (want_o)
+                                QS[p] = MF::k32(s_qt, LKQ, 16 * p, 32 * s2, sb[2 * s2], sb[2 * s2 + 1], QS[p], lane);
+                        }
+                    }
+                }
+            }
             // up to 3 tile tasks per wave; every task's loads and products come before any
             // of the wave's stores
             constexpr int NPAIR = NT * (NT + 1) / 2;
@@ -596,14 +691,14 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
                         // diagonal block of beta A, strictly lower, stored transposed: [p][s][t]
                         f32x4 col;
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) col[r] = (jl < g4 + r) ? acc[sl][r] * s_beta[16 * p + g4 + r] : 0.f;
+                        for (int r = 0; r < 4; ++r) col[r] = (jl < g4 + r) ? acc[sl][r] * sb_n[16 * p + g4 + r] : 0.f;
                         *reinterpret_cast<f32x4*>(s_ad + (p * 16 + jl) * 16 + g4) = col;
                     } else {
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             const int tr = g4 + r;
                             const int t = 16 * p + tr, s = 16 * pp + jl;
-                            if (!isM) s_an[t * LC + s] = from_f32<OpT>(-acc[sl][r] * s_beta[t]);
+                            if (!isM) s_an[t * LC + s] = from_f32<OpT>(-acc[sl][r] * sb_n[t]);
                             else s_mm[t * LC + s] = from_f32<OpT>((p == pp && jl > tr) ? 0.f : acc[sl][r]);
                         }
                     }
@@ -612,96 +707,75 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
         }
         __syncthreads();
 
-        // stage this chunk's v (the A / M operands under it are dead) and load the next chunk's
-        {
+        // ================= (3) inverses of the diagonal blocks of I + Diag(beta) A (fp32),
+        // right-looking: once x_s is final it is subtracted from every later row
+        if constexpr (nxt) {
+            if (wave == 0 && (lane >> 4) < NT) {
+                const int p = lane >> 4, j = lane & 15;
+                const float* Ab = s_ad + p * 256;                // column s at Ab[16 s .. 16 s + 15]
+                float x[16];
+#pragma unroll
+                for (int t = 0; t < 16; ++t) x[t] = (t == j) ? 1.f : 0.f;
+#pragma unroll
+                for (int s = 0; s < 15; ++s) {
+                    float col[16];
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const f32x4 c4 = *reinterpret_cast<const f32x4*>(Ab + 16 * s + 4 * q4);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) col[4 * q4 + e] = c4[e];
+                    }
+#pragma unroll
+                    for (int t = s + 1; t < 16; ++t) x[t] -= col[t] * x[s];
+                }
+#pragma unroll
+                for (int t = 0; t < 16; ++t) s_an[(16 * p + t) * LC + 16 * p + j] = from_f32<OpT>(x[t]);
+            }
+            // v(n+1) into its staging tile (transition columns of pass 1 read zeros)
 #pragma unroll
             for (int u = 0; u < NGV; ++u) {
                 const int gi2 = tid + 512 * u;
-                const int row = gi2 / GPR, gc = gi2 % GPR;
-                if (row < C) *reinterpret_cast<g16*>(s_vo + row * LVO + gc * VG) = vblk ? pv[u] : g16{0.f, 0.f, 0.f, 0.f};
+                int row, gc;
+            granule(gi2, row, gc);
+                if (row < C) *reinterpret_cast<g16*>(s_v + row * LVO + gc * VG) = vblk ? pv[u] : g16{0.f, 0.f, 0.f, 0.f};
             }
-            if (t0 + C < t_end) prefetch_v(t0 + C, tid);
+            if (n + 2 < nchunks) prefetch_v(t1 + C, tid);
         }
-
-        // ================= (3) inverses of the diagonal blocks of I + Diag(beta) A (fp32),
-        // right-looking: once x_s is final it is subtracted from every later row
-        if (wave == 0 && (lane >> 4) < NT) {
-            const int p = lane >> 4, j = lane & 15;
-            const float* Ab = s_ad + p * 256;                // column s at Ab[16 s .. 16 s + 15]
-            float x[16];
+        if constexpr (cur && want_o) {
+            if (chain) {
 #pragma unroll
-            for (int t = 0; t < 16; ++t) x[t] = (t == j) ? 1.f : 0.f;
+                for (int p = 0; p < NT; ++p)
 #pragma unroll
-            for (int s = 0; s < 15; ++s) {
-                float col[16];
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const f32x4 c4 = *reinterpret_cast<const f32x4*>(Ab + 16 * s + 4 * q4);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) col[4 * q4 + e] = c4[e];
-                }
-#pragma unroll
-                for (int t = s + 1; t < 16; ++t) x[t] -= col[t] * x[s];
+                    for (int r = 0; r < 4; ++r) s_o[(16 * p + g4 + r) * LVO + 16 * wave + jl] = orr[p][r];
             }
-#pragma unroll
-            for (int t = 0; t < 16; ++t) s_an[(16 * p + t) * LC + 16 * p + j] = from_f32<OpT>(x[t]);
         }
         __syncthreads();
 
-        // ================= (4) the state chain on this wave's 16 columns
-        if (chain) {
-            // R_p = beta (V - X);  U_p = N_pp (R_p - sum_{q<p} Ab_pq U_q)
-            B16 ub[NT];
-#pragma unroll
-            for (int p = 0; p < NT; ++p) {
-                f32x4 R;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = 16 * p + g4 + r;
-                    R[r] = s_beta[t] * (to_f32(s_vo[t * LVO + 16 * wave + jl]) - X[p][r]);
-                }
-#pragma unroll
-                for (int q = 0; q < p; ++q) R = MF::k16(s_an, LC, 16 * p, 16 * q, ub[q], R, lane);
-                const f32x4 U = MF::k16(s_an, LC, 16 * p, 16 * p, MF::b16(R), f32x4{0.f, 0.f, 0.f, 0.f}, lane);
-                ub[p] = MF::b16(U);
-            }
-            // O = QS + M U, staged over this wave's own v columns (already consumed)
-            if (want_o) {
-#pragma unroll
-                for (int p = 0; p < NT; ++p) {
-#pragma unroll
-                    for (int q = 0; q <= p; ++q) QS[p] = MF::k16(s_mm, LC, 16 * p, 16 * q, ub[q], QS[p], lane);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) s_vo[(16 * p + g4 + r) * LVO + 16 * wave + jl] = from_f32<OpT>(QS[p][r]);
-                }
-            }
-            // S <- Diag(e^Gamma_C) S + Khat^T U
-#pragma unroll
-            for (int tau = 0; tau < NCT; ++tau) {
-                const f32x4 eg = *reinterpret_cast<const f32x4*>(s_egc + 16 * tau + g4);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) Sacc[tau][r] *= eg[r];
-                if constexpr (NT == 1) {
-                    Sacc[tau] = MF::k16(s_kht, LC, 16 * tau, 0, ub[0], Sacc[tau], lane);
-                } else {
-#pragma unroll
-                    for (int s2 = 0; s2 < NT / 2; ++s2)
-                        Sacc[tau] = MF::k32(s_kht, LC, 16 * tau, 32 * s2, ub[2 * s2], ub[2 * s2 + 1], Sacc[tau], lane);
-                }
-            }
-        }
-        if (want_o) {
-            __syncthreads();                         // every wave's o columns are staged
+        // ================= (4) o(n) to HBM; v(n+1) into the accumulator layout
+        if constexpr (cur && want_o) {
             OpT* o_b = go + ((b * T + t0) * H + h) * (int64_t)dv + (int)cb * DVB;   // uniform
 #pragma unroll
             for (int u = 0; u < NGV; ++u) {
                 const int gi2 = tid + 512 * u;
-                const int row = gi2 / GPR, gc = gi2 % GPR;
+                int row, gc;
+            granule(gi2, row, gc);
                 if (row < Tc)
                     *at_bytes(reinterpret_cast<g16*>(o_b), (unsigned)(row * tok_v + gc * VG) * (unsigned)E) =
-                        *reinterpret_cast<const g16*>(s_vo + row * LVO + gc * VG);
+                        *reinterpret_cast<const g16*>(s_o + row * LVO + gc * VG);
             }
         }
+        if constexpr (nxt) {
+#pragma unroll
+            for (int p = 0; p < NT; ++p)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) vr[p][r] = s_v[(16 * p + g4 + r) * LVO + 16 * wave + jl];
+        }
+    };
+
+    if (nchunks > 0) {
+        body(BoolC<false>{}, BoolC<true>{}, -1);
+        for (int64_t n = 0; n + 1 < nchunks; ++n) body(BoolC<true>{}, BoolC<true>{}, n);
+        body(BoolC<true>{}, BoolC<false>{}, nchunks - 1);
     }
 
     // ---- final state of this unit
