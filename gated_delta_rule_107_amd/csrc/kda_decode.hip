@@ -10,38 +10,53 @@
 // serving stack").
 //
 // HBM-bound: the fp32 state is read once and written once; everything else is
-// a few hundred bytes per (n, h).  One workgroup per (n, h); thread (rg, cg)
-// holds rows rg, rg+RG, ... of the 4 state columns cg*4..cg*4+3 in registers,
-// so the state never leaves registers between its load and its store.
+// a few hundred bytes per (n, h).  One workgroup per (n, h) with up to 1024 threads:
+// thread (rg, cg) holds rows rg, rg+RG, ... of the 4 state columns cg*4..cg*4+3 in
+// registers, so the state never leaves registers between its load and its store, and
+// each thread has only a few 16-byte loads in flight (a wide workgroup with short
+// per-thread streams keeps more of HBM busy than a narrow one with long streams).
+// The column sums p, r are reduced within each wave by shuffles, across waves
+// through LDS by one thread per (column group, component), which also forms u and o.
 #include "kda_device.h"
 #include "kda_internal.h"
 
 namespace kda {
 
+template <int DK, int DV> struct DecodeMap {
+    static constexpr int CG = DV / 4;                                  // float4 column groups
+    static constexpr int RG = (DK < 1024 / CG) ? DK : 1024 / CG;       // row groups
+    static constexpr int RPT = DK / RG;                                // rows per thread
+    static constexpr int NT = CG * RG;                                 // threads
+    static constexpr int NTB = NT < WAVE ? WAVE : NT;                  // block (whole waves)
+    static constexpr int NWV = NTB / WAVE;
+};
+
 template <typename ET, int DK, int DV>
-__global__ __launch_bounds__(256) void decode_kernel(
+__global__ __launch_bounds__((DecodeMap<DK, DV>::NTB)) __attribute__((amdgpu_waves_per_eu(8))) void decode_kernel(
     float* __restrict__ state, const ET* __restrict__ q, const ET* __restrict__ k,
     const ET* __restrict__ v, const float* __restrict__ log_alpha,
     const float* __restrict__ beta, ET* __restrict__ o) {
-    constexpr int CG = DV / 4;                               // float4 column groups
-    constexpr int RG = (DK < 256 / CG) ? DK : 256 / CG;      // row groups
-    constexpr int RPT = DK / RG;                             // rows per thread
-    constexpr int NT = CG * RG;
-    constexpr int NWV = NT / WAVE;
-    static_assert(NT % WAVE == 0 && NT <= 256 && DK <= NT, "decode thread map");
+    using DM = DecodeMap<DK, DV>;
+    constexpr int CG = DM::CG, RG = DM::RG, RPT = DM::RPT, NT = DM::NT, NWV = DM::NWV;
+    static_assert(DK % RG == 0 && DK <= NT && 4 * CG <= NT, "decode thread map");
 
     const size_t unit = blockIdx.x;
     const int tid = threadIdx.x;
+    const bool act = tid < NT;                      // (small shapes: the last wave is partial)
     const int cg = tid % CG, rg = tid / CG;
+    const int w = tid / WAVE;
 
     __shared__ float s_a[DK], s_k[DK], s_q[DK];
     __shared__ f32x4 s_p[NWV][CG], s_r[NWV][CG];
     __shared__ float s_kq[NWV];
+    __shared__ f32x4 s_u[CG];
 
     f32x4* S = reinterpret_cast<f32x4*>(state + unit * (size_t)(DK * DV));
     f32x4 sv[RPT];
+    if (act) {
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) sv[i] = __builtin_nontemporal_load(&S[(rg + i * RG) * CG + cg]);
+        for (int i = 0; i < RPT; ++i) sv[i] = __builtin_nontemporal_load(&S[(rg + i * RG) * CG + cg]);
+    }
 
     float kq = 0.f;
     if (tid < DK) {
@@ -55,16 +70,19 @@ __global__ __launch_bounds__(256) void decode_kernel(
     }
 #pragma unroll
     for (int m = WAVE / 2; m >= 1; m >>= 1) kq += __shfl_xor(kq, m);
-    if ((tid & (WAVE - 1)) == 0) s_kq[tid / WAVE] = kq;
+    if ((tid & (WAVE - 1)) == 0) s_kq[w] = kq;
     __syncthreads();
 
+    // decay the state; partial column sums p = (DS)^T k, r = (DS)^T q over this thread's rows
     f32x4 p = {0.f, 0.f, 0.f, 0.f}, r = {0.f, 0.f, 0.f, 0.f};
+    if (act) {
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-        const int row = rg + i * RG;
-        sv[i] *= s_a[row];
-        p += sv[i] * s_k[row];
-        r += sv[i] * s_q[row];
+        for (int i = 0; i < RPT; ++i) {
+            const int row = rg + i * RG;
+            sv[i] *= s_a[row];
+            p += sv[i] * s_k[row];
+            r += sv[i] * s_q[row];
+        }
     }
     // reduce over the row groups that share a wave (lanes differing in bits >= log2 CG)
 #pragma unroll
@@ -76,41 +94,42 @@ __global__ __launch_bounds__(256) void decode_kernel(
         }
     }
     if ((tid & (WAVE - 1)) < CG) {
-        s_p[tid / WAVE][cg] = p;
-        s_r[tid / WAVE][cg] = r;
+        s_p[w][cg] = p;
+        s_r[w][cg] = r;
     }
     __syncthreads();
 
-    f32x4 P = s_p[0][cg], R = s_r[0][cg];
-    float KQ = s_kq[0];
+    // one thread per (column group, component): u = beta (v - p), o = r + (k . q) u
+    if (tid < 4 * CG) {
+        const int c = tid >> 2, j = tid & 3;
+        float P = 0.f, R = 0.f, KQ = 0.f;
 #pragma unroll
-    for (int w = 1; w < NWV; ++w) {
-        P += s_p[w][cg];
-        R += s_r[w][cg];
-        KQ += s_kq[w];
+        for (int ww = 0; ww < NWV; ++ww) {
+            P += s_p[ww][c][j];
+            R += s_r[ww][c][j];
+            KQ += s_kq[ww];
+        }
+        const int col = 4 * c + j;
+        const float u = beta[unit] * (to_f32(v[unit * DV + col]) - P);
+        s_u[c][j] = u;
+        o[unit * DV + col] = from_f32<ET>(R + KQ * u);
     }
-    const float b = beta[unit];
-    f32x4 u;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) u[j] = b * (to_f32(v[unit * DV + cg * 4 + j]) - P[j]);
+    __syncthreads();
 
+    if (act) {
+        const f32x4 u = s_u[cg];
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-        const int row = rg + i * RG;
-        __builtin_nontemporal_store(sv[i] + s_k[row] * u, &S[row * CG + cg]);
-    }
-    if (rg == 0) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) o[unit * DV + cg * 4 + j] = from_f32<ET>(R[j] + KQ * u[j]);
+        for (int i = 0; i < RPT; ++i) {
+            const int row = rg + i * RG;
+            __builtin_nontemporal_store(sv[i] + s_k[row] * u, &S[row * CG + cg]);
+        }
     }
 }
 
 template <typename ET, int DK, int DV>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
-    constexpr int CG = DV / 4;
-    constexpr int RG = (DK < 256 / CG) ? DK : 256 / CG;
     const unsigned nblk = (unsigned)(a.N * a.H);
-    hipLaunchKernelGGL((decode_kernel<ET, DK, DV>), dim3(nblk), dim3(CG * RG), 0, st,
+    hipLaunchKernelGGL((decode_kernel<ET, DK, DV>), dim3(nblk), dim3(DecodeMap<DK, DV>::NTB), 0, st,
                        a.state, (const ET*)a.q, (const ET*)a.k, (const ET*)a.v, a.log_alpha,
                        a.beta, (ET*)a.o);
     return hipGetLastError();
