@@ -138,9 +138,17 @@ def cpu_workers():
     return max(1, min(16, os.cpu_count() or 1))
 
 
+HOST_GEN_LIMIT = 1 << 23              # token-heads above which inputs are drawn on the device
+
+
 def cpu_baseline_prefill(r, x):
     """The oracle's chunked form over every head of the workload, repeated until about
-    10 s of CPU work; one process per core, BLAS single-threaded."""
+    10 s of CPU work; one process per core, BLAS single-threaded.  Workloads drawn on the
+    device (x is None) are sampled: the first 4096 tokens of every head."""
+    sampled = x is None
+    if sampled:
+        r = r.with_shape(T=min(r.T, 4096))
+        x = ks.make_prefill(r)
     _CPU.update(x=x, chunk=r.chunk)
     workers = cpu_workers()
     reps = 1
@@ -151,7 +159,8 @@ def cpu_baseline_prefill(r, x):
         reps = int(min(512, max(2 * reps, np.ceil(reps * 12.0 / max(wall * workers, 1e-3)))))
     tok = r.B * r.T * reps
     return {"value": tok / wall, "unit": "tokens/s", "cores": workers, "kind": "oracle",
-            "sample": f"whole workload (B={r.B} T={r.T} H={r.H}) x{reps}, float64 chunked form "
+            "sample": (f"first {r.T} tokens of every head" if sampled else "whole workload")
+                      + f" (B={r.B} T={r.T} H={r.H}) x{reps}, float64 chunked form "
                       f"(chunk {r.chunk}), one (b, h) per task", "seconds": wall,
             "cpu_model": cpu_model()}
 
@@ -183,10 +192,17 @@ def bench_prefill(g, torch, r, x, steps, warmup):
     dev = torch.device("cuda:0")
     dt = torch.bfloat16 if r.dtype == "bf16" else torch.float32
     es = 2 if r.dtype == "bf16" else 4
-    T_ = lambda a, t: torch.from_numpy(np.ascontiguousarray(a)).to(dev, t)  # noqa: E731
-    q, k, v = T_(x["q"], dt), T_(x["k"], dt), T_(x["v"], dt)
-    la, beta = T_(x["log_alpha"], torch.float32), T_(x["beta"], torch.float32)
-    S0 = None if x["S0"] is None else T_(x["S0"], torch.float32)
+    if x is None:                        # too large for host arrays: drawn on the device
+        t = time.perf_counter()
+        xd = ks.make_prefill_device(r, dev)
+        torch.cuda.synchronize()
+        log(f"generated prefill inputs on the device in {time.perf_counter() - t:.1f}s")
+        q, k, v, la, beta, S0 = xd["q"], xd["k"], xd["v"], xd["log_alpha"], xd["beta"], xd["S0"]
+    else:
+        T_ = lambda a, t: torch.from_numpy(np.ascontiguousarray(a)).to(dev, t)  # noqa: E731
+        q, k, v = T_(x["q"], dt), T_(x["k"], dt), T_(x["v"], dt)
+        la, beta = T_(x["log_alpha"], torch.float32), T_(x["beta"], torch.float32)
+        S0 = None if x["S0"] is None else T_(x["S0"], torch.float32)
     plan = g.default_plan(r.B, r.T, r.H, r.dk, r.dv, r.chunk, dt)
     nws = g.workspace_bytes(r.B, r.T, r.H, r.dk, r.dv, r.chunk, dt, plan)
     ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
@@ -343,9 +359,11 @@ def main():
 
     r = ks.WORKLOADS[args.workload]
     rd = ks.WORKLOADS[DECODE_WORKLOAD]
-    t = time.perf_counter()
-    x = ks.make_prefill(r)
-    log(f"generated prefill inputs in {time.perf_counter() - t:.1f}s")
+    x = None
+    if r.B * r.T * r.H <= HOST_GEN_LIMIT:
+        t = time.perf_counter()
+        x = ks.make_prefill(r)
+        log(f"generated prefill inputs in {time.perf_counter() - t:.1f}s")
     d = None
     if not args.no_decode:
         t = time.perf_counter()

@@ -219,3 +219,62 @@ def make_decode(r: Recipe) -> dict:
         "log_alpha": np.ascontiguousarray(pre["log_alpha"].transpose(1, 0, 2, 3)),
         "beta": np.ascontiguousarray(pre["beta"].transpose(1, 0, 2)),
     }
+
+
+def make_prefill_device(r: Recipe, device, keyed_heads=()) -> dict:
+    """Prefill inputs generated straight into device tensors, for workloads whose float32 host
+    copies would not fit (T = 1M x 32 heads is 17 GB per tensor).
+
+    Heads in ``keyed_heads`` hold exactly the keyed values of ``gen_head`` (the oracle can
+    regenerate them); every other head is drawn on the device by torch's generator, seeded
+    from the workload's tag, with the same recipe.  Returns torch tensors in the library's
+    layouts and storage dtypes: q, k, v ([B,T,H,d], bf16 or f32), log_alpha, beta (f32),
+    S0 (f32 or None).
+    """
+    import torch
+    if r.pin_frac > 0:
+        raise ValueError("pinned-floor recipes are generated on the host (make_prefill)")
+    dt = torch.bfloat16 if r.dtype == "bf16" else torch.float32
+    B, T, H = r.B, r.T, r.H
+    out = {
+        "q": torch.empty((B, T, H, r.dk), dtype=dt, device=device),
+        "k": torch.empty((B, T, H, r.dk), dtype=dt, device=device),
+        "v": torch.empty((B, T, H, r.dv), dtype=dt, device=device),
+        "log_alpha": torch.empty((B, T, H, r.dk), dtype=torch.float32, device=device),
+        "beta": torch.empty((B, T, H), dtype=torch.float32, device=device),
+    }
+    store = {"q": dt, "k": dt, "v": dt, "log_alpha": torch.float32, "beta": torch.float32}
+    keyed = set(keyed_heads)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(r.tag)
+    for b in range(B):
+        for h in range(H):
+            for name in out:
+                if h in keyed:
+                    out[name][b, :, h] = torch.from_numpy(gen_head(r, name, b, h)).to(device, store[name])
+                    continue
+                for _, t0, t1 in _blocks(T):
+                    n = t1 - t0
+                    if name in ("q", "k"):
+                        x = torch.randn((n, r.dk), generator=gen, device=device, dtype=torch.float32)
+                        x = x / torch.sqrt((x * x).sum(dim=1, keepdim=True))
+                    elif name == "v":
+                        x = torch.randn((n, r.dv), generator=gen, device=device, dtype=torch.float32)
+                    elif name == "beta":
+                        x = torch.sigmoid(r.beta_std * torch.randn(n, generator=gen, device=device,
+                                                                   dtype=torch.float32))
+                    elif r.loga == "sig15":
+                        x = -5.0 * torch.sigmoid(1.5 * torch.randn((n, r.dk), generator=gen, device=device,
+                                                                   dtype=torch.float32))
+                    else:
+                        x = -5.0 + 5.0 * torch.rand((n, r.dk), generator=gen, device=device, dtype=torch.float32)
+                    out[name][b, t0:t1, h] = x.to(store[name])
+    if r.s0_std > 0:
+        S0 = torch.empty((B, H, r.dk, r.dv), dtype=torch.float32, device=device)
+        for b in range(B):
+            for h in range(H):
+                S0[b, h] = torch.from_numpy(gen_state(r, b, h)).to(device)
+        out["S0"] = S0
+    else:
+        out["S0"] = None
+    return out
