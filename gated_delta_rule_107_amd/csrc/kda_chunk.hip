@@ -195,8 +195,8 @@ __host__ __device__ constexpr Lds lds_layout(int E, int DK, int C) {
     L.rh = off;   off += align16(C * LDK * E);
     L.rd = off;   off += RV ? align16(C * LDK * E) : 0;
     L.rf = off;   off += (RV && NT == 4) ? align16(48 * LDK * E) : 0;
-    // the Kt..RF region also holds the v and o staging tiles (C rows, up to 128 columns each)
-    if (off - L.kt < 2 * C * (128 + PADE) * E) off = L.kt + align16(2 * C * (128 + PADE) * E);
+    // the Kt..RF region also holds the v staging tile (C rows, up to 128 columns)
+    if (off - L.kt < C * (128 + PADE) * E) off = L.kt + align16(C * (128 + PADE) * E);
     L.kht = off;  off += align16(DK * LC * E);
     L.an = off;   off += align16(C * LC * E);
     L.mm = off;   off += align16(C * LC * E);
@@ -371,12 +371,11 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
             if (row < C) pv[u] = *at_bytes(reinterpret_cast<const g16*>(v_b), (unsigned)(min(row, tlim) * tok_v + col) * (unsigned)E);
         }
     };
-    // staging tiles for v (the next chunk's, before its chain) and o (this chunk's, after its
-    // chain) over the Kt..RF region, which is dead between the A / M tiles and the next gate prep
+    // staging tile for the next chunk's v, over the Kt..RF region, which is dead between the
+    // A / M tiles and the next gate prep
     constexpr int LVO = 128 + PADE;                  // pitch: up to 128 columns
     OpT* s_v = s_kt;
-    OpT* s_o = s_kt + C * LVO;
-    static_assert(2 * C * LVO * E <= L.kht - L.kt, "v / o staging tiles exceed the dead operand region");
+    static_assert(C * LVO * E <= L.kht - L.kt, "v staging tile exceeds the dead operand region");
 
     // ---- start state into accumulator layout: Sacc[tau][r] = S[16 tau + g4 + r][colw + jl]
     f32x4 Sacc[NCT];
@@ -414,12 +413,12 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
     // chunk n+1; its four barriers separate
     //   (1) chain(n) [R, U, O, S update]  +  gate prep(n+1)    (MFMA latency next to VALU work)
     //   (2) Khat^T(n+1) to LDS, X / QS(n+1) from the updated state, A / M tiles(n+1)
-    //   (3) diagonal-block inverses(n+1), v(n+1) and o(n) into the staging tiles
-    //   (4) o(n) to HBM, v(n+1) into registers in the accumulator layout.
+    //   (3) diagonal-block inverses(n+1), v(n+1) into its staging tile
+    //   (4) v(n+1) into registers in the accumulator layout.
     // beta and e^Gamma_C of chunk n are read in (1) while gate prep writes chunk n+1's, so
     // they have two slots (chunk n uses slot n & 1); Khat^T(n+1) waits in registers until (2).
     f32x4 X[NT], QS[NT];                             // Kt S, Qt S of the chunk chained next
-    B16 vr[NT], orr[NT];                             // its v, and o of the chunk just chained
+    B16 vr[NT];                                      // its v
     V4 khr[4];                                       // Khat^T(n+1): 4 channels x 4 tokens
 
     auto body = [&](auto cur_c, auto nxt_c, int64_t n) {
@@ -457,13 +456,20 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
             }
         }
 
-        // ================= (1c) O = QS + M U of chunk n, kept in registers until (3)
+        // ================= (1c) O = QS + M U of chunk n, stored straight from the accumulators
+        // (its store instructions issue while the gate prep below keeps the vector units busy)
         if constexpr (cur && want_o) {
+            OpT* o_w = go + ((b * T + t0) * H + h) * (int64_t)dv + colw;       // uniform: this wave's columns
 #pragma unroll
             for (int p = 0; p < NT; ++p) {
 #pragma unroll
                 for (int qq = 0; qq <= p; ++qq) QS[p] = MF::k16(s_mm, LC, 16 * p, 16 * qq, ub[qq], QS[p], lane);
-                orr[p] = MF::b16(QS[p]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * p + g4 + r;
+                    if (chain && row < Tc)
+                        *at_bytes(o_w, (unsigned)(row * tok_v + jl) * (unsigned)E) = from_f32<OpT>(QS[p][r]);
+                }
             }
         }
 
@@ -741,29 +747,9 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
             }
             if (n + 2 < nchunks) prefetch_v(t1 + C, tid);
         }
-        if constexpr (cur && want_o) {
-            if (chain) {
-#pragma unroll
-                for (int p = 0; p < NT; ++p)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) s_o[(16 * p + g4 + r) * LVO + 16 * wave + jl] = orr[p][r];
-            }
-        }
         __syncthreads();
 
-        // ================= (4) o(n) to HBM; v(n+1) into the accumulator layout
-        if constexpr (cur && want_o) {
-            OpT* o_b = go + ((b * T + t0) * H + h) * (int64_t)dv + (int)cb * DVB;   // uniform
-#pragma unroll
-            for (int u = 0; u < NGV; ++u) {
-                const int gi2 = tid + 512 * u;
-                int row, gc;
-            granule(gi2, row, gc);
-                if (row < Tc)
-                    *at_bytes(reinterpret_cast<g16*>(o_b), (unsigned)(row * tok_v + gc * VG) * (unsigned)E) =
-                        *reinterpret_cast<const g16*>(s_o + row * LVO + gc * VG);
-            }
-        }
+        // ================= (4) v(n+1) into the accumulator layout
         if constexpr (nxt) {
 #pragma unroll
             for (int p = 0; p < NT; ++p)
