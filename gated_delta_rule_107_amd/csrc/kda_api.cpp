@@ -63,6 +63,8 @@ kda_status_t check_problem(int64_t B, int64_t T, int32_t H, int32_t dk, int32_t 
     if (dt == KDA_DTYPE_F32 && chunk * dk > 4096)
         return fail(KDA_ERR_UNSUPPORTED, "float32 inputs need chunk * dk <= 4096 (got %d)", chunk * dk);
     if (B * T * (int64_t)H > (int64_t)1 << 40) return fail(KDA_ERR_SHAPE, "problem too large");
+    if ((int64_t)H * (dk > dv ? dk : dv) >= (int64_t)1 << 24)   // token strides are 24-bit products
+        return fail(KDA_ERR_UNSUPPORTED, "H * max(dk, dv) must be below 2^24 (got H=%d)", H);
     return KDA_OK;
 }
 

@@ -328,6 +328,8 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
     // are masked where they are used, one chunk later, so no instruction here waits for the
     // data.  beta is loaded under exactly the predicate of its consumer, so no path reaches
     // the next prefetch with that load unconsumed.
+    // Row offsets use 24-bit multiplies (the ABI bounds H * max(dk, dv) below 2^24).  When the
+    // whole chunk is in range, token j of each quad is one stride further: an add, no clamp.
     auto prefetch_gates = [&](int64_t t0, int tid) {
         const int lane = tid & 63;
         const int tq = 4 * (lane >> 4) + ((lane >> 2) & 3);
@@ -337,14 +339,24 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
         const float* la_b = a.log_alpha + base;
         const OpT* k_b = gk + base;
         const OpT* q_b = gq + base;
+        if (tlim == C - 1) {
+            unsigned off = __umul24(4 * tq, tok_k) + gc0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const unsigned off = (unsigned)(min(4 * tq + j, tlim) * tok_k + gc0);
-            pla[j] = *at_bytes(reinterpret_cast<const f32x4*>(la_b), off * 4u);
-            pk[j] = *at_bytes(reinterpret_cast<const V4*>(k_b), off * (unsigned)E);
-            if (want_o) pq[j] = *at_bytes(reinterpret_cast<const V4*>(q_b), off * (unsigned)E);
+            for (int j = 0; j < 4; ++j, off += tok_k) {
+                pla[j] = *at_bytes(reinterpret_cast<const f32x4*>(la_b), off * 4u);
+                pk[j] = *at_bytes(reinterpret_cast<const V4*>(k_b), off * (unsigned)E);
+                if (want_o) pq[j] = *at_bytes(reinterpret_cast<const V4*>(q_b), off * (unsigned)E);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const unsigned off = __umul24(min(4 * tq + j, tlim), tok_k) + gc0;
+                pla[j] = *at_bytes(reinterpret_cast<const f32x4*>(la_b), off * 4u);
+                pk[j] = *at_bytes(reinterpret_cast<const V4*>(k_b), off * (unsigned)E);
+                if (want_o) pq[j] = *at_bytes(reinterpret_cast<const V4*>(q_b), off * (unsigned)E);
+            }
         }
-        if (tid < C) pbeta = *at_bytes(a.beta + (b * T + t0) * H + h, (unsigned)(min(tid, tlim) * H) * 4u);
+        if (tid < C) pbeta = *at_bytes(a.beta + (b * T + t0) * H + h, __umul24(min(tid, tlim), H) * 4u);
     };
     // v for the chain as 16-byte granules (GPR per row); rows past the end read a clamped row
     // and are multiplied by beta = 0 later, transition columns are zeroed when staged
@@ -368,7 +380,7 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
             int row, gc;
             granule(gi2, row, gc);
             const int col = min(gc * VG, dv - (int)cb * DVB - VG);
-            if (row < C) pv[u] = *at_bytes(reinterpret_cast<const g16*>(v_b), (unsigned)(min(row, tlim) * tok_v + col) * (unsigned)E);
+            if (row < C) pv[u] = *at_bytes(reinterpret_cast<const g16*>(v_b), (__umul24(min(row, tlim), tok_v) + col) * (unsigned)E);
         }
     };
     // staging tile for the next chunk's v, over the Kt..RF region, which is dead between the
@@ -468,7 +480,7 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
                 for (int r = 0; r < 4; ++r) {
                     const int row = 16 * p + g4 + r;
                     if (chain && row < Tc)
-                        *at_bytes(o_w, (unsigned)(row * tok_v + jl) * (unsigned)E) = from_f32<OpT>(QS[p][r]);
+                        *at_bytes(o_w, (__umul24(row, tok_v) + jl) * (unsigned)E) = from_f32<OpT>(QS[p][r]);
                 }
             }
         }
@@ -480,10 +492,10 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
         if constexpr (nxt) {
             if (tid < C) sb_n[tid] = tid < Tn ? pbeta : 0.f;
             // Every lane runs the cross-lane scans; only stores are guarded.  Tokens past the
-            // end (and lanes past the last sub-tile) read clamped addresses: zero them.  Full
-            // chunks of 4 sub-tiles need no mask (idle channel lanes of DK < 128 only feed
-            // their own 16-lane rows, whose stores are skipped).  k and q stay in their packed
-            // prefetch registers until they are used.
+            // end (and lanes past the last sub-tile) read clamped addresses: their log-decay is
+            // zeroed here (idle channel lanes of DK < 128 only feed their own 16-lane rows,
+            // whose stores are skipped).  k and q stay in their packed prefetch registers until
+            // they are used.
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const bool ok = full || 4 * tq + j < Tn;
@@ -545,14 +557,14 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int t = 4 * tq + j;
-                    const bool ok = full || t < Tn;
+                    // tokens past the end keep their (clamped, finite) k and q: their beta is 0
+                    // and their log-decay 0, so they change neither U, O nor the state
                     float k[4][4], q[4][4];
                     L4::to_f(pk[j], k[j]);
                     if (want_o) L4::to_f(pq[j], q[j]);
+                    else {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        k[j][e] = ok ? k[j][e] : 0.f;
-                        q[j][e] = (want_o && ok) ? q[j][e] : 0.f;
+                        for (int e = 0; e < 4; ++e) q[j][e] = 0.f;
                     }
                     float kl[4], ql[4], rh[4], kt[4], qt[4], rd[4], rf1[4], rf2[4];
 #pragma unroll

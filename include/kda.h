@@ -31,8 +31,9 @@
  *   values are not checked: NaN / Inf propagate.
  * - A failed kernel launch returns KDA_ERR_HIP (text via kda_last_error()).
  * - Supported sizes: dk, dv in {16, 32, 64, 128}; chunk in {16, 32, 64};
- *   any T >= 0 (a partial last chunk is masked); B, N, H >= 1.  For float32
- *   q/k/v the chunk must satisfy chunk * dk <= 4096 (LDS capacity).
+ *   any T >= 0 (a partial last chunk is masked); B, N, H >= 1 with
+ *   H * max(dk, dv) < 2^24 (token strides are formed as 24-bit products).  For
+ *   float32 q/k/v the chunk must satisfy chunk * dk <= 4096 (LDS capacity).
  * - Thread safety: calls are reentrant; concurrent calls on one stream run in
  *   stream order, calls on different streams must not share output buffers.
  */

@@ -63,7 +63,7 @@ def call_chunk(lib, **kw):
     (dict(B=0), SHAPE), (dict(H=0), SHAPE), (dict(T=-1), SHAPE),
     (dict(dt=7), DTYPE),
     (dict(dk=24), UNSUP), (dict(dv=256), UNSUP), (dict(chunk=128), UNSUP), (dict(chunk=8), UNSUP),
-    (dict(dk=128, chunk=64, dt=F32), UNSUP),
+    (dict(dk=128, chunk=64, dt=F32), UNSUP), (dict(H=1 << 17, dk=128), UNSUP),
     (dict(q=A[0] + 4), ALIGN), (dict(S_T=A[7] + 8), ALIGN),
     (dict(o=A[0]), ALIAS), (dict(o=A[4] + 256), ALIAS), (dict(S_T=A[1]), ALIAS),
     (dict(S0=A[7] + 16), ALIAS),
