@@ -68,15 +68,22 @@ template <> struct MM<bf16> {
         return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
                                                          __builtin_bit_cast(i16x4, b), acc, 0, 0, 0);
     }
-    // the same over 32 contraction rows given as two tiles (rows c0.. and c0+16..)
-    static __device__ __forceinline__ f32x4 k32(const bf16* A, int ld, int r0, int c0, B16 b0, B16 b1,
-                                                f32x4 acc, int lane) {
+    // the same over 32 contraction rows given as two tiles (rows c0.. and c0+16..), as a load
+    // of the A operand and the product, so that callers can have several loads in flight
+    typedef bf16x8 A32;
+    static __device__ __forceinline__ A32 ld32(const bf16* A, int ld, int r0, int c0, int lane) {
         const bf16* p = A + (r0 + (lane & 15)) * ld + c0 + 4 * (lane >> 4);
         const bf16x4 lo = *reinterpret_cast<const bf16x4*>(p);
         const bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 16);
-        const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    static __device__ __forceinline__ f32x4 mma32(const A32& a, B16 b0, B16 b1, f32x4 acc) {
         const bf16x8 b = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+    }
+    static __device__ __forceinline__ f32x4 k32(const bf16* A, int ld, int r0, int c0, B16 b0, B16 b1,
+                                                f32x4 acc, int lane) {
+        return mma32(ld32(A, ld, r0, c0, lane), b0, b1, acc);
     }
     // natural order, both operands in LDS:
     // acc += (A[ra + m][k0 + kk] * fac[k0 + kk]) * Bm[rb + n][k0 + kk] over kk < 32
@@ -113,6 +120,18 @@ template <> struct MM<float> {
                                                 f32x4 acc, int lane) {
         acc = k16(A, ld, r0, c0, b0, acc, lane);
         return k16(A, ld, r0, c0 + 16, b1, acc, lane);
+    }
+    struct A32 { f32x4 lo, hi; };
+    static __device__ __forceinline__ A32 ld32(const float* A, int ld, int r0, int c0, int lane) {
+        const float* p = A + (r0 + (lane & 15)) * ld + c0 + 4 * (lane >> 4);
+        return A32{*reinterpret_cast<const f32x4*>(p), *reinterpret_cast<const f32x4*>(p + 16)};
+    }
+    static __device__ __forceinline__ f32x4 mma32(const A32& a, B16 b0, B16 b1, f32x4 acc) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[s], b0[s], acc, 0, 0, 0);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[s], b1[s], acc, 0, 0, 0);
+        return acc;
     }
     static __device__ __forceinline__ f32x4 nat(const float* A, int lda, int ra, const float* Bm, int ldb,
                                                 int rb, int k0, const float* fac, f32x4 acc, int lane) {
@@ -649,20 +668,49 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
                 B16 sb[NCT];
 #pragma unroll
                 for (int tau = 0; tau < NCT; ++tau) sb[tau] = MF::b16(Sacc[tau]);
+                if constexpr (NCT == 1 || E == 4) {
+                    // (float32 operands are 4x larger: no room to hold a second sub-tile's)
 #pragma unroll
-                for (int p = 0; p < NT; ++p) {
-                    X[p] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    QS[p] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    if constexpr (NCT == 1) {
-                        X[p] = MF::k16(s_kt, LKQ, 16 * p, 0, sb[0], X[p], lane);
-                        if (want_o) QS[p] = MF::k16(s_qt, LKQ, 16 * p, 0, sb[0], QS[p], lane);
-                    } else {
+                    for (int p = 0; p < NT; ++p) {
+                        X[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        QS[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        if constexpr (NCT == 1) {
+                            X[p] = MF::k16(s_kt, LKQ, 16 * p, 0, sb[0], X[p], lane);
+                            if (want_o) QS[p] = MF::k16(s_qt, LKQ, 16 * p, 0, sb[0], QS[p], lane);
+                        } else {
+#pragma unroll
+                            for (int s2 = 0; s2 < NCT / 2; ++s2) {
+                                X[p] = MF::k32(s_kt, LKQ, 16 * p, 32 * s2, sb[2 * s2], sb[2 * s2 + 1], X[p], lane);
+                                if (want_o)
+                                    QS[p] = MF::k32(s_qt, LKQ, 16 * p, 32 * s2, sb[2 * s2], sb[2 * s2 + 1], QS[p], lane);
+                            }
+                        }
+                    }
+                } else {
+                    // Software-pipelined over the sub-tiles: the operand loads of sub-tile p+1
+                    // are issued before the products of sub-tile p (scheduling barriers keep the
+                    // compiler from pulling them back next to their uses).
+                    typename MF::A32 ax[2][NCT / 2], aq[2][NCT / 2];
+                    auto load = [&](int p, int buf) {
 #pragma unroll
                         for (int s2 = 0; s2 < NCT / 2; ++s2) {
-                            X[p] = MF::k32(s_kt, LKQ, 16 * p, 32 * s2, sb[2 * s2], sb[2 * s2 + 1], X[p], lane);
-                            if (want_o)
-                                QS[p] = MF::k32(s_qt, LKQ, 16 * p, 32 * s2, sb[2 * s2], sb[2 * s2 + 1], QS[p], lane);
+                            ax[buf][s2] = MF::ld32(s_kt, LKQ, 16 * p, 32 * s2, lane);
+                            if (want_o) aq[buf][s2] = MF::ld32(s_qt, LKQ, 16 * p, 32 * s2, lane);
                         }
+                    };
+                    load(0, 0);
+#pragma unroll
+                    for (int p = 0; p < NT; ++p) {
+                        if (p + 1 < NT) load(p + 1, (p + 1) & 1);
+                        __builtin_amdgcn_sched_barrier(0);
+                        X[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        QS[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int s2 = 0; s2 < NCT / 2; ++s2) {
+                            X[p] = MF::mma32(ax[p & 1][s2], sb[2 * s2], sb[2 * s2 + 1], X[p]);
+                            if (want_o) QS[p] = MF::mma32(aq[p & 1][s2], sb[2 * s2], sb[2 * s2 + 1], QS[p]);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
                     }
                 }
             }
