@@ -10,7 +10,9 @@ prefill B=1, T=4096, H=16, dk=dv=128, chunk 64, bf16 q/k/v with float32 gates
 and state.  Inputs are seeded synthetic tensors already resident in HBM when
 the timed region starts.
 
-The same JSON line also carries the decode figure (256 sequences x 32 heads,
+The prefill block also reports the same step with state checkpoints every 512
+tokens (the prefix-reuse output of kda_plan_t.state_ckpt).  The same JSON line
+also carries the decode figure (256 sequences x 32 heads,
 128x128 float32 state, 64 consecutive in-place steps), the roofline of the
 dominant prefill kernel (algorithmic bytes per launch / its mean duration,
 taken from HIP events the library records around each launch on the stream
@@ -139,6 +141,7 @@ def cpu_workers():
 
 
 HOST_GEN_LIMIT = 1 << 23              # token-heads above which inputs are drawn on the device
+CKPT_STRIDE = 512                     # state checkpoint stride of the side figure (the hash block)
 
 
 def cpu_baseline_prefill(r, x):
@@ -243,7 +246,27 @@ def bench_prefill(g, torch, r, x, steps, warmup):
         per_launch.append({"kernel": name, "ms": float(np.mean(d)), "bytes": int(nbytes),
                            "GBps": nbytes / (np.mean(d) * 1e-3) / 1e9})
     log("prefill per launch:", json.dumps(per_launch))
-    return ms, plan, per_launch
+
+    # the same step with state checkpoints every CKPT_STRIDE tokens (prefix reuse)
+    ckpt = None
+    if r.T >= CKPT_STRIDE and CKPT_STRIDE % r.chunk == 0:
+        nck = r.T // CKPT_STRIDE
+        sck = torch.empty((r.B, nck, r.H, r.dk, r.dv), dtype=torch.float32, device=dev)
+        for _ in range(warmup):
+            g.chunk_fwd(q, k, v, la, beta, S0, chunk=r.chunk, plan=plan, o=o, S_T=S_T, workspace=ws,
+                        ckpt_stride=CKPT_STRIDE, state_ckpt=sck)
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(steps):
+            g.chunk_fwd(q, k, v, la, beta, S0, chunk=r.chunk, plan=plan, o=o, S_T=S_T, workspace=ws,
+                        ckpt_stride=CKPT_STRIDE, state_ckpt=sck)
+        t1.record()
+        torch.cuda.synchronize()
+        ms_ck = t0.elapsed_time(t1) / steps
+        ckpt = {"stride": CKPT_STRIDE, "checkpoints": nck, "ms_per_step": round(ms_ck, 5),
+                "overhead": round(ms_ck / ms - 1.0, 4), "extra_bytes": int(sck.numel() * 4)}
+        log("prefill with state checkpoints:", json.dumps(ckpt))
+    return ms, plan, per_launch, ckpt
 
 
 def bench_decode(g, torch, rd, d, reps):
@@ -386,7 +409,7 @@ def main():
     props = torch.cuda.get_device_properties(0)
     log(f"device: {props.name} {getattr(props, 'gcnArchName', '')} CUs={props.multi_processor_count}")
 
-    ms, plan, per_launch = bench_prefill(g, torch, r, x, args.steps, args.warmup)
+    ms, plan, per_launch, ckpt = bench_prefill(g, torch, r, x, args.steps, args.warmup)
     es = 2 if r.dtype == "bf16" else 4
     token_heads = r.B * r.T * r.H
     flops = token_heads * prefill_flops_per_token_head(r.dk, r.dv, r.chunk)
@@ -434,7 +457,7 @@ def main():
                     "hbm_frac_alg": round(nbytes / sec / (PEAK_HBM_GBPS * 1e9), 4),
                     "roofline_frac": round(max(flops / (peak_mf * 1e12), nbytes / (PEAK_HBM_GBPS * 1e9)) / sec, 4),
                     "alg_gflop": round(flops / 1e9, 3), "alg_mb": round(nbytes / 1e6, 2),
-                    "launches": per_launch},
+                    "launches": per_launch, "with_state_checkpoints": ckpt},
         "decode": dec,
         "hbm_copy_GBps": round(copy_gbps, 1),
     }

@@ -34,9 +34,11 @@ class KdaError(RuntimeError):
 
 
 class Plan(ctypes.Structure):
-    """kda_plan_t: segmentation, column blocking and optional launch-timing events."""
+    """kda_plan_t: segmentation, column blocking, optional launch-timing events and optional
+    state checkpoints."""
     _fields_ = [("n_segments", ctypes.c_int32), ("dv_block", ctypes.c_int32),
-                ("launch_events", ctypes.POINTER(ctypes.c_void_p)), ("n_launch_events", ctypes.c_int32)]
+                ("launch_events", ctypes.POINTER(ctypes.c_void_p)), ("n_launch_events", ctypes.c_int32),
+                ("state_ckpt", ctypes.c_void_p), ("ckpt_stride", ctypes.c_int64)]
 
     def __repr__(self):
         return f"Plan(n_segments={self.n_segments}, dv_block={self.dv_block})"
@@ -132,8 +134,10 @@ def workspace_bytes(B, T, H, dk, dv, chunk=64, dtype=torch.bfloat16, plan: Plan 
 
 
 def chunk_fwd(q, k, v, log_alpha, beta, S0=None, chunk: int = 64, plan: Plan | None = None,
-              o=None, S_T=None, workspace=None):
-    """Chunked prefill: returns (o [B,T,H,dv] in q's dtype, S_T [B,H,dk,dv] float32).
+              o=None, S_T=None, workspace=None, ckpt_stride: int = 0, state_ckpt=None):
+    """Chunked prefill: returns (o [B,T,H,dv] in q's dtype, S_T [B,H,dk,dv] float32), and with
+    ``ckpt_stride`` > 0 also the state checkpoints [B, T // ckpt_stride, H, dk, dv] float32
+    (the state after every ckpt_stride tokens; a multiple of ``chunk``).
 
     ``S_T`` may be passed as ``S0`` itself to advance the state in place.
     ``plan`` (a Plan) overrides the library's default segmentation / column blocking.
@@ -161,6 +165,21 @@ def chunk_fwd(q, k, v, log_alpha, beta, S0=None, chunk: int = 64, plan: Plan | N
         S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     else:
         _require(S_T, "S_T", torch.float32, (B, H, dk, dv), dev)
+    if ckpt_stride:
+        if ckpt_stride < 0 or ckpt_stride % chunk:
+            raise KdaError(5, f"ckpt_stride ({ckpt_stride}) must be a positive multiple of chunk ({chunk})")
+        nck = T // ckpt_stride
+        if state_ckpt is None:
+            state_ckpt = torch.empty((B, nck, H, dk, dv), dtype=torch.float32, device=dev)
+        else:
+            _require(state_ckpt, "state_ckpt", torch.float32, (B, nck, H, dk, dv), dev)
+        p2 = Plan()
+        if plan is not None:
+            ctypes.memmove(ctypes.addressof(p2), ctypes.addressof(plan), ctypes.sizeof(Plan))
+        if nck > 0:                          # (T < ckpt_stride: no checkpoint to write)
+            p2.state_ckpt = state_ckpt.data_ptr()
+            p2.ckpt_stride = ckpt_stride
+        plan = p2
     nws = workspace_bytes(B, T, H, dk, dv, chunk, q.dtype, plan)
     if nws > 0:
         if workspace is None or workspace.numel() * workspace.element_size() < nws:
@@ -172,6 +191,8 @@ def chunk_fwd(q, k, v, log_alpha, beta, S0=None, chunk: int = 64, plan: Plan | N
                               ctypes.byref(plan) if plan is not None else None,
                               _ptr(workspace), nws, _stream(dev))
     _check(code)
+    if ckpt_stride:
+        return o, S_T, state_ckpt
     return o, S_T
 
 

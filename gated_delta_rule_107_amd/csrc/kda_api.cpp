@@ -76,7 +76,7 @@ struct Resolved {
 
 kda_status_t resolve_plan(int64_t B, int64_t T, int32_t H, int32_t dk, int32_t dv, int32_t chunk,
                           kda_dtype_t dt, const kda_plan_t* plan, Resolved* out) {
-    kda_plan_t p = plan ? *plan : kda_plan_t{0, 0, nullptr, 0};
+    kda_plan_t p = plan ? *plan : kda_plan_t{0, 0, nullptr, 0, nullptr, 0};
     int32_t dvb = p.dv_block;
     if (dvb == 0) dvb = dv;                                   // one column block per (b, h)
     if (dvb < 16 || dvb > 128 || dvb % 16 != 0 || dv % dvb != 0)
@@ -166,8 +166,7 @@ kda_status_t kda_chunk_fwd_default_plan(int64_t B, int64_t T, int32_t H, int32_t
     Resolved r;
     s = resolve_plan(B, T, H, dk, dv, chunk, dt, nullptr, &r);
     if (s != KDA_OK) return s;
-    plan->n_segments = r.n_seg;
-    plan->dv_block = r.dv_block;
+    *plan = kda_plan_t{r.n_seg, r.dv_block, nullptr, 0, nullptr, 0};
     return KDA_OK;
 }
 
@@ -194,7 +193,12 @@ kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v, const fl
     if (!S_T) return fail(KDA_ERR_NULL, "S_T is NULL");
     if (T > 0 && (!q || !k || !v || !log_alpha || !beta || !o))
         return fail(KDA_ERR_NULL, "q, k, v, log_alpha, beta and o are required when T > 0");
-    const void* ptrs[] = {q, k, v, log_alpha, beta, S0, o, S_T, workspace};
+    float* ckpt = plan ? plan->state_ckpt : nullptr;
+    const int64_t ckpt_stride = ckpt ? plan->ckpt_stride : 0;
+    if (ckpt && (ckpt_stride <= 0 || ckpt_stride % chunk != 0))
+        return fail(KDA_ERR_UNSUPPORTED, "ckpt_stride (%lld) must be a positive multiple of chunk (%d)",
+                    (long long)ckpt_stride, chunk);
+    const void* ptrs[] = {q, k, v, log_alpha, beta, S0, o, S_T, workspace, ckpt};
     for (const void* p : ptrs)
         if (p && !aligned(p)) return fail(KDA_ERR_ALIGN, "pointer %p is not 16-byte aligned", p);
     Resolved r;
@@ -221,6 +225,12 @@ kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v, const fl
         for (int i = 0; i < 7; ++i)
             if (overlaps(workspace, need, ins[i].p, ins[i].n)) return fail(KDA_ERR_ALIAS, "workspace overlaps %s", ins[i].name);
     }
+    if (ckpt) {
+        const size_t n_ck = (size_t)(T / ckpt_stride) * n_s;
+        for (const Span& in : ins)
+            if (overlaps(ckpt, n_ck, in.p, in.n)) return fail(KDA_ERR_ALIAS, "state_ckpt overlaps %s", in.name);
+        if (T > 0 && overlaps(ckpt, n_ck, o, n_o)) return fail(KDA_ERR_ALIAS, "state_ckpt overlaps o");
+    }
 
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     if (plan && plan->launch_events && plan->n_launch_events < 0)
@@ -231,6 +241,7 @@ kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v, const fl
     a.o = o; a.s_final = S_T;
     a.B = B; a.T = T; a.H = H; a.dk = dk; a.dv = dv; a.chunk = chunk;
     a.n_seg = r.n_seg; a.seg_len = r.seg_len; a.dv_block = r.dv_block;
+    a.ckpt = ckpt; a.ckpt_stride = ckpt_stride;
     a.bf16 = dt == KDA_DTYPE_BF16;
     hipError_t e;
     if (r.n_seg == 1) {

@@ -452,6 +452,16 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
     B16 vr[NT];                                      // its v
     V4 khr[4];                                       // Khat^T(n+1): 4 channels x 4 tokens
 
+    // state checkpoints (pass 2 / one pass): tokens into this unit's range that end the next
+    // one (-1: none), and where it goes (this head's columns of checkpoint t / stride - 1)
+    int ck_rel = -1;
+    float* ck_ptr = nullptr;
+    if (MODE == 0 && a.ckpt) {
+        const int64_t first = t_begin / a.ckpt_stride;            // index of the next checkpoint
+        ck_rel = (int)((first + 1) * a.ckpt_stride - t_begin);
+        ck_ptr = a.ckpt + ((b * (T / a.ckpt_stride) + first) * H + h) * (int64_t)DK * dv + colw;
+    }
+
     auto body = [&](auto cur_c, auto nxt_c, int64_t n) {
         constexpr bool cur = decltype(cur_c)::value;  // a chain runs (chunk n exists)
         constexpr bool nxt = decltype(nxt_c)::value;  // chunk n+1 exists
@@ -652,6 +662,19 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
                     for (int s2 = 0; s2 < NT / 2; ++s2)
                         Sacc[tau] = MF::k32(s_kht, LC, 16 * tau, 32 * s2, ub[2 * s2], ub[2 * s2 + 1], Sacc[tau], lane);
                 }
+            }
+        }
+        // state checkpoint after tokens [0, t0 + C) when that is a multiple of the stride
+        if constexpr (cur && MODE == 0) {
+            if ((int)(n + 1) * C == ck_rel) {        // (never true without checkpoints)
+                if (chain && t_begin + ck_rel <= T) {
+#pragma unroll
+                    for (int tau = 0; tau < NCT; ++tau)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) ck_ptr[(16 * tau + g4 + r) * dv + jl] = Sacc[tau][r];
+                }
+                ck_rel += (int)a.ckpt_stride;
+                ck_ptr += (int64_t)H * DK * dv;
             }
         }
         // chunk n+2's gates, keys and queries load while chunk n+1 is processed

@@ -40,6 +40,8 @@ struct ChunkArgs {
     int32_t n_seg;          // P
     int64_t seg_len;        // tokens per segment, a multiple of chunk
     int32_t dv_block;       // columns per workgroup (16 per wave)
+    float* ckpt;            // [B, T / ckpt_stride, H, dk, dv] state checkpoints (mode 0) or null
+    int64_t ckpt_stride;    // tokens between checkpoints, a multiple of chunk
     int32_t mode;
     bool bf16;
 };

@@ -77,6 +77,15 @@ typedef enum {
  *   recurrence is independent per state column, so column blocks run in
  *   parallel; the shared per-chunk work (gates, WY transform) is repeated
  *   per block.
+ * state_ckpt / ckpt_stride: optional state checkpoints for prefix reuse
+ *   (orkas.ai "Kimi K3 architecture", section "The cost comes back in the
+ *   serving stack": the recurrent state is checkpointed sparsely, at some of
+ *   the 512-token hash boundaries, so a cache hit can restore it).  When
+ *   state_ckpt is not NULL, ckpt_stride is a positive multiple of chunk and
+ *   state_ckpt [B, T / ckpt_stride (rounded down), H, dk, dv] float32 receives
+ *   the state after tokens ckpt_stride, 2 ckpt_stride, ... of each sequence
+ *   (the start state S0 counts as the state before token 0).  It must be
+ *   16-byte aligned and overlap no other argument.  NULL = no checkpoints.
  * A zeroed plan (all fields 0 / NULL) means "library default" for each field.
  */
 typedef struct {
@@ -90,6 +99,8 @@ typedef struct {
      * on `stream`; launches beyond the array's capacity record nothing. */
     void* const* launch_events;
     int32_t n_launch_events;
+    float* state_ckpt;
+    int64_t ckpt_stride;
 } kda_plan_t;
 
 /* Fills *plan with the library's default for this problem on the current

@@ -83,6 +83,26 @@ def test_chunk_fwd_plan_errors(lib):
     assert r == WS
 
 
+def test_chunk_fwd_checkpoint_errors(lib):
+    import gated_delta_rule_107_amd as g
+
+    def plan_ck(ptr, stride):
+        p = g.Plan(1, 0)
+        p.state_ckpt, p.ckpt_stride = ptr, stride
+        return p
+    assert call_chunk(lib, plan=plan_ck(A[9], 24)) == UNSUP        # not a multiple of chunk 16
+    assert call_chunk(lib, plan=plan_ck(A[9], 0)) == UNSUP
+    assert call_chunk(lib, plan=plan_ck(A[9], -32)) == UNSUP
+    assert call_chunk(lib, plan=plan_ck(A[9] + 4, 32)) == ALIGN
+    assert call_chunk(lib, plan=plan_ck(A[6], 32)) == ALIAS        # overlaps o
+    assert call_chunk(lib, plan=plan_ck(A[7], 32)) == ALIAS        # overlaps S_T
+    with pytest.raises(g.KdaError) as e:                           # the binding's own check
+        import torch
+        x = torch.zeros(1)
+        g.chunk_fwd(x, x, x, x, x, ckpt_stride=24, chunk=16)
+    assert e.value.code in (2, 5)
+
+
 def test_plan_and_workspace_queries(lib):
     import gated_delta_rule_107_amd as g
     import torch

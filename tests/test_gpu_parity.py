@@ -323,3 +323,37 @@ def test_workload3_long_context_full_size(g):
         _say(f"oracle over 1,048,576 tokens of head {h}")
         o_ref, S_ref = _oracle_head(r, h)
         check(to_np(o[:, :, h:h + 1]), to_np(S[:, h:h + 1]), o_ref, S_ref, TOL["bf16"], f"workload 3 head {h}")
+
+
+@pytest.mark.parametrize("shape,stride,nseg", [
+    (("f32", 1, 64, 2, 16, 16, 16), 32, 1),
+    (("bf16", 2, 300, 2, 64, 64, 64), 128, 1),
+    (("bf16", 1, 500, 2, 128, 128, 64), 64, 3),
+    (("bf16", 1, 512, 2, 128, 128, 64), 256, 2),       # the last checkpoint is the final state
+], ids=["f32-tiny", "bf16-ragged", "bf16-segments", "bf16-final"])
+def test_state_checkpoints(g, shape, stride, nseg):
+    """State checkpoints every `stride` tokens (prefix reuse, orkas.ai page, section "The cost
+    comes back in the serving stack"): checkpoint j must equal the oracle's state after the
+    first (j + 1) * stride tokens; o and S_T are unchanged by asking for checkpoints."""
+    import torch
+    dtype, B, T, H, dk, dv, chunk = shape
+    r = small_recipe(dtype, B, T, H, dk, dv, chunk, s0_std=0.05)
+    _say(f"case: checkpoints {shape} stride {stride} segments {nseg}")
+    x = ks.make_prefill(r)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    args = [dev_tensor(x[n], dt) for n in ("q", "k", "v")]
+    args += [dev_tensor(x["log_alpha"], torch.float32), dev_tensor(x["beta"], torch.float32),
+             dev_tensor(x["S0"], torch.float32)]
+    o, S, ck = g.chunk_fwd(*args, chunk=chunk, plan=g.Plan(nseg, dv), ckpt_stride=stride)
+    torch.cuda.synchronize()
+    assert tuple(ck.shape) == (B, T // stride, H, dk, dv)
+    o_ref, S_ref = oracle.kda_chunked(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["S0"], chunk=chunk)
+    check(to_np(o), to_np(S), o_ref, S_ref, TOL[dtype], "checkpointed run")
+    for j in range(T // stride):
+        tj = (j + 1) * stride
+        pre = lambda a: a[:, :tj]  # noqa: E731
+        _, Sj = oracle.kda_chunked(pre(x["q"]), pre(x["k"]), pre(x["v"]), pre(x["log_alpha"]), pre(x["beta"]),
+                                   x["S0"], chunk=chunk)
+        ej = oracle.rel_fro(to_np(ck[:, j]), Sj)
+        _say(f"  checkpoint {j} (after {tj} tokens): rel_fro {ej:.3e}")
+        assert ej <= TOL[dtype], (j, ej)
