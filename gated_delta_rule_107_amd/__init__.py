@@ -38,7 +38,8 @@ class Plan(ctypes.Structure):
     state checkpoints."""
     _fields_ = [("n_segments", ctypes.c_int32), ("dv_block", ctypes.c_int32),
                 ("launch_events", ctypes.POINTER(ctypes.c_void_p)), ("n_launch_events", ctypes.c_int32),
-                ("state_ckpt", ctypes.c_void_p), ("ckpt_stride", ctypes.c_int64)]
+                ("state_ckpt", ctypes.c_void_p), ("ckpt_stride", ctypes.c_int64),
+                ("cu_seqlens", ctypes.c_void_p), ("n_seqs", ctypes.c_int32)]
 
     def __repr__(self):
         return f"Plan(n_segments={self.n_segments}, dv_block={self.dv_block})"
@@ -134,13 +135,15 @@ def workspace_bytes(B, T, H, dk, dv, chunk=64, dtype=torch.bfloat16, plan: Plan 
 
 
 def chunk_fwd(q, k, v, log_alpha, beta, S0=None, chunk: int = 64, plan: Plan | None = None,
-              o=None, S_T=None, workspace=None, ckpt_stride: int = 0, state_ckpt=None):
+              o=None, S_T=None, workspace=None, ckpt_stride: int = 0, state_ckpt=None, cu_seqlens=None):
     """Chunked prefill: returns (o [B,T,H,dv] in q's dtype, S_T [B,H,dk,dv] float32), and with
     ``ckpt_stride`` > 0 also the state checkpoints [B, T // ckpt_stride, H, dk, dv] float32
     (the state after every ckpt_stride tokens; a multiple of ``chunk``).
 
     ``S_T`` may be passed as ``S0`` itself to advance the state in place.
     ``plan`` (a Plan) overrides the library's default segmentation / column blocking.
+    ``cu_seqlens`` (int32 [N+1] on the device) packs N sequences along T of a single batch
+    row; S0 / S_T are then [N, H, dk, dv].
     """
     if q.dim() != 4:
         raise KdaError(2, "q must be [B,T,H,dk]")
@@ -155,16 +158,29 @@ def chunk_fwd(q, k, v, log_alpha, beta, S0=None, chunk: int = 64, plan: Plan | N
     _require(v, "v", q.dtype, (B, T, H, dv), dev)
     _require(log_alpha, "log_alpha", torch.float32, (B, T, H, dk), dev)
     _require(beta, "beta", torch.float32, (B, T, H), dev)
+    NS = B
+    if cu_seqlens is not None:
+        if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+            raise KdaError(2, "cu_seqlens must be [N+1] with N >= 1")
+        _require(cu_seqlens, "cu_seqlens", torch.int32, (cu_seqlens.numel(),), dev)
+        NS = cu_seqlens.numel() - 1
     if S0 is not None:
-        _require(S0, "S0", torch.float32, (B, H, dk, dv), dev)
+        _require(S0, "S0", torch.float32, (NS, H, dk, dv), dev)
     if o is None:
         o = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
     else:
         _require(o, "o", q.dtype, (B, T, H, dv), dev)
     if S_T is None:
-        S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+        S_T = torch.empty((NS, H, dk, dv), dtype=torch.float32, device=dev)
     else:
-        _require(S_T, "S_T", torch.float32, (B, H, dk, dv), dev)
+        _require(S_T, "S_T", torch.float32, (NS, H, dk, dv), dev)
+    if cu_seqlens is not None:
+        p2 = Plan()
+        if plan is not None:
+            ctypes.memmove(ctypes.addressof(p2), ctypes.addressof(plan), ctypes.sizeof(Plan))
+        p2.cu_seqlens = cu_seqlens.data_ptr()
+        p2.n_seqs = NS
+        plan = p2
     if ckpt_stride:
         if ckpt_stride < 0 or ckpt_stride % chunk:
             raise KdaError(5, f"ckpt_stride ({ckpt_stride}) must be a positive multiple of chunk ({chunk})")

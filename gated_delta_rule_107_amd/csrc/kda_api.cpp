@@ -76,7 +76,7 @@ struct Resolved {
 
 kda_status_t resolve_plan(int64_t B, int64_t T, int32_t H, int32_t dk, int32_t dv, int32_t chunk,
                           kda_dtype_t dt, const kda_plan_t* plan, Resolved* out) {
-    kda_plan_t p = plan ? *plan : kda_plan_t{0, 0, nullptr, 0, nullptr, 0};
+    kda_plan_t p = plan ? *plan : kda_plan_t{0, 0, nullptr, 0, nullptr, 0, nullptr, 0};
     int32_t dvb = p.dv_block;
     if (dvb == 0) dvb = dv;                                   // one column block per (b, h)
     if (dvb < 16 || dvb > 128 || dvb % 16 != 0 || dv % dvb != 0)
@@ -86,6 +86,10 @@ kda_status_t resolve_plan(int64_t B, int64_t T, int32_t H, int32_t dk, int32_t d
     const int64_t nchunks = (T + chunk - 1) / chunk;
     int64_t nseg = p.n_segments;
     if (nseg < 0) return fail(KDA_ERR_UNSUPPORTED, "n_segments must be >= 0");
+    if (p.cu_seqlens) {
+        if (nseg > 1) return fail(KDA_ERR_UNSUPPORTED, "packed sequences (cu_seqlens) run in one pass");
+        nseg = 1;
+    }
     if (nseg == 0) {
         // enough workgroups to cover every compute unit; segments only when (b, h, column
         // block) units alone cannot, and only if each segment keeps at least 2 chunks
@@ -166,7 +170,7 @@ kda_status_t kda_chunk_fwd_default_plan(int64_t B, int64_t T, int32_t H, int32_t
     Resolved r;
     s = resolve_plan(B, T, H, dk, dv, chunk, dt, nullptr, &r);
     if (s != KDA_OK) return s;
-    *plan = kda_plan_t{r.n_seg, r.dv_block, nullptr, 0, nullptr, 0};
+    *plan = kda_plan_t{r.n_seg, r.dv_block, nullptr, 0, nullptr, 0, nullptr, 0};
     return KDA_OK;
 }
 
@@ -193,6 +197,14 @@ kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v, const fl
     if (!S_T) return fail(KDA_ERR_NULL, "S_T is NULL");
     if (T > 0 && (!q || !k || !v || !log_alpha || !beta || !o))
         return fail(KDA_ERR_NULL, "q, k, v, log_alpha, beta and o are required when T > 0");
+    const int32_t* cu = plan ? plan->cu_seqlens : nullptr;
+    const int64_t n_seq = cu ? plan->n_seqs : B;            // state rows: sequences
+    if (cu) {
+        if (B != 1) return fail(KDA_ERR_SHAPE, "packed sequences (cu_seqlens) need B == 1 (got %lld)", (long long)B);
+        if (plan->n_seqs < 1) return fail(KDA_ERR_SHAPE, "n_seqs must be >= 1 (got %d)", plan->n_seqs);
+        if (reinterpret_cast<uintptr_t>(cu) % 4 != 0) return fail(KDA_ERR_ALIGN, "cu_seqlens is not 4-byte aligned");
+        if (plan->state_ckpt) return fail(KDA_ERR_UNSUPPORTED, "state checkpoints are not available with cu_seqlens");
+    }
     float* ckpt = plan ? plan->state_ckpt : nullptr;
     const int64_t ckpt_stride = ckpt ? plan->ckpt_stride : 0;
     if (ckpt && (ckpt_stride <= 0 || ckpt_stride % chunk != 0))
@@ -210,7 +222,7 @@ kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v, const fl
 
     const size_t es = dt == KDA_DTYPE_BF16 ? 2 : 4;
     const size_t n_qk = (size_t)(B * T * H) * dk, n_v = (size_t)(B * T * H) * dv;
-    const size_t n_s = (size_t)(B * H) * dk * dv * 4;
+    const size_t n_s = (size_t)(n_seq * H) * dk * dv * 4;
     const size_t n_o = n_v * es;
     struct Span { const void* p; size_t n; const char* name; } ins[] = {
         {q, n_qk * es, "q"}, {k, n_qk * es, "k"}, {v, n_v * es, "v"}, {log_alpha, n_qk * 4, "log_alpha"},
@@ -242,6 +254,8 @@ kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v, const fl
     a.B = B; a.T = T; a.H = H; a.dk = dk; a.dv = dv; a.chunk = chunk;
     a.n_seg = r.n_seg; a.seg_len = r.seg_len; a.dv_block = r.dv_block;
     a.ckpt = ckpt; a.ckpt_stride = ckpt_stride;
+    a.cu_seqlens = cu;
+    if (cu) a.B = n_seq;                      // units and state rows are sequences
     a.bf16 = dt == KDA_DTYPE_BF16;
     hipError_t e;
     if (r.n_seg == 1) {

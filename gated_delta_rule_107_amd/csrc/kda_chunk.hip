@@ -300,12 +300,22 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
         }
     }
     const int seg = (int)(unit % nseg_grid);
-    const int64_t bh = unit / nseg_grid;
+    const int64_t bh = unit / nseg_grid;                 // (sequence, head): indexes the states
     const int h = (int)(bh % H);
-    const int64_t b = bh / H;
     const int64_t T = a.T;
-    const int64_t t_begin = (int64_t)seg * a.seg_len;
-    const int64_t t_end = t_begin + a.seg_len < T ? t_begin + a.seg_len : T;
+    int64_t b = bh / H, t_begin, t_end;                 // b, t: index the token tensors
+    if (a.cu_seqlens) {
+        // packed sequences (one pass): sequence bh / H owns tokens [cu[i], cu[i+1]) of the
+        // single batch row; offsets are clamped into [0, T], so bad offsets cannot fault
+        const int64_t i = b;
+        b = 0;
+        const int64_t c0 = a.cu_seqlens[i], c1 = a.cu_seqlens[i + 1];
+        t_begin = c0 < 0 ? 0 : (c0 > T ? T : c0);
+        t_end = c1 < t_begin ? t_begin : (c1 > T ? T : c1);
+    } else {
+        t_begin = (int64_t)seg * a.seg_len;
+        t_end = t_begin + a.seg_len < T ? t_begin + a.seg_len : T;
+    }
 
     const int colw = (int)cb * DVB + 16 * wave;      // first (virtual) column of this wave
     const bool chain = 16 * wave < DVB;              // this wave owns state columns

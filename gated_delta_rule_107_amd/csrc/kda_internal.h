@@ -35,11 +35,12 @@ struct ChunkArgs {
     float* s_final;         // [B,H,dk,dv] (mode 0)
     float* s_loc;           // [B,H,P,dk,dv] (mode 1)
     void* m_tr;             // [B,H,P][2][dk][dk] bf16 (mode 1): M split into high and low parts
-    int64_t B, T;
+    int64_t B, T;           // with cu_seqlens: B = number of sequences, T = packed tokens
     int32_t H, dk, dv, chunk;
     int32_t n_seg;          // P
     int64_t seg_len;        // tokens per segment, a multiple of chunk
     int32_t dv_block;       // columns per workgroup (16 per wave)
+    const int32_t* cu_seqlens;  // [B + 1] packed sequence offsets into one batch row, or null
     float* ckpt;            // [B, T / ckpt_stride, H, dk, dv] state checkpoints (mode 0) or null
     int64_t ckpt_stride;    // tokens between checkpoints, a multiple of chunk
     int32_t mode;

@@ -86,6 +86,14 @@ typedef enum {
  *   the state after tokens ckpt_stride, 2 ckpt_stride, ... of each sequence
  *   (the start state S0 counts as the state before token 0).  It must be
  *   16-byte aligned and overlap no other argument.  NULL = no checkpoints.
+ * cu_seqlens / n_seqs: optional packed variable-length batch.  When
+ *   cu_seqlens is not NULL the call takes B == 1 and n_seqs sequences packed
+ *   along T: sequence i owns tokens [cu_seqlens[i], cu_seqlens[i+1]) (device
+ *   int32 array of n_seqs + 1 nondecreasing offsets from 0 to T; chunks start
+ *   at each sequence's first token), and S0 / S_T are [n_seqs, H, dk, dv].  One
+ *   pass only (n_segments 0 or 1) and no state checkpoints.  The offsets are
+ *   read on the device: values outside [0, T] are clamped, other invalid
+ *   arrays give unspecified (but in-bounds) results.
  * A zeroed plan (all fields 0 / NULL) means "library default" for each field.
  */
 typedef struct {
@@ -101,6 +109,8 @@ typedef struct {
     int32_t n_launch_events;
     float* state_ckpt;
     int64_t ckpt_stride;
+    const int32_t* cu_seqlens;
+    int32_t n_seqs;
 } kda_plan_t;
 
 /* Fills *plan with the library's default for this problem on the current

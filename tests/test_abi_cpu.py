@@ -103,6 +103,24 @@ def test_chunk_fwd_checkpoint_errors(lib):
     assert e.value.code in (2, 5)
 
 
+def test_chunk_fwd_packed_sequence_errors(lib):
+    import gated_delta_rule_107_amd as g
+
+    def plan_cu(n, nseg=1, ck=None):
+        p = g.Plan(nseg, 0)
+        p.cu_seqlens, p.n_seqs = A[10], n
+        if ck:
+            p.state_ckpt, p.ckpt_stride = ck, 32
+        return p
+    assert call_chunk(lib, B=2, plan=plan_cu(3)) == SHAPE           # packed means one batch row
+    assert call_chunk(lib, plan=plan_cu(0)) == SHAPE
+    assert call_chunk(lib, plan=plan_cu(3, nseg=2)) == UNSUP        # one pass only
+    assert call_chunk(lib, plan=plan_cu(3, ck=A[9])) == UNSUP       # no checkpoints
+    p = plan_cu(3)
+    p.cu_seqlens = A[10] + 2
+    assert call_chunk(lib, plan=p) == ALIGN
+
+
 def test_plan_and_workspace_queries(lib):
     import gated_delta_rule_107_amd as g
     import torch

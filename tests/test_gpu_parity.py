@@ -357,3 +357,38 @@ def test_state_checkpoints(g, shape, stride, nseg):
         ej = oracle.rel_fro(to_np(ck[:, j]), Sj)
         _say(f"  checkpoint {j} (after {tj} tokens): rel_fro {ej:.3e}")
         assert ej <= TOL[dtype], (j, ej)
+
+
+@pytest.mark.parametrize("dtype,lens,H,dk,dv,chunk", [
+    ("bf16", [100, 0, 64, 257, 1], 2, 128, 128, 64),
+    ("f32", [17, 48, 3], 2, 32, 64, 16),
+], ids=["bf16-5seq", "f32-3seq"])
+def test_packed_sequences(g, dtype, lens, H, dk, dv, chunk):
+    """Serving-shaped input: sequences of different lengths (an empty one included) packed
+    along T with cu_seqlens; each sequence's o and final state must equal the oracle run on
+    that sequence alone from its own start state."""
+    import torch
+    T = sum(lens)
+    r = small_recipe(dtype, 1, T, H, dk, dv, chunk)
+    _say(f"case: packed sequences {lens} {dtype} H{H} {dk}/{dv} chunk {chunk}")
+    x = ks.make_prefill(r)
+    N = len(lens)
+    rs = r.with_shape(s0_std=0.05)
+    S0 = np.stack([np.stack([ks.gen_state(rs, i, h) for h in range(H)]) for i in range(N)])
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    args = [dev_tensor(x[n], dt) for n in ("q", "k", "v")]
+    args += [dev_tensor(x["log_alpha"], torch.float32), dev_tensor(x["beta"], torch.float32),
+             dev_tensor(S0, torch.float32)]
+    o, S = g.chunk_fwd(*args, chunk=chunk, cu_seqlens=torch.from_numpy(cu).cuda())
+    torch.cuda.synchronize()
+    o, S = to_np(o), to_np(S)
+    for i in range(N):
+        a, b = int(cu[i]), int(cu[i + 1])
+        if b == a:
+            assert np.array_equal(S[i:i + 1], S0[i:i + 1].astype(np.float64)), "an empty sequence keeps its state"
+            continue
+        sl = lambda t: t[:, a:b]  # noqa: E731
+        o_ref, S_ref = oracle.kda_chunked(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["log_alpha"]),
+                                          sl(x["beta"]), S0[i:i + 1], chunk=chunk)
+        check(o[:, a:b], S[i:i + 1], o_ref, S_ref, TOL[dtype], f"sequence {i} ({b - a} tokens)")
