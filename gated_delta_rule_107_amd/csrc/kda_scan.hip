@@ -13,13 +13,15 @@
 //
 // The step chain is latency-bound, so nothing but the product sits on it:
 //   * M_i arrives already split (the segment pass writes its high and low bf16
-//     planes) and each wave keeps the rows of the next SCAN_DEPTH transitions in
-//     flight in registers;
+//     planes) and is copied from HBM straight into LDS (global_load_lds, 16 bytes
+//     per lane) one step ahead, into the other of two buffers, with an XOR
+//     swizzle of its 16-byte granules so that the A-operand reads are free of
+//     bank conflicts; S_loc_i is prefetched into registers one step ahead;
 //   * the new start state is split once, by the wave that produced it, into
 //     transposed bf16 high / low copies in LDS that every wave reads as its MFMA
 //     B operand with 16-byte loads;
 //   * one extra wave copies each start state (an fp32 copy in LDS) to HBM, so the
-//     product waves issue only loads.
+//     product waves' memory counter only tracks their own loads.
 // starts[0] receives a copy of S0 (or zeros), so the pass that follows never reads
 // S0 itself (S0 may alias the final state).
 #include "kda_device.h"
@@ -27,7 +29,14 @@
 
 namespace kda {
 
-constexpr int SCAN_DEPTH = 3;   // transitions in flight per wave
+// Workgroup barrier for LDS traffic only.  __syncthreads() also carries a workgroup
+// release fence, which waits for every vector-memory operation in flight, the
+// transition copy into LDS included; this barrier waits for this wave's own LDS
+// accesses (lgkmcnt) and, in lds_vm_barrier, for its vector-memory operations.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+__device__ __forceinline__ void lds_vm_barrier() {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 template <int DK>
 __global__ __launch_bounds__(64 * (DK / 16 + 1)) void scan_kernel(ScanArgs a) {
@@ -35,10 +44,15 @@ __global__ __launch_bounds__(64 * (DK / 16 + 1)) void scan_kernel(ScanArgs a) {
     constexpr int KSTEP = (DK + 31) / 32;         // 32-deep MFMA steps over the contraction
     constexpr int LDB = 32 * KSTEP + 8;           // bf16 pitch of the transposed split copies
     constexpr int LDF = DK + 4;                   // fp32 pitch of the transposed copy (store wave)
-    constexpr int D = SCAN_DEPTH;
+    constexpr int NG = DK / 8;                    // 16-byte granules per row of one plane
+    constexpr int NGX = NG < 8 ? NG : 8;          // swizzle period
+    constexpr int GM = 2 * DK * NG;               // granules of one transition (two planes)
+    constexpr int NI = GM / 64 / NW;              // copy instructions per product wave
+    static_assert(NI * 64 * NW == GM, "transition copy map");
     __shared__ __attribute__((aligned(16))) bf16 s_hi[16 * LDB];
     __shared__ __attribute__((aligned(16))) bf16 s_lo[16 * LDB];
     __shared__ __attribute__((aligned(16))) float s_f[16 * LDF];
+    __shared__ bf16x8 s_m[2 * GM];                // two transition buffers, swizzled granules
 
     // The column tiles of one (batch, head) are 8 block indices apart, so they run on one
     // XCD (workgroups go round-robin over the 8 XCDs) and share its L2 copy of M_i.
@@ -69,7 +83,7 @@ __global__ __launch_bounds__(64 * (DK / 16 + 1)) void scan_kernel(ScanArgs a) {
         s_hi[i] = (bf16)0.f;
         s_lo[i] = (bf16)0.f;
     }
-    __syncthreads();
+    lds_barrier();
 
     // publish rows row0 + 4g .. +3 of column m: fp32 for the store wave, split bf16 for the products
     auto put = [&](const f32x4& x) {
@@ -105,76 +119,79 @@ __global__ __launch_bounds__(64 * (DK / 16 + 1)) void scan_kernel(ScanArgs a) {
         put(cur);
     }
 
-    // transition rows of step i into slot u: lane (m, g) holds the high and low parts of
-    // M_i[row0 + m][32 s + 8 g .. + 7]; S_loc_i rows row0 + 4 g + r of column col
+    // LDS granule q of a buffer holds granule c = (q % NG) ^ (r % NGX) of row r = (q / NG) % DK
+    // of plane q / (DK NG); this lane copies granules (w NI + j) 64 + lane, j < NI
     const bf16* mt = reinterpret_cast<const bf16*>(a.m_tr);    // [B*H][P][2][DK][DK]
-    bf16x8 mh[D][KSTEP], ml[D][KSTEP];
-    f32x4 sl[D];
-    auto load_step = [&](int i, bf16x8 (&h)[KSTEP], bf16x8 (&l)[KSTEP], f32x4& s) {
-        const bf16* Mh = mt + ((bh * P + i) * 2) * DK * DK + (int64_t)(row0 + m) * DK;
-        const bf16* Ml = Mh + DK * DK;
+    unsigned src_off[NI];                                        // bf16 offsets inside one M_i
 #pragma unroll
-        for (int t = 0; t < KSTEP; ++t) {
-            const int k0 = 32 * t + 8 * g;
-            if (k0 < DK) {
-                h[t] = *reinterpret_cast<const bf16x8*>(Mh + k0);
-                l[t] = *reinterpret_cast<const bf16x8*>(Ml + k0);
-            } else {
+    for (int j = 0; j < NI; ++j) {
+        const int q = (w * NI + j) * 64 + lane;
+        const int pl = q / (DK * NG), r = (q / NG) % DK, c = (q % NG) ^ (r % NGX);
+        src_off[j] = (unsigned)((pl * DK + r) * DK + c * 8);
+    }
+    auto copy_m = [&](int i, int buf) {
+        const bf16* M = mt + (bh * P + i) * 2 * DK * DK;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) h[t][j] = l[t][j] = (bf16)0.f;
-            }
-        }
+        for (int j = 0; j < NI; ++j)
+            copy16_global_to_lds(M + src_off[j], s_m + buf * GM + (w * NI + j) * 64);
+    };
+    auto a_granule = [&](int buf, int pl, int r, int c) -> bf16x8 {
+        return s_m[buf * GM + (pl * DK + r) * NG + (c ^ (r % NGX))];
+    };
+    f32x4 sl;
+    auto load_sloc = [&](int i) {
         const float* L = a.s_loc + (bh * P + i) * DK * dv;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) s[r] = L[(int64_t)(row0 + 4 * g + r) * dv + col];
+        for (int r = 0; r < 4; ++r) sl[r] = L[(int64_t)(row0 + 4 * g + r) * dv + col];
     };
     const int nsteps = P - 1;
-    if (nsteps > 0 && !storer) {
-#pragma unroll
-        for (int u = 0; u < D; ++u) load_step(min(u, nsteps - 1), mh[u], ml[u], sl[u]);
-    }
 
-    // The store wave and the product waves run separate loops with the same barriers, so the
-    // product loop holds loads only and its memory counter waits cover exactly one slot.
+    // The store wave and the product waves run separate loops with the same barriers.
     if (storer) {
         for (int i = 0; i < nsteps; ++i) {
-            __syncthreads();                      // LDS holds the start of segment i
+            lds_barrier();                        // LDS holds the start of segment i
             store_start(i);
-            __syncthreads();
+            lds_barrier();
         }
-        __syncthreads();
+        lds_barrier();
         store_start(P - 1);
         return;
     }
-    // one step: the start of segment i (in LDS) times M_i plus S_loc_i, from slot u
-    auto step = [&](int i, int u, bool refill) {
-        __syncthreads();                          // LDS holds the start of segment i
-        f32x4 acc = sl[u], acc2 = {0.f, 0.f, 0.f, 0.f};
+    if (nsteps > 0) {
+        copy_m(0, 0);
+        load_sloc(0);
+    }
+    for (int i = 0; i < nsteps; ++i) {
+        const int buf = i & 1;
+        lds_vm_barrier();                         // every share of M_i landed; LDS holds start i
+        // operands into registers first, then the next transition's copy into the other buffer
+        bf16x8 ah[KSTEP], al[KSTEP], bh8[KSTEP], bl8[KSTEP];
 #pragma unroll
         for (int t = 0; t < KSTEP; ++t) {
-            const bf16x8 bh8 = *reinterpret_cast<const bf16x8*>(s_hi + m * LDB + 32 * t + 8 * g);
-            const bf16x8 bl8 = *reinterpret_cast<const bf16x8*>(s_lo + m * LDB + 32 * t + 8 * g);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mh[u][t], bh8, acc, 0, 0, 0);
-            acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mh[u][t], bl8, acc2, 0, 0, 0);
-            acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ml[u][t], bh8, acc2, 0, 0, 0);
+            const int c = 4 * t + g;
+            const bool in = 8 * c < DK;
+            const int r = row0 + m;
+            ah[t] = in ? a_granule(buf, 0, r, c) : bf16x8{};
+            al[t] = in ? a_granule(buf, 1, r, c) : bf16x8{};
+            bh8[t] = *reinterpret_cast<const bf16x8*>(s_hi + m * LDB + 32 * t + 8 * g);
+            bl8[t] = *reinterpret_cast<const bf16x8*>(s_lo + m * LDB + 32 * t + 8 * g);
         }
-        // the slot's registers are consumed: refill it with step i + D (clamped)
-        if (refill) load_step(min(i + D, nsteps - 1), mh[u], ml[u], sl[u]);
-        __syncthreads();                          // every wave has read the start of segment i
+        const f32x4 acc0 = sl;
+        if (i + 1 < nsteps) {
+            copy_m(i + 1, buf ^ 1);
+            load_sloc(i + 1);
+        }
+        f32x4 acc = acc0, acc2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < KSTEP; ++t) {
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[t], bh8[t], acc, 0, 0, 0);
+            acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[t], bl8[t], acc2, 0, 0, 0);
+            acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[t], bh8[t], acc2, 0, 0, 0);
+        }
+        lds_barrier();                            // every wave has read start i and M_i
         put(acc + acc2);
-    };
-    // Whole groups of D steps per iteration, so every slot keeps its registers across the
-    // back edge and the loop is entered only with the slots in load order; the last
-    // nsteps % D steps follow it.
-    int i = 0;
-    for (; i + D <= nsteps; i += D) {
-#pragma unroll
-        for (int u = 0; u < D; ++u) step(i + u, u, true);
     }
-#pragma unroll
-    for (int u = 0; u < D - 1; ++u)
-        if (i + u < nsteps) step(i + u, u, false);
-    __syncthreads();
+    lds_barrier();
 }
 
 template <int DK>
