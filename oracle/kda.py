@@ -23,6 +23,14 @@ Sources (web pages; section names translated from Korean):
   the state is updated sequentially and in place; zero-start states cannot be
   summed; each segment splits into (cumulative transition, zero-start state),
   which compose, and a prefix scan recovers every segment's start state.
+* [P1-act] same page, section "The floor that removed a GPU code path", read
+  backwards: the hardware's range fixed the tile interval, the interval fixed
+  the constant, and the constant made the gate's activation function need a
+  floor.
+* [P1-spec] same page, section "The cost comes back in the serving stack",
+  speculative decoding: the state is updated in place, so a rejected draft
+  cannot be rolled back; the per-token projection inputs, far smaller than the
+  state, are cached instead and the state is rebuilt from them on chip.
 * [P4-1] llm-wiki.hwlabs.dev, "Kimi K3 ... linear attention", section
   "1. Limits of softmax attention and KDA's direction" -- a fixed-size state
   matrix S is updated with each new token and the query is multiplied by S.
@@ -67,6 +75,18 @@ def floor_log_alpha(log_alpha):
     return np.minimum(np.maximum(_f64(log_alpha), LOG_ALPHA_FLOOR), 0.0)
 
 
+def gate_from_logits(x):
+    """Log-decay from raw gate logits through an activation floored at -5 ([P1-act]).
+
+    The pages name no formula.  Reading: the plainest bounded activation with that floor,
+    g = -5 * sigmoid(x) = -5 / (1 + e^-x), which lies in (-5, 0) (the clamp of
+    floor_log_alpha then changes nothing).  Large logits decay fastest.
+    """
+    x = _f64(x)
+    with np.errstate(over="ignore"):
+        return LOG_ALPHA_FLOOR / (1.0 + np.exp(-x))
+
+
 def _bhtd(x):
     """[B,T,H,D] -> [B,H,T,D] view."""
     return np.swapaxes(x, 1, 2)
@@ -102,6 +122,36 @@ def kda_decode_step(state, q, k, v, log_alpha, beta):
     o, S = kda_loop(_f64(q)[:, None], _f64(k)[:, None], _f64(v)[:, None],
                     _f64(log_alpha)[:, None], _f64(beta)[:, None], state)
     return o[:, 0], S
+
+
+def kda_decode_verify(state, q, k, v, log_alpha, beta):
+    """Speculative-decoding verify ([P1-spec]): the outputs of n draft tokens per sequence,
+    draft j read from the state advanced through drafts 0..j, with the caller's state left as
+    it was (an in-place update could not be rolled back after a rejection).
+
+    state [N,H,dk,dv]; q, k, log_alpha [N,n,H,dk]; v [N,n,H,dv]; beta [N,n,H].
+    Returns o [N,n,H,dv] float64.
+    """
+    o, _ = kda_loop(q, k, v, log_alpha, beta, state)
+    return o
+
+
+def kda_decode_commit(state, q, k, v, log_alpha, beta, n_accept):
+    """Commit after verification ([P1-spec]): the state of sequence i advanced by its first
+    n_accept[i] draft tokens (clamped to [0, n]), replayed from the cached per-token inputs.
+
+    Shapes as kda_decode_verify; n_accept [N] integers.  Returns the new state [N,H,dk,dv]
+    float64; the input is not modified.
+    """
+    out = _f64(state).copy()
+    n = np.shape(q)[1]
+    for i, m in enumerate(np.asarray(n_accept).reshape(-1)):
+        m = min(max(int(m), 0), n)
+        if m:
+            _, S = kda_loop(_f64(q)[i:i + 1, :m], _f64(k)[i:i + 1, :m], _f64(v)[i:i + 1, :m],
+                            _f64(log_alpha)[i:i + 1, :m], _f64(beta)[i:i + 1, :m], out[i:i + 1])
+            out[i] = S[0]
+    return out
 
 
 def kda_bruteforce(q, k, v, log_alpha, beta, S0=None):

@@ -314,3 +314,46 @@ def test_floor_clamps_out_of_range_gates():
     o3, _ = oracle.kda_loop(q, k, v, np.where(la_out < -5, -9.0, la_in), beta, S0)
     assert np.array_equal(o3, o1)          # the oracle itself clamps -9 to -5
     assert oracle.floor_log_alpha(np.array([-9.0, -5.0, -1.0, 0.0, 0.4])).tolist() == [-5, -5, -1, 0, 0]
+
+
+# ---------------------------------------------------------------- gate activation with a floor
+
+def test_gate_from_logits_against_library_sigmoid():
+    """-5 sigmoid(x): pinned to scipy's logistic function, its fixed point and both limits."""
+    from scipy.special import expit
+    x = np.linspace(-40.0, 40.0, 801)
+    g = oracle.gate_from_logits(x)
+    assert np.abs(g - (-5.0 * expit(x))).max() < 1e-14
+    assert oracle.gate_from_logits(0.0) == -2.5                       # sigmoid(0) = 1/2 exactly
+    assert oracle.gate_from_logits(800.0) == -5.0                     # the floor, reached in the limit
+    assert oracle.gate_from_logits(-800.0) == 0.0                     # no decay in the other limit
+    x = np.linspace(-30.0, 30.0, 601)                                  # sigmoid(x) < 1 in float64
+    g = oracle.gate_from_logits(x)
+    assert np.all(np.diff(g) < 0) and np.all((g > -5.0) & (g < 0.0))
+    # inside [-5, 0] already: the clamp of the recurrence changes nothing
+    assert np.array_equal(oracle.floor_log_alpha(g), g)
+
+
+# ---------------------------------------------------------------- speculative verify / commit
+
+def test_decode_verify_matches_bruteforce_and_keeps_state():
+    q, k, v, la, beta, S0 = rnd_inputs(21, B=3, T=6, H=2)
+    S_keep = S0.copy()
+    o = oracle.kda_decode_verify(S0, q, k, v, la, beta)
+    o_bf, _ = oracle.kda_bruteforce(q, k, v, la, beta, S0)
+    assert rel_fro(o, o_bf) < 1e-12
+    assert np.array_equal(S0, S_keep)
+
+
+def test_decode_commit_matches_bruteforce_prefixes():
+    q, k, v, la, beta, S0 = rnd_inputs(22, B=5, T=6, H=2)
+    n_accept = [0, 3, 6, 9, -2]                                        # 9 and -2 are clamped
+    S = oracle.kda_decode_commit(S0, q, k, v, la, beta, n_accept)
+    for i, m in enumerate(n_accept):
+        m = min(max(m, 0), 6)
+        if m == 0:
+            assert np.array_equal(S[i], S0[i])
+            continue
+        sl = slice(i, i + 1)
+        _, S_bf = oracle.kda_bruteforce(q[sl, :m], k[sl, :m], v[sl, :m], la[sl, :m], beta[sl, :m], S0[sl])
+        assert rel_fro(S[i], S_bf[0]) < 1e-12
