@@ -8,6 +8,11 @@ call raises ImportError if it has not been built
 
     o, S_T = chunk_fwd(q, k, v, log_alpha, beta, S0=None, chunk=64)
     o      = decode_step(state, q, k, v, log_alpha, beta)      # state updated in place
+    o      = decode_verify(state, q, k, v, log_alpha, beta)    # n draft tokens, state untouched
+    decode_commit(state, q, k, v, log_alpha, beta, n_accept)   # replay the accepted drafts
+
+``gate=GATE_LOGITS`` makes every call read log_alpha as raw gate logits x, with the
+log-decay -5 sigmoid(x) formed inside the kernels.
 """
 from __future__ import annotations
 
@@ -16,8 +21,8 @@ import os
 
 import torch
 
-__all__ = ["KdaError", "Plan", "chunk_fwd", "decode_step", "default_plan", "workspace_bytes",
-           "library_path", "ERRORS"]
+__all__ = ["KdaError", "Plan", "chunk_fwd", "decode_step", "decode_verify", "decode_commit",
+           "default_plan", "workspace_bytes", "library_path", "ERRORS", "GATE_LOG_DECAY", "GATE_LOGITS"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libkda.so")
@@ -25,6 +30,7 @@ _LIB_PATH = os.path.join(_PKG, "libkda.so")
 ERRORS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE", 4: "KDA_ERR_ALIGN",
           5: "KDA_ERR_UNSUPPORTED", 6: "KDA_ERR_WORKSPACE", 7: "KDA_ERR_HIP", 8: "KDA_ERR_ALIAS"}
 DTYPE_F32, DTYPE_BF16 = 0, 1
+GATE_LOG_DECAY, GATE_LOGITS = 0, 1
 
 
 class KdaError(RuntimeError):
@@ -34,12 +40,12 @@ class KdaError(RuntimeError):
 
 
 class Plan(ctypes.Structure):
-    """kda_plan_t: segmentation, column blocking, optional launch-timing events and optional
-    state checkpoints."""
+    """kda_plan_t: segmentation, column blocking, optional launch-timing events, optional
+    state checkpoints, packed sequences and the gate mode."""
     _fields_ = [("n_segments", ctypes.c_int32), ("dv_block", ctypes.c_int32),
                 ("launch_events", ctypes.POINTER(ctypes.c_void_p)), ("n_launch_events", ctypes.c_int32),
                 ("state_ckpt", ctypes.c_void_p), ("ckpt_stride", ctypes.c_int64),
-                ("cu_seqlens", ctypes.c_void_p), ("n_seqs", ctypes.c_int32)]
+                ("cu_seqlens", ctypes.c_void_p), ("n_seqs", ctypes.c_int32), ("gate", ctypes.c_int32)]
 
     def __repr__(self):
         return f"Plan(n_segments={self.n_segments}, dv_block={self.dv_block})"
@@ -54,7 +60,11 @@ def _load():
     lib.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, i32,
                                   ctypes.POINTER(Plan), vp, sz, vp]
     lib.kda_decode_step.restype = i32
-    lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, vp]
+    lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, vp]
+    lib.kda_decode_verify.restype = i32
+    lib.kda_decode_verify.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, vp]
+    lib.kda_decode_commit.restype = i32
+    lib.kda_decode_commit.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, vp]
     lib.kda_chunk_fwd_default_plan.restype = i32
     lib.kda_chunk_fwd_default_plan.argtypes = [i64, i64, i32, i32, i32, i32, i32, ctypes.POINTER(Plan)]
     lib.kda_chunk_fwd_workspace_bytes.restype = i32
@@ -134,8 +144,22 @@ def workspace_bytes(B, T, H, dk, dv, chunk=64, dtype=torch.bfloat16, plan: Plan 
     return n.value
 
 
+def _plan_copy(plan: Plan | None) -> Plan:
+    p2 = Plan()
+    if plan is not None:
+        ctypes.memmove(ctypes.addressof(p2), ctypes.addressof(plan), ctypes.sizeof(Plan))
+    return p2
+
+
+def _gate_code(gate: int) -> int:
+    if gate not in (GATE_LOG_DECAY, GATE_LOGITS):
+        raise KdaError(5, f"unknown gate mode {gate}")
+    return gate
+
+
 def chunk_fwd(q, k, v, log_alpha, beta, S0=None, chunk: int = 64, plan: Plan | None = None,
-              o=None, S_T=None, workspace=None, ckpt_stride: int = 0, state_ckpt=None, cu_seqlens=None):
+              o=None, S_T=None, workspace=None, ckpt_stride: int = 0, state_ckpt=None, cu_seqlens=None,
+              gate: int = GATE_LOG_DECAY):
     """Chunked prefill: returns (o [B,T,H,dv] in q's dtype, S_T [B,H,dk,dv] float32), and with
     ``ckpt_stride`` > 0 also the state checkpoints [B, T // ckpt_stride, H, dk, dv] float32
     (the state after every ckpt_stride tokens; a multiple of ``chunk``).
@@ -144,6 +168,7 @@ def chunk_fwd(q, k, v, log_alpha, beta, S0=None, chunk: int = 64, plan: Plan | N
     ``plan`` (a Plan) overrides the library's default segmentation / column blocking.
     ``cu_seqlens`` (int32 [N+1] on the device) packs N sequences along T of a single batch
     row; S0 / S_T are then [N, H, dk, dv].
+    ``gate=GATE_LOGITS``: log_alpha holds raw gate logits (log-decay -5 sigmoid(x)).
     """
     if q.dim() != 4:
         raise KdaError(2, "q must be [B,T,H,dk]")
@@ -174,10 +199,11 @@ def chunk_fwd(q, k, v, log_alpha, beta, S0=None, chunk: int = 64, plan: Plan | N
         S_T = torch.empty((NS, H, dk, dv), dtype=torch.float32, device=dev)
     else:
         _require(S_T, "S_T", torch.float32, (NS, H, dk, dv), dev)
+    if _gate_code(gate):
+        plan = _plan_copy(plan)
+        plan.gate = gate
     if cu_seqlens is not None:
-        p2 = Plan()
-        if plan is not None:
-            ctypes.memmove(ctypes.addressof(p2), ctypes.addressof(plan), ctypes.sizeof(Plan))
+        p2 = _plan_copy(plan)
         p2.cu_seqlens = cu_seqlens.data_ptr()
         p2.n_seqs = NS
         plan = p2
@@ -189,9 +215,7 @@ def chunk_fwd(q, k, v, log_alpha, beta, S0=None, chunk: int = 64, plan: Plan | N
             state_ckpt = torch.empty((B, nck, H, dk, dv), dtype=torch.float32, device=dev)
         else:
             _require(state_ckpt, "state_ckpt", torch.float32, (B, nck, H, dk, dv), dev)
-        p2 = Plan()
-        if plan is not None:
-            ctypes.memmove(ctypes.addressof(p2), ctypes.addressof(plan), ctypes.sizeof(Plan))
+        p2 = _plan_copy(plan)
         if nck > 0:                          # (T < ckpt_stride: no checkpoint to write)
             p2.state_ckpt = state_ckpt.data_ptr()
             p2.ckpt_stride = ckpt_stride
@@ -212,10 +236,9 @@ def chunk_fwd(q, k, v, log_alpha, beta, S0=None, chunk: int = 64, plan: Plan | N
     return o, S_T
 
 
-def decode_step(state, q, k, v, log_alpha, beta, o=None):
-    """One recurrent step for N sequences; ``state`` [N,H,dk,dv] float32 is updated in place.
-    q, k [N,H,dk], v [N,H,dv] (bf16 or float32), log_alpha [N,H,dk], beta [N,H] float32.
-    Returns o [N,H,dv]."""
+def _decode_inputs(state, q, k, v, log_alpha, beta, n_tok):
+    """Checks the decode family's tensors; per-token tensors are [N,H,.] for a step
+    (n_tok None) or [N,n,H,.]. Returns (N, H, dk, dv, n, dt, dev)."""
     if state.dim() != 4:
         raise KdaError(2, "state must be [N,H,dk,dv]")
     N, H, dk, dv = state.shape
@@ -223,16 +246,56 @@ def decode_step(state, q, k, v, log_alpha, beta, o=None):
     if dev.type != "cuda":
         raise KdaError(2, "tensors must be on a GPU")
     dt = _dtype_code(q)
+    lead = (N, H) if n_tok is None else (N, n_tok, H)
     _require(state, "state", torch.float32, (N, H, dk, dv), dev)
-    _require(q, "q", q.dtype, (N, H, dk), dev)
-    _require(k, "k", q.dtype, (N, H, dk), dev)
-    _require(v, "v", q.dtype, (N, H, dv), dev)
-    _require(log_alpha, "log_alpha", torch.float32, (N, H, dk), dev)
-    _require(beta, "beta", torch.float32, (N, H), dev)
+    _require(q, "q", q.dtype, lead + (dk,), dev)
+    _require(k, "k", q.dtype, lead + (dk,), dev)
+    _require(v, "v", q.dtype, lead + (dv,), dev)
+    _require(log_alpha, "log_alpha", torch.float32, lead + (dk,), dev)
+    _require(beta, "beta", torch.float32, lead, dev)
+    return N, H, dk, dv, dt, dev
+
+
+def decode_step(state, q, k, v, log_alpha, beta, o=None, gate: int = GATE_LOG_DECAY):
+    """One recurrent step for N sequences; ``state`` [N,H,dk,dv] float32 is updated in place.
+    q, k [N,H,dk], v [N,H,dv] (bf16 or float32), log_alpha [N,H,dk], beta [N,H] float32.
+    Returns o [N,H,dv]."""
+    N, H, dk, dv, dt, dev = _decode_inputs(state, q, k, v, log_alpha, beta, None)
     if o is None:
         o = torch.empty((N, H, dv), dtype=q.dtype, device=dev)
     else:
         _require(o, "o", q.dtype, (N, H, dv), dev)
     _check(lib().kda_decode_step(_ptr(state), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
-                                _ptr(o), N, H, dk, dv, dt, _stream(dev)))
+                                _ptr(o), N, H, dk, dv, dt, _gate_code(gate), _stream(dev)))
     return o
+
+
+def decode_verify(state, q, k, v, log_alpha, beta, o=None, gate: int = GATE_LOG_DECAY):
+    """Speculative decoding, verify: outputs of n draft tokens per sequence from ``state``
+    [N,H,dk,dv], which is left unchanged.  q, k [N,n,H,dk], v [N,n,H,dv], log_alpha [N,n,H,dk],
+    beta [N,n,H].  Returns o [N,n,H,dv] (draft j read after drafts 0..j)."""
+    if q.dim() != 4:
+        raise KdaError(2, "q must be [N,n,H,dk]")
+    n = q.shape[1]
+    N, H, dk, dv, dt, dev = _decode_inputs(state, q, k, v, log_alpha, beta, n)
+    if o is None:
+        o = torch.empty((N, n, H, dv), dtype=q.dtype, device=dev)
+    else:
+        _require(o, "o", q.dtype, (N, n, H, dv), dev)
+    _check(lib().kda_decode_verify(_ptr(state), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                  _ptr(o), N, n, H, dk, dv, dt, _gate_code(gate), _stream(dev)))
+    return o
+
+
+def decode_commit(state, q, k, v, log_alpha, beta, n_accept, gate: int = GATE_LOG_DECAY):
+    """Speculative decoding, commit: advances ``state`` [N,H,dk,dv] in place by the first
+    n_accept[i] (int32 [N] on the device, clamped to [0, n]) of sequence i's n draft tokens,
+    given as for decode_verify.  Returns state."""
+    if q.dim() != 4:
+        raise KdaError(2, "q must be [N,n,H,dk]")
+    n = q.shape[1]
+    N, H, dk, dv, dt, dev = _decode_inputs(state, q, k, v, log_alpha, beta, n)
+    _require(n_accept, "n_accept", torch.int32, (N,), dev)
+    _check(lib().kda_decode_commit(_ptr(state), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                  _ptr(n_accept), N, n, H, dk, dv, dt, _gate_code(gate), _stream(dev)))
+    return state

@@ -76,7 +76,7 @@ struct Resolved {
 
 kda_status_t resolve_plan(int64_t B, int64_t T, int32_t H, int32_t dk, int32_t dv, int32_t chunk,
                           kda_dtype_t dt, const kda_plan_t* plan, Resolved* out) {
-    kda_plan_t p = plan ? *plan : kda_plan_t{0, 0, nullptr, 0, nullptr, 0, nullptr, 0};
+    kda_plan_t p = plan ? *plan : kda_plan_t{};
     int32_t dvb = p.dv_block;
     if (dvb == 0) dvb = dv;                                   // one column block per (b, h)
     if (dvb < 16 || dvb > 128 || dvb % 16 != 0 || dv % dvb != 0)
@@ -170,7 +170,9 @@ kda_status_t kda_chunk_fwd_default_plan(int64_t B, int64_t T, int32_t H, int32_t
     Resolved r;
     s = resolve_plan(B, T, H, dk, dv, chunk, dt, nullptr, &r);
     if (s != KDA_OK) return s;
-    *plan = kda_plan_t{r.n_seg, r.dv_block, nullptr, 0, nullptr, 0, nullptr, 0};
+    *plan = kda_plan_t{};
+    plan->n_segments = r.n_seg;
+    plan->dv_block = r.dv_block;
     return KDA_OK;
 }
 
@@ -205,6 +207,8 @@ kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v, const fl
         if (reinterpret_cast<uintptr_t>(cu) % 4 != 0) return fail(KDA_ERR_ALIGN, "cu_seqlens is not 4-byte aligned");
         if (plan->state_ckpt) return fail(KDA_ERR_UNSUPPORTED, "state checkpoints are not available with cu_seqlens");
     }
+    const int32_t gate = plan ? plan->gate : 0;
+    if (gate != KDA_GATE_LOG_DECAY && gate != KDA_GATE_LOGITS) return fail(KDA_ERR_UNSUPPORTED, "unknown gate mode %d", gate);
     float* ckpt = plan ? plan->state_ckpt : nullptr;
     const int64_t ckpt_stride = ckpt ? plan->ckpt_stride : 0;
     if (ckpt && (ckpt_stride <= 0 || ckpt_stride % chunk != 0))
@@ -255,6 +259,7 @@ kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v, const fl
     a.n_seg = r.n_seg; a.seg_len = r.seg_len; a.dv_block = r.dv_block;
     a.ckpt = ckpt; a.ckpt_stride = ckpt_stride;
     a.cu_seqlens = cu;
+    a.gate = gate;
     if (cu) a.B = n_seq;                      // units and state rows are sequences
     a.bf16 = dt == KDA_DTYPE_BF16;
     hipError_t e;
@@ -297,30 +302,78 @@ kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v, const fl
     return KDA_OK;
 }
 
-kda_status_t kda_decode_step(float* state, const void* q, const void* k, const void* v,
-                             const float* log_alpha, const float* beta, void* o, int64_t N,
-                             int32_t H, int32_t dk, int32_t dv, kda_dtype_t dt, void* stream) {
-    if (N < 1 || H < 1) return fail(KDA_ERR_SHAPE, "need N >= 1, H >= 1 (got N=%lld H=%d)", (long long)N, H);
+}  // extern "C"
+
+namespace {
+
+// Shared validation of the decode family: n_tok tokens per sequence; `state_out` says whether
+// the call writes the state (then it must overlap no input), `o` may be null (commit).
+kda_status_t decode_call(int mode, float* state, const void* q, const void* k, const void* v,
+                         const float* log_alpha, const float* beta, void* o, const int32_t* n_accept,
+                         int64_t N, int32_t n_tok, int32_t H, int32_t dk, int32_t dv, kda_dtype_t dt,
+                         kda_gate_t gate, void* stream) {
+    if (N < 1 || H < 1 || n_tok < 1)
+        return fail(KDA_ERR_SHAPE, "need N >= 1, H >= 1, n_draft >= 1 (got N=%lld H=%d n=%d)", (long long)N, H, n_tok);
     if (dt != KDA_DTYPE_F32 && dt != KDA_DTYPE_BF16) return fail(KDA_ERR_DTYPE, "unknown dtype %d", (int)dt);
     if (!dim_ok(dk) || !dim_ok(dv)) return fail(KDA_ERR_UNSUPPORTED, "dk, dv must be 16, 32, 64 or 128 (got %d, %d)", dk, dv);
-    if (N * (int64_t)H > 0x7fffffff) return fail(KDA_ERR_SHAPE, "N * H too large");
-    if (!state || !q || !k || !v || !log_alpha || !beta || !o) return fail(KDA_ERR_NULL, "all pointers are required");
+    if (gate != KDA_GATE_LOG_DECAY && gate != KDA_GATE_LOGITS) return fail(KDA_ERR_UNSUPPORTED, "unknown gate mode %d", (int)gate);
+    if (N * (int64_t)H * n_tok > 0x7fffffff) return fail(KDA_ERR_SHAPE, "N * n_draft * H too large");
+    const bool want_o = mode != kda::DECODE_COMMIT;
+    if (!state || !q || !k || !v || !log_alpha || !beta || (want_o && !o) || (!want_o && !n_accept))
+        return fail(KDA_ERR_NULL, "all pointers are required");
     const void* ptrs[] = {state, q, k, v, log_alpha, beta, o};
     for (const void* p : ptrs)
-        if (!aligned(p)) return fail(KDA_ERR_ALIGN, "pointer %p is not 16-byte aligned", p);
+        if (p && !aligned(p)) return fail(KDA_ERR_ALIGN, "pointer %p is not 16-byte aligned", p);
+    if (n_accept && reinterpret_cast<uintptr_t>(n_accept) % 4 != 0) return fail(KDA_ERR_ALIGN, "n_accept is not 4-byte aligned");
     const size_t es = dt == KDA_DTYPE_BF16 ? 2 : 4;
-    const size_t nh = (size_t)N * H;
+    const size_t nh = (size_t)N * H, nth = nh * n_tok;
     struct Span { const void* p; size_t n; const char* name; } ins[] = {
-        {state, nh * dk * dv * 4, "state"}, {q, nh * dk * es, "q"}, {k, nh * dk * es, "k"}, {v, nh * dv * es, "v"},
-        {log_alpha, nh * dk * 4, "log_alpha"}, {beta, nh * 4, "beta"}};
-    for (const Span& in : ins)
-        if (overlaps(o, nh * dv * es, in.p, in.n)) return fail(KDA_ERR_ALIAS, "o overlaps %s", in.name);
-    for (int i = 1; i < 6; ++i)
-        if (overlaps(state, ins[0].n, ins[i].p, ins[i].n)) return fail(KDA_ERR_ALIAS, "state overlaps %s", ins[i].name);
-    kda::DecodeArgs a{state, q, k, v, log_alpha, beta, o, N, H, dk, dv, dt == KDA_DTYPE_BF16};
+        {state, nh * dk * dv * 4, "state"}, {q, nth * dk * es, "q"}, {k, nth * dk * es, "k"}, {v, nth * dv * es, "v"},
+        {log_alpha, nth * dk * 4, "log_alpha"}, {beta, nth * 4, "beta"}, {n_accept, n_accept ? (size_t)N * 4 : 0, "n_accept"}};
+    if (want_o)
+        for (const Span& in : ins)
+            if (overlaps(o, nth * dv * es, in.p, in.n)) return fail(KDA_ERR_ALIAS, "o overlaps %s", in.name);
+    if (mode != kda::DECODE_VERIFY)
+        for (int i = 1; i < 7; ++i)
+            if (overlaps(state, ins[0].n, ins[i].p, ins[i].n)) return fail(KDA_ERR_ALIAS, "state overlaps %s", ins[i].name);
+    kda::DecodeArgs a{};
+    a.state = state; a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta;
+    a.o = want_o ? o : nullptr;
+    a.n_accept = n_accept;
+    a.N = N; a.n_tok = n_tok; a.H = H; a.dk = dk; a.dv = dv;
+    a.mode = mode; a.gate = gate; a.bf16 = dt == KDA_DTYPE_BF16;
     hipError_t e = kda::launch_decode(a, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
     return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status_t kda_decode_step(float* state, const void* q, const void* k, const void* v,
+                             const float* log_alpha, const float* beta, void* o, int64_t N,
+                             int32_t H, int32_t dk, int32_t dv, kda_dtype_t dt, kda_gate_t gate,
+                             void* stream) {
+    return decode_call(kda::DECODE_STEP, state, q, k, v, log_alpha, beta, o, nullptr, N, 1, H, dk, dv, dt,
+                       gate, stream);
+}
+
+kda_status_t kda_decode_verify(const float* state, const void* q, const void* k, const void* v,
+                               const float* log_alpha, const float* beta, void* o, int64_t N,
+                               int32_t n_draft, int32_t H, int32_t dk, int32_t dv, kda_dtype_t dt,
+                               kda_gate_t gate, void* stream) {
+    // the kernel of this mode never writes the state
+    return decode_call(kda::DECODE_VERIFY, const_cast<float*>(state), q, k, v, log_alpha, beta, o, nullptr, N,
+                       n_draft, H, dk, dv, dt, gate, stream);
+}
+
+kda_status_t kda_decode_commit(float* state, const void* q, const void* k, const void* v,
+                               const float* log_alpha, const float* beta, const int32_t* n_accept,
+                               int64_t N, int32_t n_draft, int32_t H, int32_t dk, int32_t dv,
+                               kda_dtype_t dt, kda_gate_t gate, void* stream) {
+    return decode_call(kda::DECODE_COMMIT, state, q, k, v, log_alpha, beta, nullptr, n_accept, N, n_draft, H,
+                       dk, dv, dt, gate, stream);
 }
 
 }  // extern "C"

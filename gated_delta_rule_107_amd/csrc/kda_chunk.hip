@@ -535,6 +535,12 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
             // zeroed here (idle channel lanes of DK < 128 only feed their own 16-lane rows,
             // whose stores are skipped).  k and q stay in their packed prefetch registers until
             // they are used.
+            if (a.gate) {                                  // raw logits: -5 sigmoid (uniform branch)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) pla[j][e] = gate_from_logit(pla[j][e]);
+            }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const bool ok = full || 4 * tq + j < Tn;

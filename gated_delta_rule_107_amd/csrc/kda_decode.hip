@@ -1,4 +1,5 @@
-// Recurrent decode step: one token per sequence, state updated in place.
+// Recurrent decode: one token per sequence with the state updated in place, and the
+// multi-token verify / commit pair of speculative decoding built on the same step.
 //
 // Per (sequence n, head h), with D = Diag(exp(g)) and g the floored log-decay:
 //     DS = D S;  p = (DS)^T k;  r = (DS)^T q;  u = beta (v - p)
@@ -31,22 +32,38 @@ template <int DK, int DV> struct DecodeMap {
     static constexpr int NWV = NTB / WAVE;
 };
 
-template <typename ET, int DK, int DV>
+// MODE 0 (DECODE_STEP): one token per sequence, o written, state updated in place.
+// MODE 1 (DECODE_VERIFY): n_tok draft tokens per sequence, o written for each, the state
+//   kept in registers only: the caller's state is left as it was, since an in-place update
+//   could not be rolled back after a rejected draft.
+// MODE 2 (DECODE_COMMIT): the state advanced by the first n_accept[n] draft tokens of
+//   sequence n, replayed from their cached per-token inputs (q, k, v, gate, beta: far
+//   smaller than the state), no o.
+// Both follow orkas.ai "Kimi K3 architecture", section "The cost comes back in the serving
+// stack" (speculative decoding).  Token j of sequence n, head h sits at token-head index
+// (n n_tok + j) H + h of q, k, v, the gates, beta and o.
+template <typename ET, int DK, int DV, int MODE>
 __global__ __launch_bounds__((DecodeMap<DK, DV>::NTB)) __attribute__((amdgpu_waves_per_eu(8))) void decode_kernel(
     float* __restrict__ state, const ET* __restrict__ q, const ET* __restrict__ k,
     const ET* __restrict__ v, const float* __restrict__ log_alpha,
-    const float* __restrict__ beta, ET* __restrict__ o) {
+    const float* __restrict__ beta, ET* __restrict__ o, const int* __restrict__ n_accept,
+    int H, int n_tok, int gate) {
     using DM = DecodeMap<DK, DV>;
     constexpr int CG = DM::CG, RG = DM::RG, RPT = DM::RPT, NT = DM::NT, NWV = DM::NWV;
     static_assert(DK % RG == 0 && DK <= NT && 4 * CG <= NT, "decode thread map");
+    constexpr bool want_o = MODE != DECODE_COMMIT;
+    constexpr bool write_state = MODE != DECODE_VERIFY;
 
-    const size_t unit = blockIdx.x;
+    const size_t unit = blockIdx.x;                 // n H + h
+    const size_t n = unit / (unsigned)H, h = unit - n * (unsigned)H;
     const int tid = threadIdx.x;
     const bool act = tid < NT;                      // (small shapes: the last wave is partial)
     const int cg = tid % CG, rg = tid / CG;
     const int w = tid / WAVE;
 
-    __shared__ float s_a[DK], s_k[DK], s_q[DK];
+    // per-token vectors are double-buffered by token parity: token j+1 writes its copy while
+    // threads may still read token j's in the state update
+    __shared__ float s_a[2][DK], s_k[2][DK], s_q[2][DK];
     __shared__ f32x4 s_p[NWV][CG], s_r[NWV][CG];
     __shared__ float s_kq[NWV];
     __shared__ f32x4 s_u[CG];
@@ -57,82 +74,104 @@ __global__ __launch_bounds__((DecodeMap<DK, DV>::NTB)) __attribute__((amdgpu_wav
 #pragma unroll
         for (int i = 0; i < RPT; ++i) sv[i] = __builtin_nontemporal_load(&S[(rg + i * RG) * CG + cg]);
     }
+    int cnt = MODE == DECODE_STEP ? 1 : n_tok;
+    if (MODE == DECODE_COMMIT) cnt = min(max(n_accept[n], 0), n_tok);
 
-    float kq = 0.f;
-    if (tid < DK) {
-        const float a = fast_exp(clamp_log_alpha(log_alpha[unit * DK + tid]));
-        const float kk = to_f32(k[unit * DK + tid]);
-        const float qq = to_f32(q[unit * DK + tid]);
-        s_a[tid] = a;
-        s_k[tid] = kk;
-        s_q[tid] = qq;
-        kq = kk * qq;
-    }
+    for (int j = 0; j < cnt; ++j) {
+        const int buf = j & 1;
+        const size_t th = (n * (unsigned)n_tok + j) * (unsigned)H + h;   // token-head index
+        float kq = 0.f;
+        if (tid < DK) {
+            const float kk = to_f32(k[th * DK + tid]);
+            s_a[buf][tid] = fast_exp(log_decay(log_alpha[th * DK + tid], gate));
+            s_k[buf][tid] = kk;
+            if (want_o) {
+                const float qq = to_f32(q[th * DK + tid]);
+                s_q[buf][tid] = qq;
+                kq = kk * qq;
+            }
+        }
+        if (want_o) {
 #pragma unroll
-    for (int m = WAVE / 2; m >= 1; m >>= 1) kq += __shfl_xor(kq, m);
-    if ((tid & (WAVE - 1)) == 0) s_kq[w] = kq;
-    __syncthreads();
+            for (int m = WAVE / 2; m >= 1; m >>= 1) kq += __shfl_xor(kq, m);
+            if ((tid & (WAVE - 1)) == 0) s_kq[w] = kq;
+        }
+        __syncthreads();
 
-    // decay the state; partial column sums p = (DS)^T k, r = (DS)^T q over this thread's rows
-    f32x4 p = {0.f, 0.f, 0.f, 0.f}, r = {0.f, 0.f, 0.f, 0.f};
-    if (act) {
+        // decay the state; partial column sums p = (DS)^T k, r = (DS)^T q over this thread's rows
+        f32x4 p = {0.f, 0.f, 0.f, 0.f}, r = {0.f, 0.f, 0.f, 0.f};
+        if (act) {
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-            const int row = rg + i * RG;
-            sv[i] *= s_a[row];
-            p += sv[i] * s_k[row];
-            r += sv[i] * s_q[row];
+            for (int i = 0; i < RPT; ++i) {
+                const int row = rg + i * RG;
+                sv[i] *= s_a[buf][row];
+                p += sv[i] * s_k[buf][row];
+                if (want_o) r += sv[i] * s_q[buf][row];
+            }
+        }
+        // reduce over the row groups that share a wave (lanes differing in bits >= log2 CG)
+#pragma unroll
+        for (int m = CG; m < WAVE; m <<= 1) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                p[e] += __shfl_xor(p[e], m);
+                if (want_o) r[e] += __shfl_xor(r[e], m);
+            }
+        }
+        if ((tid & (WAVE - 1)) < CG) {
+            s_p[w][cg] = p;
+            if (want_o) s_r[w][cg] = r;
+        }
+        __syncthreads();
+
+        // one thread per (column group, component): u = beta (v - p), o = r + (k . q) u
+        if (tid < 4 * CG) {
+            const int c = tid >> 2, e = tid & 3;
+            float P = 0.f, R = 0.f, KQ = 0.f;
+#pragma unroll
+            for (int ww = 0; ww < NWV; ++ww) {
+                P += s_p[ww][c][e];
+                if (want_o) {
+                    R += s_r[ww][c][e];
+                    KQ += s_kq[ww];
+                }
+            }
+            const int col = 4 * c + e;
+            const float u = beta[th] * (to_f32(v[th * DV + col]) - P);
+            s_u[c][e] = u;
+            if (want_o) o[th * DV + col] = from_f32<ET>(R + KQ * u);
+        }
+        __syncthreads();
+
+        if (act) {
+            const f32x4 u = s_u[cg];
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) sv[i] += s_k[buf][rg + i * RG] * u;
         }
     }
-    // reduce over the row groups that share a wave (lanes differing in bits >= log2 CG)
+    if (write_state && act) {
 #pragma unroll
-    for (int m = CG; m < WAVE; m <<= 1) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            p[j] += __shfl_xor(p[j], m);
-            r[j] += __shfl_xor(r[j], m);
-        }
+        for (int i = 0; i < RPT; ++i) __builtin_nontemporal_store(sv[i], &S[(rg + i * RG) * CG + cg]);
     }
-    if ((tid & (WAVE - 1)) < CG) {
-        s_p[w][cg] = p;
-        s_r[w][cg] = r;
-    }
-    __syncthreads();
+}
 
-    // one thread per (column group, component): u = beta (v - p), o = r + (k . q) u
-    if (tid < 4 * CG) {
-        const int c = tid >> 2, j = tid & 3;
-        float P = 0.f, R = 0.f, KQ = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < NWV; ++ww) {
-            P += s_p[ww][c][j];
-            R += s_r[ww][c][j];
-            KQ += s_kq[ww];
-        }
-        const int col = 4 * c + j;
-        const float u = beta[unit] * (to_f32(v[unit * DV + col]) - P);
-        s_u[c][j] = u;
-        o[unit * DV + col] = from_f32<ET>(R + KQ * u);
-    }
-    __syncthreads();
-
-    if (act) {
-        const f32x4 u = s_u[cg];
-#pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-            const int row = rg + i * RG;
-            __builtin_nontemporal_store(sv[i] + s_k[row] * u, &S[row * CG + cg]);
-        }
-    }
+template <typename ET, int DK, int DV, int MODE>
+static hipError_t launch_decode_m(const DecodeArgs& a, hipStream_t st) {
+    const unsigned nblk = (unsigned)(a.N * a.H);
+    hipLaunchKernelGGL((decode_kernel<ET, DK, DV, MODE>), dim3(nblk), dim3(DecodeMap<DK, DV>::NTB), 0, st,
+                       a.state, (const ET*)a.q, (const ET*)a.k, (const ET*)a.v, a.log_alpha, a.beta,
+                       (ET*)a.o, a.n_accept, (int)a.H, (int)a.n_tok, (int)a.gate);
+    return hipGetLastError();
 }
 
 template <typename ET, int DK, int DV>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
-    const unsigned nblk = (unsigned)(a.N * a.H);
-    hipLaunchKernelGGL((decode_kernel<ET, DK, DV>), dim3(nblk), dim3(DecodeMap<DK, DV>::NTB), 0, st,
-                       a.state, (const ET*)a.q, (const ET*)a.k, (const ET*)a.v, a.log_alpha,
-                       a.beta, (ET*)a.o);
-    return hipGetLastError();
+    switch (a.mode) {
+        case DECODE_STEP: return launch_decode_m<ET, DK, DV, DECODE_STEP>(a, st);
+        case DECODE_VERIFY: return launch_decode_m<ET, DK, DV, DECODE_VERIFY>(a, st);
+        case DECODE_COMMIT: return launch_decode_m<ET, DK, DV, DECODE_COMMIT>(a, st);
+    }
+    return hipErrorInvalidValue;
 }
 
 template <typename ET, int DK>

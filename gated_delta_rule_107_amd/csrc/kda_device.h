@@ -28,6 +28,19 @@ __device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp
 // 2^x (hardware v_exp_f32).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Log-decay from a raw gate logit x through an activation that stops at the floor:
+// -5 sigmoid(x) = -5 / (1 + e^-x), in (-5, 0).  The floor constant is what made the
+// gate's activation need a lower bound (orkas.ai "Kimi K3 architecture", section "The
+// floor that removed a GPU code path"); the sigmoid form is this library's reading.
+// Large logits decay fastest; e^-x overflowing to inf gives 0 (no decay).
+__device__ __forceinline__ float gate_from_logit(float x) {
+    return clamp_log_alpha(LOG_ALPHA_FLOOR * __builtin_amdgcn_rcpf(1.0f + fast_exp(-x)));
+}
+// Gate input -> floored log-decay; gate 0: the input is the log-decay, 1: a raw logit.
+__device__ __forceinline__ float log_decay(float x, int gate) {
+    return gate ? gate_from_logit(x) : clamp_log_alpha(x);
+}
+
 // Copies 16 bytes per lane from global memory straight into LDS: lane i writes
 // lds + 16 i (lds wave-uniform); completion is tracked by the vector-memory counter.
 // The builtin exists for the device target only, and a host-pass reference to it

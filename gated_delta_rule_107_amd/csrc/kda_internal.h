@@ -8,13 +8,21 @@
 
 namespace kda {
 
+// Decode modes: one step (state updated in place); verify n_tok draft tokens (outputs only,
+// the state read but not written); commit the first n_accept[n] of n_tok tokens (state only).
+enum { DECODE_STEP = 0, DECODE_VERIFY = 1, DECODE_COMMIT = 2 };
+
 struct DecodeArgs {
     float* state;
     const void *q, *k, *v;
-    const float *log_alpha, *beta;
-    void* o;
+    const float *log_alpha, *beta;   // log_alpha: log-decays or raw logits (gate)
+    void* o;                         // null for commit
+    const int32_t* n_accept;         // [N] (commit), else null
     int64_t N;
+    int32_t n_tok;                   // tokens per sequence (1 for a step)
     int32_t H, dk, dv;
+    int32_t mode;
+    int32_t gate;                    // 0: log_alpha is the log-decay; 1: raw logit, -5 sigmoid
     bool bf16;
 };
 
@@ -43,6 +51,7 @@ struct ChunkArgs {
     const int32_t* cu_seqlens;  // [B + 1] packed sequence offsets into one batch row, or null
     float* ckpt;            // [B, T / ckpt_stride, H, dk, dv] state checkpoints (mode 0) or null
     int64_t ckpt_stride;    // tokens between checkpoints, a multiple of chunk
+    int32_t gate;           // 0: log_alpha holds log-decays; 1: raw logits, log-decay -5 sigmoid
     int32_t mode;
     bool bf16;
 };

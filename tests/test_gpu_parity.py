@@ -392,3 +392,96 @@ def test_packed_sequences(g, dtype, lens, H, dk, dv, chunk):
         o_ref, S_ref = oracle.kda_chunked(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["log_alpha"]),
                                           sl(x["beta"]), S0[i:i + 1], chunk=chunk)
         check(o[:, a:b], S[i:i + 1], o_ref, S_ref, TOL[dtype], f"sequence {i} ({b - a} tokens)")
+
+
+# ------------------------------------------------------------------ gate activation with a floor
+
+@pytest.mark.parametrize("dtype,B,T,H,dk,dv,chunk,nseg", [
+    ("f32", 1, 64, 2, 16, 16, 16, 1),
+    ("bf16", 2, 333, 2, 64, 64, 32, 1),
+    ("bf16", 1, 500, 2, 128, 128, 64, 3),
+])
+def test_prefill_gate_logits(g, dtype, B, T, H, dk, dv, chunk, nseg):
+    """log_alpha holding raw logits x: the kernels form -5 sigmoid(x) themselves."""
+    import torch
+    _say(f"case: gate logits {dtype} B{B} T{T} H{H} {dk}/{dv} C{chunk} P{nseg}")
+    x = ks.make_prefill(small_recipe(dtype, B, T, H, dk, dv, chunk, loga="logit15", s0_std=0.05))
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q, k, v = (dev_tensor(x[n], dt) for n in ("q", "k", "v"))
+    o, S = g.chunk_fwd(q, k, v, dev_tensor(x["log_alpha"], torch.float32), dev_tensor(x["beta"], torch.float32),
+                       dev_tensor(x["S0"], torch.float32), chunk=chunk, plan=g.Plan(nseg, 0), gate=g.GATE_LOGITS)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.kda_loop(x["q"], x["k"], x["v"], oracle.gate_from_logits(x["log_alpha"]), x["beta"],
+                                   x["S0"])
+    check(to_np(o), to_np(S), o_ref, S_ref, TOL[dtype], "prefill from gate logits")
+
+
+# ------------------------------------------------------------------ speculative verify / commit
+
+def _drafts(dtype, N, n, H, dk, dv, loga="unif"):
+    """Draft-token inputs [N, n, H, .] (the prefill layout) and a start state [N, H, dk, dv]."""
+    r = ks.Recipe("drafts", B=N, T=1, H=H, dk=dk, dv=dv, chunk=16, dtype=dtype, loga=loga, s0_std=0.05,
+                  tag=ks.TAG_BASE + 300, steps=n)
+    d = ks.make_decode(r)
+    tr = lambda a: np.ascontiguousarray(np.swapaxes(a, 0, 1))  # noqa: E731
+    return d["state"], {name: tr(d[name]) for name in ("q", "k", "v", "log_alpha", "beta")}
+
+
+@pytest.mark.parametrize("dtype,dk,dv,gate", [("f32", 16, 16, 0), ("f32", 32, 128, 1), ("bf16", 128, 128, 0),
+                                              ("bf16", 64, 32, 1), ("bf16", 128, 16, 0)])
+def test_decode_verify_then_commit(g, dtype, dk, dv, gate):
+    import torch
+    N, n, H = 5, 4, 3
+    _say(f"case: verify/commit {dtype} {dk}/{dv} gate {gate}")
+    state0, x = _drafts(dtype, N, n, H, dk, dv, loga="logit15" if gate else "unif")
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    xd = {nm: dev_tensor(x[nm], torch.float32 if nm in ("log_alpha", "beta") else dt) for nm in x}
+    la_ref = oracle.gate_from_logits(x["log_alpha"]) if gate else x["log_alpha"]
+    state = dev_tensor(state0, torch.float32)
+    keep = state.clone()
+    o = g.decode_verify(state, xd["q"], xd["k"], xd["v"], xd["log_alpha"], xd["beta"], gate=gate)
+    torch.cuda.synchronize()
+    assert torch.equal(state, keep), "verify wrote the state"
+    o_ref = oracle.kda_decode_verify(state0, x["q"], x["k"], x["v"], la_ref, x["beta"])
+    tol = TOL[dtype] if dtype == "bf16" else 1e-5
+    eo = oracle.rel_fro(to_np(o), o_ref)
+    _say(f"verify: rel_fro o={eo:.3e} (tol {tol:g})")
+    assert np.isfinite(to_np(o)).all() and eo <= tol
+    n_acc = np.array([0, 1, 4, 2, 9], np.int32)                     # 9 is clamped to n = 4
+    g.decode_commit(state, xd["q"], xd["k"], xd["v"], xd["log_alpha"], xd["beta"],
+                    torch.from_numpy(n_acc).cuda(), gate=gate)
+    torch.cuda.synchronize()
+    S = to_np(state)
+    S_ref = oracle.kda_decode_commit(state0, x["q"], x["k"], x["v"], la_ref, x["beta"], n_acc)
+    assert np.array_equal(S[0], state0[0]), "n_accept = 0 changed the state"
+    es = oracle.rel_fro(S, S_ref)
+    _say(f"commit: rel_fro S={es:.3e} (tol {tol:g})")
+    assert np.isfinite(S).all() and es <= tol
+
+
+def test_decode_verify_commit_full_size(g):
+    """256 sequences x 32 heads, 128/128, 4 drafts: verify equals 4 decode steps and commit
+    of every draft equals their final state (same kernel arithmetic, so to float32 rounding);
+    8 sampled sequences against the oracle."""
+    import torch
+    r = ks.WORKLOADS[4]
+    N, n, H = r.B, 4, r.H
+    _say("case: verify/commit full size")
+    state0, x = _drafts("bf16", N, n, H, r.dk, r.dv)
+    xd = {nm: dev_tensor(x[nm], torch.float32 if nm in ("log_alpha", "beta") else torch.bfloat16) for nm in x}
+    state = dev_tensor(state0, torch.float32)
+    o = g.decode_verify(state, xd["q"], xd["k"], xd["v"], xd["log_alpha"], xd["beta"])
+    st2 = state.clone()
+    outs = [g.decode_step(st2, xd["q"][:, j].contiguous(), xd["k"][:, j].contiguous(), xd["v"][:, j].contiguous(),
+                          xd["log_alpha"][:, j].contiguous(), xd["beta"][:, j].contiguous()) for j in range(n)]
+    g.decode_commit(state, xd["q"], xd["k"], xd["v"], xd["log_alpha"], xd["beta"],
+                    torch.full((N,), n, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    o_steps = torch.stack(outs, 1)
+    assert oracle.rel_fro(to_np(o), to_np(o_steps)) < 1e-6
+    assert oracle.rel_fro(to_np(state), to_np(st2)) < 1e-6
+    sel = np.random.default_rng(5).choice(N, 8, replace=False)
+    o_ref = oracle.kda_decode_verify(state0[sel], *(x[nm][sel] for nm in ("q", "k", "v", "log_alpha", "beta")))
+    S_ref = oracle.kda_decode_commit(state0[sel], *(x[nm][sel] for nm in ("q", "k", "v", "log_alpha", "beta")),
+                                     np.full(8, n))
+    check(to_np(o)[sel], to_np(state)[sel], o_ref, S_ref, TOL["bf16"], "verify/commit (8 sampled sequences)")
