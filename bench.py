@@ -11,9 +11,11 @@ and state.  Inputs are seeded synthetic tensors already resident in HBM when
 the timed region starts.
 
 The prefill block also reports the same step with state checkpoints every 512
-tokens (the prefix-reuse output of kda_plan_t.state_ckpt).  The same JSON line
+tokens (the prefix-reuse output of kda_plan_t.state_ckpt) and the same step
+reading raw gate logits (kda_gate_t KDA_GATE_LOGITS).  The same JSON line
 also carries the decode figure (256 sequences x 32 heads,
-128x128 float32 state, 64 consecutive in-place steps), the roofline of the
+128x128 float32 state, 64 consecutive in-place steps) with the speculative
+verify of 4 drafts per sequence and the commit of all 4, the roofline of the
 dominant prefill kernel (algorithmic bytes per launch / its mean duration,
 taken from HIP events the library records around each launch on the stream
 the kernels run on), and the float64 CPU oracle timed on the host cores.
@@ -84,6 +86,18 @@ def decode_bytes_per_step(N, H, dk, dv, es):
     return N * H * (2 * dk * dv * 4 + 2 * dk * es + dv * es + 4 * dk + 4 + dv * es)
 
 
+def verify_bytes(N, n, H, dk, dv, es):
+    """Speculative verify of n drafts: state read once (float32), per draft q, k, v, o in the
+    storage dtype and log_alpha, beta float32."""
+    return N * H * (dk * dv * 4 + n * (2 * dk * es + dv * es + 4 * dk + 4 + dv * es))
+
+
+def commit_bytes(N, n, H, dk, dv, es):
+    """Commit of all n drafts: state read + write, per draft k, v (storage dtype), log_alpha,
+    beta; n_accept."""
+    return N * H * (2 * dk * dv * 4 + n * (dk * es + dv * es + 4 * dk + 4)) + 4 * N
+
+
 # ----------------------------------------------------------------------------- CPU baseline (oracle)
 
 _CPU = {}
@@ -142,6 +156,7 @@ def cpu_workers():
 
 HOST_GEN_LIMIT = 1 << 23              # token-heads above which inputs are drawn on the device
 CKPT_STRIDE = 512                     # state checkpoint stride of the side figure (the hash block)
+SPEC_DRAFTS = 4                       # draft tokens per sequence of the speculative-decoding side figure
 
 
 def cpu_baseline_prefill(r, x):
@@ -266,7 +281,55 @@ def bench_prefill(g, torch, r, x, steps, warmup):
         ckpt = {"stride": CKPT_STRIDE, "checkpoints": nck, "ms_per_step": round(ms_ck, 5),
                 "overhead": round(ms_ck / ms - 1.0, 4), "extra_bytes": int(sck.numel() * 4)}
         log("prefill with state checkpoints:", json.dumps(ckpt))
-    return ms, plan, per_launch, ckpt
+    # the same step reading log_alpha as raw gate logits (-5 sigmoid formed in gate prep)
+    for _ in range(warmup):
+        g.chunk_fwd(q, k, v, la, beta, S0, chunk=r.chunk, plan=plan, o=o, S_T=S_T, workspace=ws, gate=g.GATE_LOGITS)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(steps):
+        g.chunk_fwd(q, k, v, la, beta, S0, chunk=r.chunk, plan=plan, o=o, S_T=S_T, workspace=ws, gate=g.GATE_LOGITS)
+    t1.record()
+    torch.cuda.synchronize()
+    ms_gate = t0.elapsed_time(t1) / steps
+    gate = {"ms_per_step": round(ms_gate, 5), "overhead": round(ms_gate / ms - 1.0, 4)}
+    log("prefill from gate logits:", json.dumps(gate))
+    return ms, plan, per_launch, ckpt, gate
+
+
+def bench_speculative(g, torch, rd, d, n, reps):
+    """Verify of n drafts per sequence and commit of all of them, on the decode workload's
+    state and its first n steps' inputs laid out [N, n, H, .]."""
+    dev = torch.device("cuda:0")
+    dt = torch.bfloat16
+    T_ = lambda a, t: torch.from_numpy(np.ascontiguousarray(np.swapaxes(a[:n], 0, 1))).to(dev, t)  # noqa: E731
+    q, k, v = T_(d["q"], dt), T_(d["k"], dt), T_(d["v"], dt)
+    la, beta = T_(d["log_alpha"], torch.float32), T_(d["beta"], torch.float32)
+    pristine = torch.from_numpy(d["state"]).to(dev)
+    state = pristine.clone()
+    o = torch.empty((rd.B, n, rd.H, rd.dv), dtype=dt, device=dev)
+    acc = torch.full((rd.B,), n, dtype=torch.int32, device=dev)
+    out = {}
+    for name in ("verify", "commit"):
+        times = []
+        for i in range(reps + 1):
+            state.copy_(pristine)           # restore (not timed)
+            torch.cuda.synchronize()
+            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0.record()
+            if name == "verify":
+                g.decode_verify(state, q, k, v, la, beta, o=o)
+            else:
+                g.decode_commit(state, q, k, v, la, beta, acc)
+            t1.record()
+            torch.cuda.synchronize()
+            if i:                           # the first call is a warm-up
+                times.append(t0.elapsed_time(t1))
+        ms = float(np.median(times))
+        nb = (verify_bytes if name == "verify" else commit_bytes)(rd.B, n, rd.H, rd.dk, rd.dv, 2)
+        gbps = nb / (ms * 1e-3) / 1e9
+        out[name] = {"ms": round(ms, 5), "bytes": nb, "GBps": round(gbps, 1), "frac": round(gbps / PEAK_HBM_GBPS, 4)}
+    out["n_draft"] = n
+    return out
 
 
 def bench_decode(g, torch, rd, d, reps):
@@ -409,7 +472,7 @@ def main():
     props = torch.cuda.get_device_properties(0)
     log(f"device: {props.name} {getattr(props, 'gcnArchName', '')} CUs={props.multi_processor_count}")
 
-    ms, plan, per_launch, ckpt = bench_prefill(g, torch, r, x, args.steps, args.warmup)
+    ms, plan, per_launch, ckpt, gate = bench_prefill(g, torch, r, x, args.steps, args.warmup)
     es = 2 if r.dtype == "bf16" else 4
     token_heads = r.B * r.T * r.H
     flops = token_heads * prefill_flops_per_token_head(r.dk, r.dv, r.chunk)
@@ -432,7 +495,8 @@ def main():
                "roofline": {"bound": "hbm", "kernel": "decode_kernel", "achieved": round(dgbps, 1),
                             "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(dgbps / PEAK_HBM_GBPS, 4),
                             "traffic": measured_traffic(rd.name, "decode_kernel"), "launch_bytes": dbytes},
-               "cpu_baseline": cpu_dec}
+               "cpu_baseline": cpu_dec,
+               "speculative": bench_speculative(g, torch, rd, d, SPEC_DRAFTS, 2 * args.decode_reps)}
         log("decode:", json.dumps(dec))
     copy_gbps = copy_bandwidth(torch)
 
@@ -457,7 +521,7 @@ def main():
                     "hbm_frac_alg": round(nbytes / sec / (PEAK_HBM_GBPS * 1e9), 4),
                     "roofline_frac": round(max(flops / (peak_mf * 1e12), nbytes / (PEAK_HBM_GBPS * 1e9)) / sec, 4),
                     "alg_gflop": round(flops / 1e9, 3), "alg_mb": round(nbytes / 1e6, 2),
-                    "launches": per_launch, "with_state_checkpoints": ckpt},
+                    "launches": per_launch, "with_state_checkpoints": ckpt, "from_gate_logits": gate},
         "decode": dec,
         "hbm_copy_GBps": round(copy_gbps, 1),
     }

@@ -61,9 +61,9 @@ __global__ __launch_bounds__((DecodeMap<DK, DV>::NTB)) __attribute__((amdgpu_wav
     const int cg = tid % CG, rg = tid / CG;
     const int w = tid / WAVE;
 
-    // per-token vectors are double-buffered by token parity: token j+1 writes its copy while
-    // threads may still read token j's in the state update
-    __shared__ float s_a[2][DK], s_k[2][DK], s_q[2][DK];
+    // per-token vectors (decay factors, k, q), double-buffered by token parity: token j+1
+    // writes its copy while threads may still read token j's in the state update
+    __shared__ float s_tok[2][3][DK];
     __shared__ f32x4 s_p[NWV][CG], s_r[NWV][CG];
     __shared__ float s_kq[NWV];
     __shared__ f32x4 s_u[CG];
@@ -77,17 +77,47 @@ __global__ __launch_bounds__((DecodeMap<DK, DV>::NTB)) __attribute__((amdgpu_wav
     int cnt = MODE == DECODE_STEP ? 1 : n_tok;
     if (MODE == DECODE_COMMIT) cnt = min(max(n_accept[n], 0), n_tok);
 
+    // Per-token inputs are loaded one token ahead, in their storage types (converted where
+    // they are used), so their memory latency overlaps the previous token's reductions:
+    // gate, k, q for lanes tid < DK; v (column tid) and beta for the reducer lanes tid < DV.
+    // Addresses are a uniform per-token base plus a 32-bit lane offset; beta goes through a
+    // lane-varying (zero) offset so that it is a vector load like the rest, not a scalar
+    // load that would be waited for on the spot.
+    const unsigned ut = (unsigned)tid;
+    unsigned zero = 0;
+    asm volatile("" : "+v"(zero));
+    float la_n = 0.f, b_n = 0.f;
+    ET k_n{}, q_n{}, v_n{};
+    auto load_tok = [&](int j) {
+        const size_t th = (n * (unsigned)n_tok + j) * (unsigned)H + h;   // token-head index
+        if (tid < DK) {
+            la_n = (log_alpha + th * DK)[ut];
+            k_n = (k + th * DK)[ut];
+            if (want_o) q_n = (q + th * DK)[ut];
+        }
+        if (tid < DV) {
+            v_n = (v + th * DV)[ut];
+            b_n = (beta + th)[zero];
+        }
+    };
+    if (cnt > 0) load_tok(0);
+
     for (int j = 0; j < cnt; ++j) {
         const int buf = j & 1;
-        const size_t th = (n * (unsigned)n_tok + j) * (unsigned)H + h;   // token-head index
+        const float la_c = la_n, b_c = b_n;
+        const ET k_c = k_n, q_c = q_n, v_c = v_n;
+        if (j + 1 < cnt) load_tok(j + 1);
+        float* s_a = s_tok[buf][0];
+        float* s_k = s_tok[buf][1];
+        float* s_q = s_tok[buf][2];
         float kq = 0.f;
         if (tid < DK) {
-            const float kk = to_f32(k[th * DK + tid]);
-            s_a[buf][tid] = fast_exp(log_decay(log_alpha[th * DK + tid], gate));
-            s_k[buf][tid] = kk;
+            const float kk = to_f32(k_c);
+            s_a[tid] = fast_exp(log_decay(la_c, gate));
+            s_k[tid] = kk;
             if (want_o) {
-                const float qq = to_f32(q[th * DK + tid]);
-                s_q[buf][tid] = qq;
+                const float qq = to_f32(q_c);
+                s_q[tid] = qq;
                 kq = kk * qq;
             }
         }
@@ -104,9 +134,9 @@ __global__ __launch_bounds__((DecodeMap<DK, DV>::NTB)) __attribute__((amdgpu_wav
 #pragma unroll
             for (int i = 0; i < RPT; ++i) {
                 const int row = rg + i * RG;
-                sv[i] *= s_a[buf][row];
-                p += sv[i] * s_k[buf][row];
-                if (want_o) r += sv[i] * s_q[buf][row];
+                sv[i] *= s_a[row];
+                p += sv[i] * s_k[row];
+                if (want_o) r += sv[i] * s_q[row];
             }
         }
         // reduce over the row groups that share a wave (lanes differing in bits >= log2 CG)
@@ -124,29 +154,31 @@ __global__ __launch_bounds__((DecodeMap<DK, DV>::NTB)) __attribute__((amdgpu_wav
         }
         __syncthreads();
 
-        // one thread per (column group, component): u = beta (v - p), o = r + (k . q) u
-        if (tid < 4 * CG) {
-            const int c = tid >> 2, e = tid & 3;
+        // one thread per (column group, component) = column tid: u = beta (v - p), o = r + (k . q) u
+        if (tid < DV) {
+            const int rc = tid >> 2, re = tid & 3;
             float P = 0.f, R = 0.f, KQ = 0.f;
 #pragma unroll
             for (int ww = 0; ww < NWV; ++ww) {
-                P += s_p[ww][c][e];
+                P += s_p[ww][rc][re];
                 if (want_o) {
-                    R += s_r[ww][c][e];
+                    R += s_r[ww][rc][re];
                     KQ += s_kq[ww];
                 }
             }
-            const int col = 4 * c + e;
-            const float u = beta[th] * (to_f32(v[th * DV + col]) - P);
-            s_u[c][e] = u;
-            if (want_o) o[th * DV + col] = from_f32<ET>(R + KQ * u);
+            const float u = b_c * (to_f32(v_c) - P);
+            s_u[rc][re] = u;
+            if (want_o) {
+                const size_t th = (n * (unsigned)n_tok + j) * (unsigned)H + h;
+                (o + th * DV)[ut] = from_f32<ET>(R + KQ * u);
+            }
         }
         __syncthreads();
 
         if (act) {
             const f32x4 u = s_u[cg];
 #pragma unroll
-            for (int i = 0; i < RPT; ++i) sv[i] += s_k[buf][rg + i * RG] * u;
+            for (int i = 0; i < RPT; ++i) sv[i] += s_k[rg + i * RG] * u;
         }
     }
     if (write_state && act) {
