@@ -234,8 +234,11 @@ __host__ __device__ constexpr int pair_fo_index(int p, int pp) {   // p - pp >= 
 
 // ---------------------------------------------------------------- the kernel
 // MODE 0: outputs and final states; MODE 1: segment summaries (see ChunkArgs).
-template <typename OpT, int DK, int C, int MODE>
+// CK (MODE 0 only): also write state checkpoints.  A separate instantiation: the
+// checkpoint code, even never taken, costs the loop about 4 % on a full-GPU workload.
+template <typename OpT, int DK, int C, int MODE, bool CK>
 __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
+    static_assert(!CK || MODE == 0, "checkpoints are written by the one-pass / pass-2 kernel");
     using MF = MM<OpT>;
     using B16 = typename MF::B16;
     using L4 = Ld4<OpT>;
@@ -466,7 +469,7 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
     // one (-1: none), and where it goes (this head's columns of checkpoint t / stride - 1)
     int ck_rel = -1;
     float* ck_ptr = nullptr;
-    if (MODE == 0 && a.ckpt) {
+    if (CK && a.ckpt) {
         const int64_t first = t_begin / a.ckpt_stride;            // index of the next checkpoint
         ck_rel = (int)((first + 1) * a.ckpt_stride - t_begin);
         ck_ptr = a.ckpt + ((b * (T / a.ckpt_stride) + first) * H + h) * (int64_t)DK * dv + colw;
@@ -491,6 +494,16 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
         const int gc0 = 16 * wave + 4 * gx;
         const bool gact = gc0 < DK && gp < NT;
         __syncthreads();   // the previous iteration's readers of the staging tiles are done
+        // Branches stay at phase boundaries: the chain and the gate prep below form one block
+        // in which the compiler interleaves MFMA and VALU work.
+        if constexpr (nxt) {
+            if (a.gate) {                            // raw logits: log-decay -5 sigmoid (uniform)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) pla[j][e] = gate_from_logit(pla[j][e]);
+            }
+        }
 
         // ================= (1a) chain of chunk n: R_p = beta (V - X); U_p = N_pp (R_p - sum_{q<p} Ab_pq U_q)
         B16 ub[NT];
@@ -535,12 +548,6 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
             // zeroed here (idle channel lanes of DK < 128 only feed their own 16-lane rows,
             // whose stores are skipped).  k and q stay in their packed prefetch registers until
             // they are used.
-            if (a.gate) {                                  // raw logits: -5 sigmoid (uniform branch)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) pla[j][e] = gate_from_logit(pla[j][e]);
-            }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const bool ok = full || 4 * tq + j < Tn;
@@ -680,8 +687,13 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
                 }
             }
         }
+        // chunk n+2's gates, keys and queries load while chunk n+1 is processed
+        if (nxt && n + 2 < nchunks) prefetch_gates(t1 + C, tid);
+        __syncthreads();
+
         // state checkpoint after tokens [0, t0 + C) when that is a multiple of the stride
-        if constexpr (cur && MODE == 0) {
+        // (Sacc holds the state after chunk n)
+        if constexpr (cur && CK) {
             if ((int)(n + 1) * C == ck_rel) {        // (never true without checkpoints)
                 if (chain && t_begin + ck_rel <= T) {
 #pragma unroll
@@ -693,9 +705,6 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
                 ck_ptr += (int64_t)H * DK * dv;
             }
         }
-        // chunk n+2's gates, keys and queries load while chunk n+1 is processed
-        if (nxt && n + 2 < nchunks) prefetch_gates(t1 + C, tid);
-        __syncthreads();
 
         // ================= (2) Khat^T(n+1) to LDS; X = Kt S and QS = Qt S; the A / M tiles
         if constexpr (nxt) {
@@ -821,17 +830,22 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
                 float x[16];
 #pragma unroll
                 for (int t = 0; t < 16; ++t) x[t] = (t == j) ? 1.f : 0.f;
+                // each step needs rows s+1.. of column s; the columns are read two steps ahead
+                // into a ring of three register buffers, so no step waits for its LDS read
+                f32x4 cb[3][4];
+                auto read_col = [&](int s, f32x4* c) {
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4)
+                        if (4 * q4 + 3 > s) c[q4] = *reinterpret_cast<const f32x4*>(Ab + 16 * s + 4 * q4);
+                };
+                read_col(0, cb[0]);
+                read_col(1, cb[1]);
 #pragma unroll
                 for (int s = 0; s < 15; ++s) {
-                    float col[16];
+                    if (s + 2 < 15) read_col(s + 2, cb[(s + 2) % 3]);
+                    const f32x4* c = cb[s % 3];
 #pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        const f32x4 c4 = *reinterpret_cast<const f32x4*>(Ab + 16 * s + 4 * q4);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) col[4 * q4 + e] = c4[e];
-                    }
-#pragma unroll
-                    for (int t = s + 1; t < 16; ++t) x[t] -= col[t] * x[s];
+                    for (int t = s + 1; t < 16; ++t) x[t] -= c[t >> 2][t & 3] * x[s];
                 }
 #pragma unroll
                 for (int t = 0; t < 16; ++t) s_an[(16 * p + t) * LC + 16 * p + j] = from_f32<OpT>(x[t]);
@@ -900,10 +914,10 @@ size_t chunk_lds_bytes(bool bf16_, int dk, int chunk, int /*dv_block*/) {
     return (size_t)lds_layout(bf16_ ? 2 : 4, dk, chunk).total;
 }
 
-template <typename OpT, int DK, int C, int MODE>
+template <typename OpT, int DK, int C, int MODE, bool CK>
 static hipError_t launch_chunk_m(const ChunkArgs& a, hipStream_t st) {
     constexpr size_t lds = (size_t)lds_layout(sizeof(OpT), DK, C).total;
-    auto kern = chunk_kernel<OpT, DK, C, MODE>;
+    auto kern = chunk_kernel<OpT, DK, C, MODE, CK>;
     static bool attr_set = false;   // per instantiation; the attribute is device-independent
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 163840);
@@ -920,7 +934,8 @@ static hipError_t launch_chunk_m(const ChunkArgs& a, hipStream_t st) {
 
 template <typename OpT, int DK, int C>
 static hipError_t launch_chunk_t(const ChunkArgs& a, hipStream_t st) {
-    return a.mode == 0 ? launch_chunk_m<OpT, DK, C, 0>(a, st) : launch_chunk_m<OpT, DK, C, 1>(a, st);
+    if (a.mode == 1) return launch_chunk_m<OpT, DK, C, 1, false>(a, st);
+    return a.ckpt ? launch_chunk_m<OpT, DK, C, 0, true>(a, st) : launch_chunk_m<OpT, DK, C, 0, false>(a, st);
 }
 
 template <typename OpT, int DK>
