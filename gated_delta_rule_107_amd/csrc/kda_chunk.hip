@@ -362,9 +362,12 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
     // the next prefetch with that load unconsumed.
     // Row offsets use 24-bit multiplies (the ABI bounds H * max(dk, dv) below 2^24).  When the
     // whole chunk is in range, token j of each quad is one stride further: an add, no clamp.
+    // The lane map covers 64 tokens; with C < 64 the lanes of sub-tiles C/16.. are idle and
+    // their token quad is clamped to the chunk's last one (their values are never used, and
+    // on a sequence's last chunk they would otherwise read past the end of the tensors).
     auto prefetch_gates = [&](int64_t t0, int tid) {
         const int lane = tid & 63;
-        const int tq = 4 * (lane >> 4) + ((lane >> 2) & 3);
+        const int tq = min(4 * (lane >> 4) + ((lane >> 2) & 3), C / 4 - 1);
         const int gc0 = min(16 * wave + 4 * (lane & 3), DK - 4);
         const int tlim = (int)(t_end - 1 - t0 < C - 1 ? t_end - 1 - t0 : C - 1);
         const int64_t base = ((b * T + t0) * H + h) * (int64_t)DK;       // uniform

@@ -114,6 +114,24 @@ def test_small_shapes_one_pass(g, shape):
         check(o, S, o_ref, S_ref, TOL[dtype], f"{shape} dv_block=16")
 
 
+@pytest.mark.parametrize("shape,nseg", [(("bf16", 1, 256, 2, 128, 128, 32), 1), (("bf16", 1, 256, 2, 128, 128, 32), 4),
+                                        (("f32", 1, 128, 2, 32, 32, 16), 1), (("f32", 1, 128, 2, 32, 32, 16), 3),
+                                        (("bf16", 1, 96, 1, 64, 64, 16), 2)],
+                         ids=lambda s: "-".join(map(str, s)) if isinstance(s, tuple) else str(s))
+def test_last_chunk_full_small_chunks(g, shape, nseg):
+    """Sequences that end exactly on a full chunk of 16 or 32 tokens, in a single batch row:
+    the gate prefetch of the last chunk must stay inside the tensors (regression: its idle
+    lanes, which exist when the chunk is shorter than 64 tokens, once read up to 48 tokens
+    past the end)."""
+    dtype, B, T, H, dk, dv, chunk = shape
+    r = small_recipe(dtype, B, T, H, dk, dv, chunk, s0_std=0.1)
+    _say("case: last chunk full", shape, nseg)
+    x = ks.make_prefill(r)
+    o_ref, S_ref = oracle.kda_loop(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["S0"])
+    o, S = run_prefill(g, x, dtype, chunk, plan=g.Plan(nseg, min(dv, dk)))
+    check(o, S, o_ref, S_ref, TOL[dtype], f"{shape} {nseg} segments, last chunk full")
+
+
 @pytest.mark.parametrize("shape", [("f32", 1, 200, 2, 32, 32, 16), ("bf16", 1, 500, 2, 128, 128, 64),
                                    ("bf16", 2, 333, 1, 64, 64, 32), ("f32", 1, 64, 1, 16, 16, 16)],
                          ids=lambda s: "-".join(map(str, s)))
