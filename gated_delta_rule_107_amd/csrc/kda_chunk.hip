@@ -147,6 +147,20 @@ template <> struct MM<float> {
 template <int N> __device__ __forceinline__ float row_shr(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x110 | N, 0xF, 0xF, true));
 }
+// Value of the neighbouring lane (lanes 2i and 2i+1 swap).
+__device__ __forceinline__ float swap_adjacent(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+}
+// Two adjacent output elements stored as one 4-byte (bf16) or 8-byte (float32) write.
+template <typename OpT> struct Pair2;
+template <> struct Pair2<bf16> {
+    typedef bf16x2 V;
+    __device__ static V make(float a, float b) { return V{(bf16)a, (bf16)b}; }
+};
+template <> struct Pair2<float> {
+    typedef float __attribute__((__vector_size__(2 * sizeof(float)))) V;
+    __device__ static V make(float a, float b) { return V{a, b}; }
+};
 // ---------------------------------------------------------------- global addressing
 // base (wave-uniform, in scalar registers) + a 32-bit byte offset per lane: the form the
 // hardware's scalar-base addressing takes, with no 64-bit arithmetic per access
@@ -524,19 +538,25 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
         }
 
         // ================= (1c) O = QS + M U of chunk n, stored straight from the accumulators
-        // (its store instructions issue while the gate prep below keeps the vector units busy)
+        // (its store instructions issue while the gate prep below keeps the vector units busy).
+        // Adjacent lanes pair up their columns: the even lane writes rows 4g, 4g+1 and the
+        // odd lane rows 4g+2, 4g+3 of columns (jl & ~1, jl | 1), two elements per store.
         if constexpr (cur && want_o) {
-            OpT* o_w = go + ((b * T + t0) * H + h) * (int64_t)dv + colw;       // uniform: this wave's columns
+            using P2 = Pair2<OpT>;
+            typename P2::V* o_w = reinterpret_cast<typename P2::V*>(go + ((b * T + t0) * H + h) * (int64_t)dv + colw);
+            const bool odd = jl & 1;
+            const int cpair = jl & ~1;
 #pragma unroll
             for (int p = 0; p < NT; ++p) {
 #pragma unroll
                 for (int qq = 0; qq <= p; ++qq) QS[p] = MF::k16(s_mm, LC, 16 * p, 16 * qq, ub[qq], QS[p], lane);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = 16 * p + g4 + r;
-                    if (chain && row < Tc)
-                        *at_bytes(o_w, (__umul24(row, tok_v) + jl) * (unsigned)E) = from_f32<OpT>(QS[p][r]);
-                }
+                const float n0 = swap_adjacent(odd ? QS[p][0] : QS[p][2]);
+                const float n1 = swap_adjacent(odd ? QS[p][1] : QS[p][3]);
+                const int ra = 16 * p + g4 + (odd ? 2 : 0);
+                const typename P2::V w0 = odd ? P2::make(n0, QS[p][2]) : P2::make(QS[p][0], n0);
+                const typename P2::V w1 = odd ? P2::make(n1, QS[p][3]) : P2::make(QS[p][1], n1);
+                if (chain && ra < Tc) *at_bytes(o_w, (__umul24(ra, tok_v) + cpair) * (unsigned)E) = w0;
+                if (chain && ra + 1 < Tc) *at_bytes(o_w, (__umul24(ra + 1, tok_v) + cpair) * (unsigned)E) = w1;
             }
         }
 
