@@ -87,6 +87,20 @@ def gate_from_logits(x):
         return LOG_ALPHA_FLOOR / (1.0 + np.exp(-x))
 
 
+QK_NORM_EPS = 1e-6
+
+
+def l2_normalize(x, eps=QK_NORM_EPS):
+    """Optional per-token normalisation of q and k over the dk channels: x / sqrt(sum x^2 + eps).
+
+    The pages leave normalisation to the model (no formula is printed); this is the common
+    form, with a small epsilon so that a zero vector stays finite.  Applied, when asked for,
+    to q and k as stored, before every other step.
+    """
+    x = _f64(x)
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)
+
+
 def _bhtd(x):
     """[B,T,H,D] -> [B,H,T,D] view."""
     return np.swapaxes(x, 1, 2)

@@ -357,3 +357,27 @@ def test_decode_commit_matches_bruteforce_prefixes():
         sl = slice(i, i + 1)
         _, S_bf = oracle.kda_bruteforce(q[sl, :m], k[sl, :m], v[sl, :m], la[sl, :m], beta[sl, :m], S0[sl])
         assert rel_fro(S[i], S_bf[0]) < 1e-12
+
+
+# ---------------------------------------------------------------- optional q/k L2 normalisation
+
+def test_l2_normalize_against_library_and_closed_form():
+    from sklearn.preprocessing import normalize
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((7, 5, 33)) * rng.uniform(0.01, 30.0, (7, 5, 1))
+    flat = x.reshape(-1, 33)
+    assert np.abs(oracle.l2_normalize(flat, eps=0.0) - normalize(flat)).max() < 1e-15
+    y = oracle.l2_normalize(x)
+    s = np.sum(x * x, axis=-1)
+    assert np.abs(np.linalg.norm(y, axis=-1) - np.sqrt(s / (s + oracle.QK_NORM_EPS))).max() < 1e-14
+    assert np.array_equal(oracle.l2_normalize(np.zeros((2, 16))), np.zeros((2, 16)))   # finite at zero
+
+
+def test_normalised_keys_write_then_read_any_length():
+    """alpha = beta = 1 and q = k: with k normalised inside, o_t = v_t for keys of any length
+    (the erase / write algebra needs unit keys, which the normalisation supplies)."""
+    q, k, v, la, beta, S0 = rnd_inputs(32, T=10, unit_k=False)
+    k = k * np.random.default_rng(33).uniform(0.2, 9.0, k.shape[:-1] + (1,))
+    kn = oracle.l2_normalize(k, eps=0.0)
+    o, _ = oracle.kda_loop(kn, kn, v, np.zeros_like(la), np.ones_like(beta), S0)
+    assert np.abs(o - v).max() < 1e-12
