@@ -12,7 +12,8 @@ call raises ImportError if it has not been built
     decode_commit(state, q, k, v, log_alpha, beta, n_accept)   # replay the accepted drafts
 
 ``gate=GATE_LOGITS`` makes every call read log_alpha as raw gate logits x, with the
-log-decay -5 sigmoid(x) formed inside the kernels.
+log-decay -5 sigmoid(x) formed inside the kernels; ``qk_norm=True`` normalises q and k
+per token inside the kernels (x / sqrt(sum x^2 + 1e-6)).
 """
 from __future__ import annotations
 
@@ -31,6 +32,7 @@ ERRORS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE"
           5: "KDA_ERR_UNSUPPORTED", 6: "KDA_ERR_WORKSPACE", 7: "KDA_ERR_HIP", 8: "KDA_ERR_ALIAS"}
 DTYPE_F32, DTYPE_BF16 = 0, 1
 GATE_LOG_DECAY, GATE_LOGITS = 0, 1
+FLAG_GATE_LOGITS, FLAG_QK_L2NORM = 1, 2          # kda_input_flag_t
 
 
 class KdaError(RuntimeError):
@@ -41,11 +43,11 @@ class KdaError(RuntimeError):
 
 class Plan(ctypes.Structure):
     """kda_plan_t: segmentation, column blocking, optional launch-timing events, optional
-    state checkpoints, packed sequences and the gate mode."""
+    state checkpoints, packed sequences and the input flags."""
     _fields_ = [("n_segments", ctypes.c_int32), ("dv_block", ctypes.c_int32),
                 ("launch_events", ctypes.POINTER(ctypes.c_void_p)), ("n_launch_events", ctypes.c_int32),
                 ("state_ckpt", ctypes.c_void_p), ("ckpt_stride", ctypes.c_int64),
-                ("cu_seqlens", ctypes.c_void_p), ("n_seqs", ctypes.c_int32), ("gate", ctypes.c_int32)]
+                ("cu_seqlens", ctypes.c_void_p), ("n_seqs", ctypes.c_int32), ("flags", ctypes.c_uint32)]
 
     def __repr__(self):
         return f"Plan(n_segments={self.n_segments}, dv_block={self.dv_block})"
@@ -60,11 +62,12 @@ def _load():
     lib.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, i32,
                                   ctypes.POINTER(Plan), vp, sz, vp]
     lib.kda_decode_step.restype = i32
-    lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, vp]
+    u32 = ctypes.c_uint32
+    lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, u32, vp]
     lib.kda_decode_verify.restype = i32
-    lib.kda_decode_verify.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, vp]
+    lib.kda_decode_verify.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, u32, vp]
     lib.kda_decode_commit.restype = i32
-    lib.kda_decode_commit.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, vp]
+    lib.kda_decode_commit.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, u32, vp]
     lib.kda_chunk_fwd_default_plan.restype = i32
     lib.kda_chunk_fwd_default_plan.argtypes = [i64, i64, i32, i32, i32, i32, i32, ctypes.POINTER(Plan)]
     lib.kda_chunk_fwd_workspace_bytes.restype = i32
@@ -151,15 +154,15 @@ def _plan_copy(plan: Plan | None) -> Plan:
     return p2
 
 
-def _gate_code(gate: int) -> int:
+def _flags(gate: int, qk_norm: bool) -> int:
     if gate not in (GATE_LOG_DECAY, GATE_LOGITS):
         raise KdaError(5, f"unknown gate mode {gate}")
-    return gate
+    return (FLAG_GATE_LOGITS if gate == GATE_LOGITS else 0) | (FLAG_QK_L2NORM if qk_norm else 0)
 
 
 def chunk_fwd(q, k, v, log_alpha, beta, S0=None, chunk: int = 64, plan: Plan | None = None,
               o=None, S_T=None, workspace=None, ckpt_stride: int = 0, state_ckpt=None, cu_seqlens=None,
-              gate: int = GATE_LOG_DECAY):
+              gate: int = GATE_LOG_DECAY, qk_norm: bool = False):
     """Chunked prefill: returns (o [B,T,H,dv] in q's dtype, S_T [B,H,dk,dv] float32), and with
     ``ckpt_stride`` > 0 also the state checkpoints [B, T // ckpt_stride, H, dk, dv] float32
     (the state after every ckpt_stride tokens; a multiple of ``chunk``).
@@ -169,6 +172,7 @@ def chunk_fwd(q, k, v, log_alpha, beta, S0=None, chunk: int = 64, plan: Plan | N
     ``cu_seqlens`` (int32 [N+1] on the device) packs N sequences along T of a single batch
     row; S0 / S_T are then [N, H, dk, dv].
     ``gate=GATE_LOGITS``: log_alpha holds raw gate logits (log-decay -5 sigmoid(x)).
+    ``qk_norm=True``: q and k are L2-normalised per token inside the kernels.
     """
     if q.dim() != 4:
         raise KdaError(2, "q must be [B,T,H,dk]")
@@ -199,9 +203,10 @@ def chunk_fwd(q, k, v, log_alpha, beta, S0=None, chunk: int = 64, plan: Plan | N
         S_T = torch.empty((NS, H, dk, dv), dtype=torch.float32, device=dev)
     else:
         _require(S_T, "S_T", torch.float32, (NS, H, dk, dv), dev)
-    if _gate_code(gate):
+    flags = _flags(gate, qk_norm)
+    if flags:
         plan = _plan_copy(plan)
-        plan.gate = gate
+        plan.flags = flags
     if cu_seqlens is not None:
         p2 = _plan_copy(plan)
         p2.cu_seqlens = cu_seqlens.data_ptr()
@@ -256,7 +261,7 @@ def _decode_inputs(state, q, k, v, log_alpha, beta, n_tok):
     return N, H, dk, dv, dt, dev
 
 
-def decode_step(state, q, k, v, log_alpha, beta, o=None, gate: int = GATE_LOG_DECAY):
+def decode_step(state, q, k, v, log_alpha, beta, o=None, gate: int = GATE_LOG_DECAY, qk_norm: bool = False):
     """One recurrent step for N sequences; ``state`` [N,H,dk,dv] float32 is updated in place.
     q, k [N,H,dk], v [N,H,dv] (bf16 or float32), log_alpha [N,H,dk], beta [N,H] float32.
     Returns o [N,H,dv]."""
@@ -266,11 +271,11 @@ def decode_step(state, q, k, v, log_alpha, beta, o=None, gate: int = GATE_LOG_DE
     else:
         _require(o, "o", q.dtype, (N, H, dv), dev)
     _check(lib().kda_decode_step(_ptr(state), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
-                                _ptr(o), N, H, dk, dv, dt, _gate_code(gate), _stream(dev)))
+                                _ptr(o), N, H, dk, dv, dt, _flags(gate, qk_norm), _stream(dev)))
     return o
 
 
-def decode_verify(state, q, k, v, log_alpha, beta, o=None, gate: int = GATE_LOG_DECAY):
+def decode_verify(state, q, k, v, log_alpha, beta, o=None, gate: int = GATE_LOG_DECAY, qk_norm: bool = False):
     """Speculative decoding, verify: outputs of n draft tokens per sequence from ``state``
     [N,H,dk,dv], which is left unchanged.  q, k [N,n,H,dk], v [N,n,H,dv], log_alpha [N,n,H,dk],
     beta [N,n,H].  Returns o [N,n,H,dv] (draft j read after drafts 0..j)."""
@@ -283,11 +288,11 @@ def decode_verify(state, q, k, v, log_alpha, beta, o=None, gate: int = GATE_LOG_
     else:
         _require(o, "o", q.dtype, (N, n, H, dv), dev)
     _check(lib().kda_decode_verify(_ptr(state), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
-                                  _ptr(o), N, n, H, dk, dv, dt, _gate_code(gate), _stream(dev)))
+                                  _ptr(o), N, n, H, dk, dv, dt, _flags(gate, qk_norm), _stream(dev)))
     return o
 
 
-def decode_commit(state, q, k, v, log_alpha, beta, n_accept, gate: int = GATE_LOG_DECAY):
+def decode_commit(state, q, k, v, log_alpha, beta, n_accept, gate: int = GATE_LOG_DECAY, qk_norm: bool = False):
     """Speculative decoding, commit: advances ``state`` [N,H,dk,dv] in place by the first
     n_accept[i] (int32 [N] on the device, clamped to [0, n]) of sequence i's n draft tokens,
     given as for decode_verify.  Returns state."""
@@ -297,5 +302,5 @@ def decode_commit(state, q, k, v, log_alpha, beta, n_accept, gate: int = GATE_LO
     N, H, dk, dv, dt, dev = _decode_inputs(state, q, k, v, log_alpha, beta, n)
     _require(n_accept, "n_accept", torch.int32, (N,), dev)
     _check(lib().kda_decode_commit(_ptr(state), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
-                                  _ptr(n_accept), N, n, H, dk, dv, dt, _gate_code(gate), _stream(dev)))
+                                  _ptr(n_accept), N, n, H, dk, dv, dt, _flags(gate, qk_norm), _stream(dev)))
     return state

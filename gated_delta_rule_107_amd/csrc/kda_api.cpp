@@ -30,6 +30,7 @@ kda_status_t hip_fail(hipError_t e, const char* what) {
 bool dim_ok(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 bool chunk_ok(int32_t c) { return c == 16 || c == 32 || c == 64; }
 bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+constexpr uint32_t kAllFlags = KDA_GATE_LOGITS | KDA_QK_L2NORM;
 
 // Compute units of the current device, cached per device; 256 (MI355X) if no device is visible.
 int device_cus() {
@@ -207,8 +208,8 @@ kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v, const fl
         if (reinterpret_cast<uintptr_t>(cu) % 4 != 0) return fail(KDA_ERR_ALIGN, "cu_seqlens is not 4-byte aligned");
         if (plan->state_ckpt) return fail(KDA_ERR_UNSUPPORTED, "state checkpoints are not available with cu_seqlens");
     }
-    const int32_t gate = plan ? plan->gate : 0;
-    if (gate != KDA_GATE_LOG_DECAY && gate != KDA_GATE_LOGITS) return fail(KDA_ERR_UNSUPPORTED, "unknown gate mode %d", gate);
+    const uint32_t flags = plan ? plan->flags : 0u;
+    if (flags & ~kAllFlags) return fail(KDA_ERR_UNSUPPORTED, "unknown input flags 0x%x", flags);
     float* ckpt = plan ? plan->state_ckpt : nullptr;
     const int64_t ckpt_stride = ckpt ? plan->ckpt_stride : 0;
     if (ckpt && (ckpt_stride <= 0 || ckpt_stride % chunk != 0))
@@ -259,7 +260,7 @@ kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v, const fl
     a.n_seg = r.n_seg; a.seg_len = r.seg_len; a.dv_block = r.dv_block;
     a.ckpt = ckpt; a.ckpt_stride = ckpt_stride;
     a.cu_seqlens = cu;
-    a.gate = gate;
+    a.flags = flags;
     if (cu) a.B = n_seq;                      // units and state rows are sequences
     a.bf16 = dt == KDA_DTYPE_BF16;
     hipError_t e;
@@ -311,12 +312,12 @@ namespace {
 kda_status_t decode_call(int mode, float* state, const void* q, const void* k, const void* v,
                          const float* log_alpha, const float* beta, void* o, const int32_t* n_accept,
                          int64_t N, int32_t n_tok, int32_t H, int32_t dk, int32_t dv, kda_dtype_t dt,
-                         kda_gate_t gate, void* stream) {
+                         uint32_t flags, void* stream) {
     if (N < 1 || H < 1 || n_tok < 1)
         return fail(KDA_ERR_SHAPE, "need N >= 1, H >= 1, n_draft >= 1 (got N=%lld H=%d n=%d)", (long long)N, H, n_tok);
     if (dt != KDA_DTYPE_F32 && dt != KDA_DTYPE_BF16) return fail(KDA_ERR_DTYPE, "unknown dtype %d", (int)dt);
     if (!dim_ok(dk) || !dim_ok(dv)) return fail(KDA_ERR_UNSUPPORTED, "dk, dv must be 16, 32, 64 or 128 (got %d, %d)", dk, dv);
-    if (gate != KDA_GATE_LOG_DECAY && gate != KDA_GATE_LOGITS) return fail(KDA_ERR_UNSUPPORTED, "unknown gate mode %d", (int)gate);
+    if (flags & ~kAllFlags) return fail(KDA_ERR_UNSUPPORTED, "unknown input flags 0x%x", flags);
     if (N * (int64_t)H * n_tok > 0x7fffffff) return fail(KDA_ERR_SHAPE, "N * n_draft * H too large");
     const bool want_o = mode != kda::DECODE_COMMIT;
     if (!state || !q || !k || !v || !log_alpha || !beta || (want_o && !o) || (!want_o && !n_accept))
@@ -341,7 +342,7 @@ kda_status_t decode_call(int mode, float* state, const void* q, const void* k, c
     a.o = want_o ? o : nullptr;
     a.n_accept = n_accept;
     a.N = N; a.n_tok = n_tok; a.H = H; a.dk = dk; a.dv = dv;
-    a.mode = mode; a.gate = gate; a.bf16 = dt == KDA_DTYPE_BF16;
+    a.mode = mode; a.flags = flags; a.bf16 = dt == KDA_DTYPE_BF16;
     hipError_t e = kda::launch_decode(a, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
     return KDA_OK;
@@ -353,27 +354,27 @@ extern "C" {
 
 kda_status_t kda_decode_step(float* state, const void* q, const void* k, const void* v,
                              const float* log_alpha, const float* beta, void* o, int64_t N,
-                             int32_t H, int32_t dk, int32_t dv, kda_dtype_t dt, kda_gate_t gate,
+                             int32_t H, int32_t dk, int32_t dv, kda_dtype_t dt, uint32_t flags,
                              void* stream) {
     return decode_call(kda::DECODE_STEP, state, q, k, v, log_alpha, beta, o, nullptr, N, 1, H, dk, dv, dt,
-                       gate, stream);
+                       flags, stream);
 }
 
 kda_status_t kda_decode_verify(const float* state, const void* q, const void* k, const void* v,
                                const float* log_alpha, const float* beta, void* o, int64_t N,
                                int32_t n_draft, int32_t H, int32_t dk, int32_t dv, kda_dtype_t dt,
-                               kda_gate_t gate, void* stream) {
+                               uint32_t flags, void* stream) {
     // the kernel of this mode never writes the state
     return decode_call(kda::DECODE_VERIFY, const_cast<float*>(state), q, k, v, log_alpha, beta, o, nullptr, N,
-                       n_draft, H, dk, dv, dt, gate, stream);
+                       n_draft, H, dk, dv, dt, flags, stream);
 }
 
 kda_status_t kda_decode_commit(float* state, const void* q, const void* k, const void* v,
                                const float* log_alpha, const float* beta, const int32_t* n_accept,
                                int64_t N, int32_t n_draft, int32_t H, int32_t dk, int32_t dv,
-                               kda_dtype_t dt, kda_gate_t gate, void* stream) {
+                               kda_dtype_t dt, uint32_t flags, void* stream) {
     return decode_call(kda::DECODE_COMMIT, state, q, k, v, log_alpha, beta, nullptr, n_accept, N, n_draft, H,
-                       dk, dv, dt, gate, stream);
+                       dk, dv, dt, flags, stream);
 }
 
 }  // extern "C"

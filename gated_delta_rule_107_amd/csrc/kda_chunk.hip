@@ -147,6 +147,10 @@ template <> struct MM<float> {
 template <int N> __device__ __forceinline__ float row_shr(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x110 | N, 0xF, 0xF, true));
 }
+// Within quads of lanes: value of lane (i ^ M), M in {1, 2}.
+template <int M> __device__ __forceinline__ float quad_xor(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), M == 1 ? 0xB1 : 0x4E, 0xF, 0xF, false));
+}
 // Value of the neighbouring lane (lanes 2i and 2i+1 swap).
 __device__ __forceinline__ float swap_adjacent(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
@@ -248,11 +252,12 @@ __host__ __device__ constexpr int pair_fo_index(int p, int pp) {   // p - pp >= 
 
 // ---------------------------------------------------------------- the kernel
 // MODE 0: outputs and final states; MODE 1: segment summaries (see ChunkArgs).
-// CK (MODE 0 only): also write state checkpoints.  A separate instantiation: the
-// checkpoint code, even never taken, costs the loop about 4 % on a full-GPU workload.
-template <typename OpT, int DK, int C, int MODE, bool CK>
+// EXT: the optional features of a call (state checkpoints in MODE 0, gate logits, q / k
+// normalisation), switched by the arguments at run time.  A separate instantiation: their
+// code, even never taken, costs the plain loop several per cent.
+template <typename OpT, int DK, int C, int MODE, bool EXT>
 __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
-    static_assert(!CK || MODE == 0, "checkpoints are written by the one-pass / pass-2 kernel");
+    constexpr bool CK = EXT && MODE == 0;             // checkpoints: one-pass / pass-2 kernel only
     using MF = MM<OpT>;
     using B16 = typename MF::B16;
     using L4 = Ld4<OpT>;
@@ -463,11 +468,49 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
             }
     }
 
+    // Optional q / k normalisation.  For the chunk whose k and q sit in the prefetch
+    // registers, each wave sums the squares of its 16 channels per token; the partials go to
+    // the diagonal-block area of LDS (dead from phase 4 until the next phase 2) as
+    // [wave][token][k, q], and gate prep scales k and q by 1 / sqrt(sum + eps) before use.
+    const bool qk_norm = EXT && (a.flags & FLAG_QK_L2NORM);
+    float* s_nrm = s_ad;
+    static_assert(8 * C * 2 * 4 <= NT * 16 * 16 * 4, "normalisation partials exceed their LDS area");
+    auto norm_partials = [&](int tid) {
+        const int lane = tid & 63;
+        const int tq = 4 * (lane >> 4) + ((lane >> 2) & 3);        // this lane's prefetched token quad
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float kf[4], qf[4], kk = 0.f, qq = 0.f;
+            L4::to_f(pk[j], kf);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) kk += kf[e] * kf[e];
+            if (want_o) {
+                L4::to_f(pq[j], qf);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) qq += qf[e] * qf[e];
+            }
+            kk += quad_xor<1>(kk);                               // the wave's 4 channel quads
+            kk += quad_xor<2>(kk);
+            qq += quad_xor<1>(qq);
+            qq += quad_xor<2>(qq);
+            if ((lane & 3) == 0 && tq < C / 4) {
+                s_nrm[(wave * C + 4 * tq + j) * 2] = kk;
+                s_nrm[(wave * C + 4 * tq + j) * 2 + 1] = qq;
+            }
+        }
+    };
+
     __builtin_amdgcn_s_waitcnt(0x0F70);              // vmcnt(0): the start state is in registers
     const int64_t nchunks = t_end > t_begin ? (t_end - t_begin + C - 1) / C : 0;
     if (nchunks > 0) {
         prefetch_gates(t_begin, threadIdx.x);
         prefetch_v(t_begin, threadIdx.x);
+        if constexpr (EXT) {
+            if (qk_norm) {
+                __syncthreads();                     // LDS zeroing done before the partials land
+                norm_partials(threadIdx.x);
+            }
+        }
     }
 
     // Software pipeline over chunks.  Iteration n runs the state chain of chunk n and prepares
@@ -513,12 +556,37 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
         __syncthreads();   // the previous iteration's readers of the staging tiles are done
         // Branches stay at phase boundaries: the chain and the gate prep below form one block
         // in which the compiler interleaves MFMA and VALU work.
-        if constexpr (nxt) {
-            if (a.gate) {                            // raw logits: log-decay -5 sigmoid (uniform)
+        if constexpr (nxt && EXT) {
+            if (a.flags & FLAG_GATE_LOGITS) {        // raw logits: log-decay -5 sigmoid (uniform)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) pla[j][e] = gate_from_logit(pla[j][e]);
+            }
+            if (qk_norm) {                           // k, q of chunk n+1 scaled to unit norm (uniform)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int t = min(4 * tq + j, C - 1);           // (idle lanes: any token)
+                    float sk = 0.f, sq = 0.f;
+#pragma unroll
+                    for (int w2 = 0; w2 < NCT; ++w2) {
+                        sk += s_nrm[(w2 * C + t) * 2];
+                        sq += s_nrm[(w2 * C + t) * 2 + 1];
+                    }
+                    const float ik = __builtin_amdgcn_rsqf(sk + QK_NORM_EPS);
+                    float f[4];
+                    L4::to_f(pk[j], f);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) f[e] *= ik;
+                    pk[j] = L4::from_f(f);
+                    if (want_o) {
+                        const float iq = __builtin_amdgcn_rsqf(sq + QK_NORM_EPS);
+                        L4::to_f(pq[j], f);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) f[e] *= iq;
+                        pq[j] = L4::from_f(f);
+                    }
+                }
             }
         }
 
@@ -878,19 +946,23 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
             for (int u = 0; u < NGV; ++u) {
                 const int gi2 = tid + 512 * u;
                 int row, gc;
-            granule(gi2, row, gc);
+                granule(gi2, row, gc);
                 if (row < C) *reinterpret_cast<g16*>(s_v + row * LVO + gc * VG) = vblk ? pv[u] : g16{0.f, 0.f, 0.f, 0.f};
             }
             if (n + 2 < nchunks) prefetch_v(t1 + C, tid);
         }
         __syncthreads();
 
-        // ================= (4) v(n+1) into the accumulator layout
+        // ================= (4) v(n+1) into the accumulator layout; normalisation partials of
+        // chunk n+2, whose k and q the prefetch registers now hold
         if constexpr (nxt) {
 #pragma unroll
             for (int p = 0; p < NT; ++p)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) vr[p][r] = s_v[(16 * p + g4 + r) * LVO + 16 * wave + jl];
+            if constexpr (EXT) {
+                if (qk_norm && n + 2 < nchunks) norm_partials(tid);
+            }
         }
     };
 
@@ -937,10 +1009,10 @@ size_t chunk_lds_bytes(bool bf16_, int dk, int chunk, int /*dv_block*/) {
     return (size_t)lds_layout(bf16_ ? 2 : 4, dk, chunk).total;
 }
 
-template <typename OpT, int DK, int C, int MODE, bool CK>
+template <typename OpT, int DK, int C, int MODE, bool EXT>
 static hipError_t launch_chunk_m(const ChunkArgs& a, hipStream_t st) {
     constexpr size_t lds = (size_t)lds_layout(sizeof(OpT), DK, C).total;
-    auto kern = chunk_kernel<OpT, DK, C, MODE, CK>;
+    auto kern = chunk_kernel<OpT, DK, C, MODE, EXT>;
     static bool attr_set = false;   // per instantiation; the attribute is device-independent
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 163840);
@@ -957,8 +1029,9 @@ static hipError_t launch_chunk_m(const ChunkArgs& a, hipStream_t st) {
 
 template <typename OpT, int DK, int C>
 static hipError_t launch_chunk_t(const ChunkArgs& a, hipStream_t st) {
-    if (a.mode == 1) return launch_chunk_m<OpT, DK, C, 1, false>(a, st);
-    return a.ckpt ? launch_chunk_m<OpT, DK, C, 0, true>(a, st) : launch_chunk_m<OpT, DK, C, 0, false>(a, st);
+    const bool ext = a.flags != 0 || (a.mode == 0 && a.ckpt);
+    if (a.mode == 1) return ext ? launch_chunk_m<OpT, DK, C, 1, true>(a, st) : launch_chunk_m<OpT, DK, C, 1, false>(a, st);
+    return ext ? launch_chunk_m<OpT, DK, C, 0, true>(a, st) : launch_chunk_m<OpT, DK, C, 0, false>(a, st);
 }
 
 template <typename OpT, int DK>

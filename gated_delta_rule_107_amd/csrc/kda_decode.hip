@@ -47,7 +47,7 @@ __global__ __launch_bounds__((DecodeMap<DK, DV>::NTB)) __attribute__((amdgpu_wav
     float* __restrict__ state, const ET* __restrict__ q, const ET* __restrict__ k,
     const ET* __restrict__ v, const float* __restrict__ log_alpha,
     const float* __restrict__ beta, ET* __restrict__ o, const int* __restrict__ n_accept,
-    int H, int n_tok, int gate) {
+    int H, int n_tok, unsigned flags) {
     using DM = DecodeMap<DK, DV>;
     constexpr int CG = DM::CG, RG = DM::RG, RPT = DM::RPT, NT = DM::NT, NWV = DM::NWV;
     static_assert(DK % RG == 0 && DK <= NT && 4 * CG <= NT, "decode thread map");
@@ -65,8 +65,10 @@ __global__ __launch_bounds__((DecodeMap<DK, DV>::NTB)) __attribute__((amdgpu_wav
     // writes its copy while threads may still read token j's in the state update
     __shared__ float s_tok[2][3][DK];
     __shared__ f32x4 s_p[NWV][CG], s_r[NWV][CG];
-    __shared__ float s_kq[NWV];
+    __shared__ float s_kq[NWV], s_kk[NWV], s_qq[NWV];   // per-wave k.q, |k|^2, |q|^2
     __shared__ f32x4 s_u[CG];
+    const int gate = flags & FLAG_GATE_LOGITS;
+    const bool norm = flags & FLAG_QK_L2NORM;       // q, k normalised per token (uniform)
 
     f32x4* S = reinterpret_cast<f32x4*>(state + unit * (size_t)(DK * DV));
     f32x4 sv[RPT];
@@ -110,21 +112,36 @@ __global__ __launch_bounds__((DecodeMap<DK, DV>::NTB)) __attribute__((amdgpu_wav
         float* s_a = s_tok[buf][0];
         float* s_k = s_tok[buf][1];
         float* s_q = s_tok[buf][2];
-        float kq = 0.f;
+        // With normalisation the raw k and q go to LDS and their norms scale the results
+        // instead: p and u by 1/|k|, r by 1/|q|, k.q by both (the reducer applies them).
+        float kq = 0.f, k2 = 0.f, q2 = 0.f;
         if (tid < DK) {
             const float kk = to_f32(k_c);
             s_a[tid] = fast_exp(log_decay(la_c, gate));
             s_k[tid] = kk;
+            k2 = kk * kk;
             if (want_o) {
                 const float qq = to_f32(q_c);
                 s_q[tid] = qq;
                 kq = kk * qq;
+                q2 = qq * qq;
             }
         }
         if (want_o) {
 #pragma unroll
             for (int m = WAVE / 2; m >= 1; m >>= 1) kq += __shfl_xor(kq, m);
             if ((tid & (WAVE - 1)) == 0) s_kq[w] = kq;
+        }
+        if (norm) {
+#pragma unroll
+            for (int m = WAVE / 2; m >= 1; m >>= 1) {
+                k2 += __shfl_xor(k2, m);
+                if (want_o) q2 += __shfl_xor(q2, m);
+            }
+            if ((tid & (WAVE - 1)) == 0) {
+                s_kk[w] = k2;
+                s_qq[w] = q2;
+            }
         }
         __syncthreads();
 
@@ -166,11 +183,22 @@ __global__ __launch_bounds__((DecodeMap<DK, DV>::NTB)) __attribute__((amdgpu_wav
                     KQ += s_kq[ww];
                 }
             }
-            const float u = b_c * (to_f32(v_c) - P);
-            s_u[rc][re] = u;
+            float ik = 1.f, iq = 1.f;                   // 1 / |k|, 1 / |q| (normalisation)
+            if (norm) {
+                float KK = 0.f, QQ = 0.f;
+#pragma unroll
+                for (int ww = 0; ww < NWV; ++ww) {
+                    KK += s_kk[ww];
+                    QQ += s_qq[ww];
+                }
+                ik = __builtin_amdgcn_rsqf(KK + QK_NORM_EPS);
+                iq = __builtin_amdgcn_rsqf(QQ + QK_NORM_EPS);
+            }
+            const float u = b_c * (to_f32(v_c) - P * ik);
+            s_u[rc][re] = u * ik;                       // the update adds raw k times u / |k|
             if (want_o) {
                 const size_t th = (n * (unsigned)n_tok + j) * (unsigned)H + h;
-                (o + th * DV)[ut] = from_f32<ET>(R + KQ * u);
+                (o + th * DV)[ut] = from_f32<ET>(R * iq + KQ * ik * iq * u);
             }
         }
         __syncthreads();
@@ -192,7 +220,7 @@ static hipError_t launch_decode_m(const DecodeArgs& a, hipStream_t st) {
     const unsigned nblk = (unsigned)(a.N * a.H);
     hipLaunchKernelGGL((decode_kernel<ET, DK, DV, MODE>), dim3(nblk), dim3(DecodeMap<DK, DV>::NTB), 0, st,
                        a.state, (const ET*)a.q, (const ET*)a.k, (const ET*)a.v, a.log_alpha, a.beta,
-                       (ET*)a.o, a.n_accept, (int)a.H, (int)a.n_tok, (int)a.gate);
+                       (ET*)a.o, a.n_accept, (int)a.H, (int)a.n_tok, a.flags);
     return hipGetLastError();
 }
 

@@ -8,6 +8,10 @@
 
 namespace kda {
 
+// kda_input_flag_t bits as the kernels see them
+constexpr uint32_t FLAG_GATE_LOGITS = 1u, FLAG_QK_L2NORM = 2u;
+constexpr float QK_NORM_EPS = 1e-6f;          // x / sqrt(sum x^2 + eps)
+
 // Decode modes: one step (state updated in place); verify n_tok draft tokens (outputs only,
 // the state read but not written); commit the first n_accept[n] of n_tok tokens (state only).
 enum { DECODE_STEP = 0, DECODE_VERIFY = 1, DECODE_COMMIT = 2 };
@@ -22,7 +26,7 @@ struct DecodeArgs {
     int32_t n_tok;                   // tokens per sequence (1 for a step)
     int32_t H, dk, dv;
     int32_t mode;
-    int32_t gate;                    // 0: log_alpha is the log-decay; 1: raw logit, -5 sigmoid
+    uint32_t flags;                  // kda_input_flag_t bits (gate logits, q/k L2 normalisation)
     bool bf16;
 };
 
@@ -51,7 +55,7 @@ struct ChunkArgs {
     const int32_t* cu_seqlens;  // [B + 1] packed sequence offsets into one batch row, or null
     float* ckpt;            // [B, T / ckpt_stride, H, dk, dv] state checkpoints (mode 0) or null
     int64_t ckpt_stride;    // tokens between checkpoints, a multiple of chunk
-    int32_t gate;           // 0: log_alpha holds log-decays; 1: raw logits, log-decay -5 sigmoid
+    uint32_t flags;         // kda_input_flag_t bits (gate logits, q/k L2 normalisation)
     int32_t mode;
     bool bf16;
 };

@@ -52,14 +52,17 @@ extern "C" {
 /* Storage type of q, k, v and o.  log_alpha, beta and every state are float32. */
 typedef enum { KDA_DTYPE_F32 = 0, KDA_DTYPE_BF16 = 1 } kda_dtype_t;
 
-/* How the log_alpha argument is read (every call that takes one).
- * KDA_GATE_LOG_DECAY: log_alpha holds the log-decay itself, clamped to [-5, 0].
+/* Input options of every call, bit flags (kda_plan_t.flags for kda_chunk_fwd, the `flags`
+ * argument of the decode calls); 0 = none.
  * KDA_GATE_LOGITS: log_alpha holds raw gate logits x; the log-decay is the floored
  *   activation -5 sigmoid(x) = -5 / (1 + e^-x), in (-5, 0), computed inside the kernels
  *   (the floor constant is what made the gate's activation need a lower bound: orkas.ai
  *   "Kimi K3 architecture", section "The floor that removed a GPU code path"; the
- *   sigmoid form is this library's reading).  Same bytes read, no separate pass. */
-typedef enum { KDA_GATE_LOG_DECAY = 0, KDA_GATE_LOGITS = 1 } kda_gate_t;
+ *   sigmoid form is this library's reading).  Same bytes read, no separate pass.
+ * KDA_QK_L2NORM: q and k are normalised per token and head inside the kernels,
+ *   x / sqrt(sum_c x_c^2 + 1e-6) over the dk channels, before every other step.  The
+ *   pages leave normalisation to the model; the epsilon form is this library's choice. */
+typedef enum { KDA_GATE_LOGITS = 1, KDA_QK_L2NORM = 2 } kda_input_flag_t;
 
 typedef enum {
     KDA_OK = 0,
@@ -103,7 +106,7 @@ typedef enum {
  *   pass only (n_segments 0 or 1) and no state checkpoints.  The offsets are
  *   read on the device: values outside [0, T] are clamped, other invalid
  *   arrays give unspecified (but in-bounds) results.
- * gate: a kda_gate_t, how log_alpha is read (0 = log-decays).
+ * flags: kda_input_flag_t bits (0 = log-decays, q and k used as given).
  * A zeroed plan (all fields 0 / NULL) means "library default" for each field.
  */
 typedef struct {
@@ -121,7 +124,7 @@ typedef struct {
     int64_t ckpt_stride;
     const int32_t* cu_seqlens;
     int32_t n_seqs;
-    int32_t gate;
+    uint32_t flags;
 } kda_plan_t;
 
 /* Fills *plan with the library's default for this problem on the current
@@ -143,7 +146,7 @@ kda_status_t kda_chunk_fwd_workspace_bytes(int64_t B, int64_t T, int32_t H, int3
  *   q, k       [B, T, H, dk]  dt
  *   v          [B, T, H, dv]  dt
  *   log_alpha  [B, T, H, dk]  float32 log-decays (values outside [-5, 0] are clamped),
- *              or raw gate logits when plan->gate == KDA_GATE_LOGITS
+ *              or raw gate logits when plan->flags has KDA_GATE_LOGITS
  *   beta       [B, T, H]      float32
  *   S0         [B, H, dk, dv] float32 start state, or NULL for zeros
  *   o          [B, T, H, dv]  dt, written
@@ -174,7 +177,7 @@ kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v,
  *   state      [N, H, dk, dv] float32, read and overwritten
  *   q, k       [N, H, dk]     dt
  *   v          [N, H, dv]     dt
- *   log_alpha  [N, H, dk]     float32, read as `gate` says
+ *   log_alpha  [N, H, dk]     float32, read as `flags` says
  *   beta       [N, H]         float32
  *   o          [N, H, dv]     dt, written; must not overlap state or inputs
  * Sizes: dk, dv in {16, 32, 64, 128}; N * H < 2^31.
@@ -182,7 +185,7 @@ kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v,
 kda_status_t kda_decode_step(float* state, const void* q, const void* k, const void* v,
                              const float* log_alpha, const float* beta, void* o,
                              int64_t N, int32_t H, int32_t dk, int32_t dv, kda_dtype_t dt,
-                             kda_gate_t gate, void* stream);
+                             uint32_t flags, void* stream);
 
 /*
  * Speculative decoding, verify half.  Because the state is updated in place, a
@@ -195,7 +198,7 @@ kda_status_t kda_decode_step(float* state, const void* q, const void* k, const v
  *   state      [N, H, dk, dv]       float32, read only
  *   q, k       [N, n_draft, H, dk]  dt
  *   v          [N, n_draft, H, dv]  dt
- *   log_alpha  [N, n_draft, H, dk]  float32, read as `gate` says
+ *   log_alpha  [N, n_draft, H, dk]  float32, read as `flags` says
  *   beta       [N, n_draft, H]      float32
  *   o          [N, n_draft, H, dv]  dt, written; must not overlap any input
  * Sizes: as kda_decode_step, 1 <= n_draft and N * n_draft * H < 2^31.
@@ -203,7 +206,7 @@ kda_status_t kda_decode_step(float* state, const void* q, const void* k, const v
 kda_status_t kda_decode_verify(const float* state, const void* q, const void* k, const void* v,
                                const float* log_alpha, const float* beta, void* o,
                                int64_t N, int32_t n_draft, int32_t H, int32_t dk, int32_t dv,
-                               kda_dtype_t dt, kda_gate_t gate, void* stream);
+                               kda_dtype_t dt, uint32_t flags, void* stream);
 
 /*
  * Speculative decoding, commit half (same section): the caller keeps the drafts'
@@ -221,7 +224,7 @@ kda_status_t kda_decode_verify(const float* state, const void* q, const void* k,
 kda_status_t kda_decode_commit(float* state, const void* q, const void* k, const void* v,
                                const float* log_alpha, const float* beta, const int32_t* n_accept,
                                int64_t N, int32_t n_draft, int32_t H, int32_t dk, int32_t dv,
-                               kda_dtype_t dt, kda_gate_t gate, void* stream);
+                               kda_dtype_t dt, uint32_t flags, void* stream);
 
 /* Static description of a status code. */
 const char* kda_status_str(kda_status_t status);

@@ -71,6 +71,7 @@ class Recipe:
     dv: int
     chunk: int
     dtype: str                      # "f32" or "bf16": storage of q, k, v, o
+    qk: str = "l2"                  # "l2": q, k ~ N(0,1) L2-normalised per token; "raw": not normalised
     loga: str = "sig15"             # "sig15": -5*sigmoid(N(0,1.5^2)); "unif": U[-5,0);
                                     # "logit15": raw gate logits N(0,1.5^2) (the log-decay is
                                     # formed from them by the code under test)
@@ -134,6 +135,8 @@ def _gen_block(r: Recipe, name: str, b: int, h: int, blk: int, n: int) -> np.nda
     if name in ("q", "k"):
         g = _gen(r.tag, T_Q if name == "q" else T_K, b, h, blk)
         x = g.standard_normal((n, r.dk), dtype=np.float32)
+        if r.qk == "raw":                    # unnormalised (for the in-kernel normalisation)
+            return _store(x, r.dtype)
         nrm = np.sqrt(np.sum(x * x, axis=1, dtype=np.float32), dtype=np.float32)
         return _store(x / nrm[:, None], r.dtype)
     if name == "v":
@@ -263,7 +266,8 @@ def make_prefill_device(r: Recipe, device, keyed_heads=()) -> dict:
                     n = t1 - t0
                     if name in ("q", "k"):
                         x = torch.randn((n, r.dk), generator=gen, device=device, dtype=torch.float32)
-                        x = x / torch.sqrt((x * x).sum(dim=1, keepdim=True))
+                        if r.qk != "raw":
+                            x = x / torch.sqrt((x * x).sum(dim=1, keepdim=True))
                     elif name == "v":
                         x = torch.randn((n, r.dv), generator=gen, device=device, dtype=torch.float32)
                     elif name == "beta":

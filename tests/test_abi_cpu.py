@@ -146,27 +146,27 @@ def test_plan_and_workspace_queries(lib):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(state=None), NULL), (dict(o=None), NULL), (dict(N=0), SHAPE), (dict(dt=3), DTYPE),
-    (dict(dk=48), UNSUP), (dict(gate=2), UNSUP), (dict(q=A[1] + 2), ALIGN), (dict(o=A[0]), ALIAS),
+    (dict(dk=48), UNSUP), (dict(flags=4), UNSUP), (dict(q=A[1] + 2), ALIGN), (dict(o=A[0]), ALIAS),
     (dict(q=A[0] + 64), ALIAS),
 ])
 def test_decode_step_rejects(lib, kw, code):
     args = dict(state=A[0], q=A[1], k=A[2], v=A[3], la=A[4], beta=A[5], o=A[6], N=4, H=2, dk=16, dv=16, dt=BF16,
-                gate=0)
+                flags=0)
     args.update(kw)
     r = lib.kda_decode_step(args["state"], args["q"], args["k"], args["v"], args["la"], args["beta"], args["o"],
-                            args["N"], args["H"], args["dk"], args["dv"], args["dt"], args["gate"], None)
+                            args["N"], args["H"], args["dk"], args["dv"], args["dt"], args["flags"], None)
     assert r == code
 
 
 def decode_multi_args(**kw):
     args = dict(state=A[0], q=A[1], k=A[2], v=A[3], la=A[4], beta=A[5], o=A[6], n_accept=A[7], N=4, n=3, H=2,
-                dk=16, dv=16, dt=BF16, gate=0)
+                dk=16, dv=16, dt=BF16, flags=0)
     args.update(kw)
     return args
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(o=None), NULL), (dict(n=0), SHAPE), (dict(N=1 << 20, n=1 << 12), SHAPE), (dict(gate=-1), UNSUP),
+    (dict(o=None), NULL), (dict(n=0), SHAPE), (dict(N=1 << 20, n=1 << 12), SHAPE), (dict(flags=0xFFFFFFFF), UNSUP),
     (dict(dv=8), UNSUP), (dict(o=A[6] + 8), ALIGN),
     (dict(o=A[1] + 32), ALIAS),                      # o overlaps q of the 3 draft tokens
     (dict(state=A[6]), ALIAS),                       # o overlaps the (read-only) state
@@ -174,7 +174,7 @@ def decode_multi_args(**kw):
 def test_decode_verify_rejects(lib, kw, code):
     a = decode_multi_args(**kw)
     r = lib.kda_decode_verify(a["state"], a["q"], a["k"], a["v"], a["la"], a["beta"], a["o"], a["N"], a["n"],
-                              a["H"], a["dk"], a["dv"], a["dt"], a["gate"], None)
+                              a["H"], a["dk"], a["dv"], a["dt"], a["flags"], None)
     assert r == code
 
 
@@ -185,17 +185,20 @@ def test_decode_verify_rejects(lib, kw, code):
 def test_decode_commit_rejects(lib, kw, code):
     a = decode_multi_args(**kw)
     r = lib.kda_decode_commit(a["state"], a["q"], a["k"], a["v"], a["la"], a["beta"], a["n_accept"], a["N"],
-                              a["n"], a["H"], a["dk"], a["dv"], a["dt"], a["gate"], None)
+                              a["n"], a["H"], a["dk"], a["dv"], a["dt"], a["flags"], None)
     assert r == code
 
 
-def test_chunk_fwd_gate_mode_errors(lib):
+def test_input_flag_errors(lib):
     import gated_delta_rule_107_amd as g
     p = g.Plan(1, 0)
-    p.gate = 3
+    p.flags = 4                                                      # unknown bit
     assert call_chunk(lib, plan=p) == UNSUP
-    p.gate = 1
-    assert call_chunk(lib, plan=p) == OK or True       # accepted by validation (no launch without a GPU)
+    assert "flags" in lib.kda_last_error().decode()
+    with pytest.raises(g.KdaError) as e:                             # the binding's own check
+        g._flags(7, False)
+    assert e.value.code == UNSUP
+    assert g._flags(g.GATE_LOGITS, True) == g.FLAG_GATE_LOGITS | g.FLAG_QK_L2NORM
 
 
 def test_python_binding_rejects_cpu_tensors():

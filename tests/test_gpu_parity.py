@@ -436,9 +436,9 @@ def test_prefill_gate_logits(g, dtype, B, T, H, dk, dv, chunk, nseg):
 
 # ------------------------------------------------------------------ speculative verify / commit
 
-def _drafts(dtype, N, n, H, dk, dv, loga="unif"):
+def _drafts(dtype, N, n, H, dk, dv, loga="unif", qk="l2"):
     """Draft-token inputs [N, n, H, .] (the prefill layout) and a start state [N, H, dk, dv]."""
-    r = ks.Recipe("drafts", B=N, T=1, H=H, dk=dk, dv=dv, chunk=16, dtype=dtype, loga=loga, s0_std=0.05,
+    r = ks.Recipe("drafts", B=N, T=1, H=H, dk=dk, dv=dv, chunk=16, dtype=dtype, loga=loga, qk=qk, s0_std=0.05,
                   tag=ks.TAG_BASE + 300, steps=n)
     d = ks.make_decode(r)
     tr = lambda a: np.ascontiguousarray(np.swapaxes(a, 0, 1))  # noqa: E731
@@ -503,3 +503,79 @@ def test_decode_verify_commit_full_size(g):
     S_ref = oracle.kda_decode_commit(state0[sel], *(x[nm][sel] for nm in ("q", "k", "v", "log_alpha", "beta")),
                                      np.full(8, n))
     check(to_np(o)[sel], to_np(state)[sel], o_ref, S_ref, TOL["bf16"], "verify/commit (8 sampled sequences)")
+
+
+# ------------------------------------------------------------------ optional q/k L2 normalisation
+
+@pytest.mark.parametrize("dtype,B,T,H,dk,dv,chunk,nseg,gate", [
+    ("f32", 1, 64, 2, 16, 16, 16, 1, 0),
+    ("bf16", 2, 333, 2, 64, 64, 32, 1, 1),
+    ("bf16", 1, 500, 2, 128, 128, 64, 3, 0),
+    ("bf16", 1, 200, 1, 32, 128, 16, 2, 1),
+])
+def test_prefill_qk_norm(g, dtype, B, T, H, dk, dv, chunk, nseg, gate):
+    """Unnormalised q, k (N(0,1) entries): the kernels normalise them per token."""
+    import torch
+    _say(f"case: qk norm {dtype} B{B} T{T} H{H} {dk}/{dv} C{chunk} P{nseg} gate {gate}")
+    x = ks.make_prefill(small_recipe(dtype, B, T, H, dk, dv, chunk, qk="raw", s0_std=0.05,
+                                     loga="logit15" if gate else "sig15"))
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q, k, v = (dev_tensor(x[n], dt) for n in ("q", "k", "v"))
+    o, S = g.chunk_fwd(q, k, v, dev_tensor(x["log_alpha"], torch.float32), dev_tensor(x["beta"], torch.float32),
+                       dev_tensor(x["S0"], torch.float32), chunk=chunk, plan=g.Plan(nseg, min(dk, dv)),
+                       gate=gate, qk_norm=True)
+    torch.cuda.synchronize()
+    la = oracle.gate_from_logits(x["log_alpha"]) if gate else x["log_alpha"]
+    o_ref, S_ref = oracle.kda_loop(oracle.l2_normalize(x["q"]), oracle.l2_normalize(x["k"]), x["v"], la,
+                                   x["beta"], x["S0"])
+    check(to_np(o), to_np(S), o_ref, S_ref, TOL[dtype], "prefill with q/k normalisation")
+
+
+def test_packed_sequences_qk_norm(g):
+    import torch
+    lens = [70, 0, 129, 64]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    x = ks.make_prefill(small_recipe("bf16", 1, int(cu[-1]), 2, 64, 64, 32, qk="raw"))
+    dt = torch.bfloat16
+    S0 = np.random.default_rng(7).standard_normal((len(lens), 2, 64, 64)).astype(np.float32) * 0.05
+    o, S = g.chunk_fwd(*(dev_tensor(x[n], dt) for n in ("q", "k", "v")), dev_tensor(x["log_alpha"], torch.float32),
+                       dev_tensor(x["beta"], torch.float32), dev_tensor(S0, torch.float32), chunk=32,
+                       cu_seqlens=dev_tensor(cu, torch.int32), qk_norm=True)
+    torch.cuda.synchronize()
+    o, S = to_np(o), to_np(S)
+    for i in range(len(lens)):
+        a, b = int(cu[i]), int(cu[i + 1])
+        sl = lambda t: t[:, a:b]  # noqa: E731
+        o_ref, S_ref = oracle.kda_loop(oracle.l2_normalize(sl(x["q"])), oracle.l2_normalize(sl(x["k"])), sl(x["v"]),
+                                       sl(x["log_alpha"]), sl(x["beta"]), S0[i:i + 1])
+        assert oracle.rel_fro(S[i:i + 1], S_ref) <= TOL["bf16"]
+        if b > a:
+            assert oracle.rel_fro(o[:, a:b], o_ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dtype,dk,dv", [("f32", 32, 16), ("bf16", 128, 128), ("bf16", 64, 32)])
+def test_decode_family_qk_norm(g, dtype, dk, dv):
+    """Step, verify and commit with unnormalised q, k normalised inside the kernel."""
+    import torch
+    N, n, H = 5, 3, 2
+    _say(f"case: decode qk norm {dtype} {dk}/{dv}")
+    state0, x = _drafts(dtype, N, n, H, dk, dv, qk="raw")
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    xd = {nm: dev_tensor(x[nm], torch.float32 if nm in ("log_alpha", "beta") else dt) for nm in x}
+    qn, kn = oracle.l2_normalize(x["q"]), oracle.l2_normalize(x["k"])
+    tol = TOL[dtype] if dtype == "bf16" else 1e-5
+    state = dev_tensor(state0, torch.float32)
+    o = g.decode_verify(state, xd["q"], xd["k"], xd["v"], xd["log_alpha"], xd["beta"], qk_norm=True)
+    o_ref = oracle.kda_decode_verify(state0, qn, kn, x["v"], x["log_alpha"], x["beta"])
+    st = state.clone()
+    o1 = g.decode_step(st, xd["q"][:, 0].contiguous(), xd["k"][:, 0].contiguous(), xd["v"][:, 0].contiguous(),
+                       xd["log_alpha"][:, 0].contiguous(), xd["beta"][:, 0].contiguous(), qk_norm=True)
+    n_acc = np.array([0, 1, 3, 2, 3], np.int32)
+    g.decode_commit(state, xd["q"], xd["k"], xd["v"], xd["log_alpha"], xd["beta"], torch.from_numpy(n_acc).cuda(),
+                    qk_norm=True)
+    torch.cuda.synchronize()
+    S_ref = oracle.kda_decode_commit(state0, qn, kn, x["v"], x["log_alpha"], x["beta"], n_acc)
+    eo, e1, es = (oracle.rel_fro(to_np(o), o_ref), oracle.rel_fro(to_np(o1), o_ref[:, 0]),
+                  oracle.rel_fro(to_np(state), S_ref))
+    _say(f"qk norm decode: verify {eo:.3e} step {e1:.3e} commit {es:.3e} (tol {tol:g})")
+    assert eo <= tol and e1 <= tol and es <= tol
