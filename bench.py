@@ -11,8 +11,9 @@ and state.  Inputs are seeded synthetic tensors already resident in HBM when
 the timed region starts.
 
 The prefill block also reports the same step with state checkpoints every 512
-tokens (the prefix-reuse output of kda_plan_t.state_ckpt) and the same step
-reading raw gate logits (kda_gate_t KDA_GATE_LOGITS).  The same JSON line
+tokens (the prefix-reuse output of kda_plan_t.state_ckpt), the same step
+reading raw gate logits (KDA_GATE_LOGITS) and with q / k normalised inside the
+kernels (KDA_QK_L2NORM).  The same JSON line
 also carries the decode figure (256 sequences x 32 heads,
 128x128 float32 state, 64 consecutive in-place steps) with the speculative
 verify of 4 drafts per sequence and the commit of all 4, the roofline of the
@@ -293,6 +294,18 @@ def bench_prefill(g, torch, r, x, steps, warmup):
     ms_gate = t0.elapsed_time(t1) / steps
     gate = {"ms_per_step": round(ms_gate, 5), "overhead": round(ms_gate / ms - 1.0, 4)}
     log("prefill from gate logits:", json.dumps(gate))
+    # ... and normalising q and k inside the kernels
+    for _ in range(warmup):
+        g.chunk_fwd(q, k, v, la, beta, S0, chunk=r.chunk, plan=plan, o=o, S_T=S_T, workspace=ws, qk_norm=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(steps):
+        g.chunk_fwd(q, k, v, la, beta, S0, chunk=r.chunk, plan=plan, o=o, S_T=S_T, workspace=ws, qk_norm=True)
+    t1.record()
+    torch.cuda.synchronize()
+    ms_norm = t0.elapsed_time(t1) / steps
+    gate["with_qk_norm"] = {"ms_per_step": round(ms_norm, 5), "overhead": round(ms_norm / ms - 1.0, 4)}
+    log("prefill with q/k normalisation:", json.dumps(gate["with_qk_norm"]))
     return ms, plan, per_launch, ckpt, gate
 
 
