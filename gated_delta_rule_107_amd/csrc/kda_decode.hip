@@ -42,7 +42,10 @@ template <int DK, int DV> struct DecodeMap {
 // Both follow orkas.ai "Kimi K3 architecture", section "The cost comes back in the serving
 // stack" (speculative decoding).  Token j of sequence n, head h sits at token-head index
 // (n n_tok + j) H + h of q, k, v, the gates, beta and o.
-template <typename ET, int DK, int DV, int MODE>
+// NORM: q and k are L2-normalised per token inside the kernel.  It is a compile-time
+// choice because its reductions, even untaken, push the plain step past the 64 VGPRs
+// that 8 waves per SIMD allow and make it spill.
+template <typename ET, int DK, int DV, int MODE, bool NORM>
 __global__ __launch_bounds__((DecodeMap<DK, DV>::NTB)) __attribute__((amdgpu_waves_per_eu(8))) void decode_kernel(
     float* __restrict__ state, const ET* __restrict__ q, const ET* __restrict__ k,
     const ET* __restrict__ v, const float* __restrict__ log_alpha,
@@ -68,7 +71,7 @@ __global__ __launch_bounds__((DecodeMap<DK, DV>::NTB)) __attribute__((amdgpu_wav
     __shared__ float s_kq[NWV], s_kk[NWV], s_qq[NWV];   // per-wave k.q, |k|^2, |q|^2
     __shared__ f32x4 s_u[CG];
     const int gate = flags & FLAG_GATE_LOGITS;
-    const bool norm = flags & FLAG_QK_L2NORM;       // q, k normalised per token (uniform)
+    constexpr bool norm = NORM;                     // q, k normalised per token
 
     f32x4* S = reinterpret_cast<f32x4*>(state + unit * (size_t)(DK * DV));
     f32x4 sv[RPT];
@@ -218,9 +221,14 @@ __global__ __launch_bounds__((DecodeMap<DK, DV>::NTB)) __attribute__((amdgpu_wav
 template <typename ET, int DK, int DV, int MODE>
 static hipError_t launch_decode_m(const DecodeArgs& a, hipStream_t st) {
     const unsigned nblk = (unsigned)(a.N * a.H);
-    hipLaunchKernelGGL((decode_kernel<ET, DK, DV, MODE>), dim3(nblk), dim3(DecodeMap<DK, DV>::NTB), 0, st,
-                       a.state, (const ET*)a.q, (const ET*)a.k, (const ET*)a.v, a.log_alpha, a.beta,
-                       (ET*)a.o, a.n_accept, (int)a.H, (int)a.n_tok, a.flags);
+    if (a.flags & FLAG_QK_L2NORM)
+        hipLaunchKernelGGL((decode_kernel<ET, DK, DV, MODE, true>), dim3(nblk), dim3(DecodeMap<DK, DV>::NTB), 0,
+                           st, a.state, (const ET*)a.q, (const ET*)a.k, (const ET*)a.v, a.log_alpha, a.beta,
+                           (ET*)a.o, a.n_accept, (int)a.H, (int)a.n_tok, a.flags);
+    else
+        hipLaunchKernelGGL((decode_kernel<ET, DK, DV, MODE, false>), dim3(nblk), dim3(DecodeMap<DK, DV>::NTB), 0,
+                           st, a.state, (const ET*)a.q, (const ET*)a.k, (const ET*)a.v, a.log_alpha, a.beta,
+                           (ET*)a.o, a.n_accept, (int)a.H, (int)a.n_tok, a.flags);
     return hipGetLastError();
 }
 
