@@ -51,15 +51,23 @@ typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
 // Accumulator layout (every 16x16 instruction here): lane l holds C[4*(l/16) + r][l % 16].
 template <typename OpT> struct MM;
 
+// Two floats rounded to bf16 and packed into one 32-bit register (v_cvt_pk_bf16_f32).  Four
+// elements converted one by one and then reinterpreted as the MFMA's 16-bit integer operand
+// compile to four single conversions and two v_perm_b32; built from two of these they take
+// two conversions.
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+typedef __attribute__((__vector_size__(2 * sizeof(unsigned)))) unsigned u32x2;
+__device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
+    return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+__device__ __forceinline__ bf16x4 pack_bf16x4(float a, float b, float c, float d) {
+    return __builtin_bit_cast(bf16x4, (u32x2){pack_bf16x2(a, b), pack_bf16x2(c, d)});
+}
+
 template <> struct MM<bf16> {
     static constexpr int KS = 32;                  // contraction per natural-order instruction
     typedef bf16x4 B16;                            // B operand for a 16-deep contraction
-    static __device__ __forceinline__ B16 b16(const f32x4& x) {
-        B16 r;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) r[j] = (bf16)x[j];
-        return r;
-    }
+    static __device__ __forceinline__ B16 b16(const f32x4& x) { return pack_bf16x4(x[0], x[1], x[2], x[3]); }
     // acc += A[r0 + m][c0 + kk] * B[kk][n] over kk < 16, B given as an accumulator-layout
     // tile (rows kk = 4g + j held by lane group g)
     static __device__ __forceinline__ f32x4 k16(const bf16* A, int ld, int r0, int c0, B16 b, f32x4 acc,
@@ -159,7 +167,7 @@ __device__ __forceinline__ float swap_adjacent(float x) {
 template <typename OpT> struct Pair2;
 template <> struct Pair2<bf16> {
     typedef bf16x2 V;
-    __device__ static V make(float a, float b) { return V{(bf16)a, (bf16)b}; }
+    __device__ static V make(float a, float b) { return __builtin_bit_cast(V, pack_bf16x2(a, b)); }
 };
 template <> struct Pair2<float> {
     typedef float __attribute__((__vector_size__(2 * sizeof(float)))) V;
@@ -185,12 +193,7 @@ template <> struct Ld4<bf16> {
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[e] = (float)v[e];
     }
-    static __device__ __forceinline__ V from_f(const float (&x)[4]) {
-        V v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (bf16)x[e];
-        return v;
-    }
+    static __device__ __forceinline__ V from_f(const float (&x)[4]) { return pack_bf16x4(x[0], x[1], x[2], x[3]); }
     static __device__ __forceinline__ V zero() { return from_f({0.f, 0.f, 0.f, 0.f}); }
 };
 template <> struct Ld4<float> {
@@ -641,9 +644,10 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
             // they are used.
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const bool ok = full || 4 * tq + j < Tn;
+                // tokens past the end scale by 0 (their loads read a clamped, valid token)
+                const float sc = (full || 4 * tq + j < Tn) ? LOG2E : 0.f;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) g2[j][e] = ok ? clamp_log_alpha(pla[j][e]) * LOG2E : 0.f;
+                for (int e = 0; e < 4; ++e) g2[j][e] = clamp_log_alpha(pla[j][e]) * sc;
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -659,8 +663,8 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
                 for (int qq = 0; qq < 4; ++qq) tp[qq] = qq < NT ? __shfl(inc, 16 * qq + 12 + gx, 64) : 0.f;
                 tot[e] = gp == 0 ? tp[0] : gp == 1 ? tp[1] : gp == 2 ? tp[2] : tp[3];
                 rp[e] = (gp > 0 ? tp[0] : 0.f) + (gp > 1 ? tp[1] : 0.f) + (gp > 2 ? tp[2] : 0.f);  // r_p
-                after[e] = (gp < 1 ? tp[1] : 0.f) + (gp < 2 ? tp[2] : 0.f) + (gp < 3 ? tp[3] : 0.f);
                 gcs[e] = tp[0] + tp[1] + tp[2] + tp[3];               // Gamma_C
+                after[e] = gcs[e] - rp[e] - tot[e];                   // later sub-tiles
                 tn1[e] = gp == 0 ? tp[1] : gp == 1 ? tp[2] : gp == 2 ? tp[3] : 0.f;   // sub-tile p+1
                 tn2[e] = gp == 0 ? tp[2] : gp == 1 ? tp[3] : 0.f;                      // p+2
                 tm1[e] = gp == 1 ? tp[0] : gp == 2 ? tp[1] : gp == 3 ? tp[2] : 0.f;   // p-1
@@ -685,6 +689,7 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
                 }
             }
             if (gact) {
+                const unsigned okq0 = (unsigned)(4 * tq * LKQ + gc0) * E, okl0 = (unsigned)(4 * tq * LDK + gc0) * E;
                 float er[4], eh[4], ed[4], ef1[4], ef2[4], gam[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -726,17 +731,20 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
                             rf2[e] = rh[e] * ef2[e];                  // ... of p+2
                         }
                     }
-                    *reinterpret_cast<V4*>(s_kt + t * LKQ + gc0) = L4::from_f(kt);
-                    *reinterpret_cast<V4*>(s_kl + t * LDK + gc0) = L4::from_f(kl);
-                    *reinterpret_cast<V4*>(s_rh + t * LDK + gc0) = L4::from_f(rh);
+                    // byte offsets: a per-lane part computed once plus constants (token j of the
+                    // quad, the array's place in LDS), which the stores take as immediates
+                    const unsigned okq = okq0 + j * (LKQ * E), okl = okl0 + j * (LDK * E);
+                    *at_bytes(reinterpret_cast<V4*>(s_kt), okq) = L4::from_f(kt);
+                    *at_bytes(reinterpret_cast<V4*>(s_kl), okl) = L4::from_f(kl);
+                    *at_bytes(reinterpret_cast<V4*>(s_rh), okl) = L4::from_f(rh);
                     if (want_o) {
-                        *reinterpret_cast<V4*>(s_qt + t * LKQ + gc0) = L4::from_f(qt);
-                        *reinterpret_cast<V4*>(s_ql + t * LDK + gc0) = L4::from_f(ql);
+                        *at_bytes(reinterpret_cast<V4*>(s_qt), okq) = L4::from_f(qt);
+                        *at_bytes(reinterpret_cast<V4*>(s_ql), okl) = L4::from_f(ql);
                     }
                     if (RV) {
-                        *reinterpret_cast<V4*>(s_rd + t * LDK + gc0) = L4::from_f(rd);
-                        if (NT == 4 && gp <= 1) *reinterpret_cast<V4*>(s_rf + t * LDK + gc0) = L4::from_f(rf1);
-                        if (NT == 4 && gp == 0) *reinterpret_cast<V4*>(s_rf + (32 + t) * LDK + gc0) = L4::from_f(rf2);
+                        *at_bytes(reinterpret_cast<V4*>(s_rd), okl) = L4::from_f(rd);
+                        if (NT == 4 && gp <= 1) *at_bytes(reinterpret_cast<V4*>(s_rf), okl) = L4::from_f(rf1);
+                        if (NT == 4 && gp == 0) *at_bytes(reinterpret_cast<V4*>(s_rf), okl + 32 * LDK * E) = L4::from_f(rf2);
                     }
                 }
             }

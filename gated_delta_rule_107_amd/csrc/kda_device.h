@@ -19,8 +19,10 @@ constexpr float LOG2E = 1.4426950408889634f;
 // path").  The upper clamp at 0 keeps every decay factor <= 1.
 constexpr float LOG_ALPHA_FLOOR = -5.0f;
 
+// One v_med3_f32 (fminf / fmaxf would first quiet signalling NaNs with an extra v_max_f32 per
+// value); a NaN input gives the floor, as fmaxf(NaN, -5) does.
 __device__ __forceinline__ float clamp_log_alpha(float x) {
-    return fminf(fmaxf(x, LOG_ALPHA_FLOOR), 0.0f);
+    return __builtin_amdgcn_fmed3f(x, LOG_ALPHA_FLOOR, 0.0f);
 }
 
 // e^x through the hardware 2^x unit.
