@@ -97,6 +97,11 @@ SHAPES = [
     ("bf16", 1, 45, 2, 16, 16, 16),
     ("bf16", 1, 300, 1, 128, 64, 16),
     ("bf16", 1, 129, 2, 128, 128, 32),
+    # one token: a single chunk holding one valid token (the degenerate prefill)
+    ("bf16", 3, 1, 2, 128, 128, 64),
+    ("f32", 1, 1, 1, 16, 16, 16),
+    # one full chunk and one token
+    ("bf16", 1, 17, 2, 64, 64, 16),
 ]
 
 
