@@ -991,16 +991,18 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
         } else if (!mcols) {
             dst = a.s_loc + (bh * a.n_seg + seg) * DK * dv; ld = dv;
         } else {
-            // the transition goes to the scan already split into bf16 high and low planes
-            bf16* mh = reinterpret_cast<bf16*>(a.m_tr) + (bh * a.n_seg + seg) * 2 * DK * DK + (col - dv);
+            // the transition goes to the scan already split into bf16 high and low planes, in
+            // the order of the scan's A operand
+            bf16* mh = reinterpret_cast<bf16*>(a.m_tr) + (bh * a.n_seg + seg) * 2 * DK * DK;
 #pragma unroll
             for (int tau = 0; tau < NCT; ++tau)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const float x = Sacc[tau][r];
                     const bf16 hi = (bf16)x;
-                    mh[(16 * tau + g4 + r) * DK] = hi;
-                    mh[DK * DK + (16 * tau + g4 + r) * DK] = (bf16)(x - (float)hi);
+                    const int at = mtr_index(DK, 16 * tau + g4 + r, col - dv);
+                    mh[at] = hi;
+                    mh[DK * DK + at] = (bf16)(x - (float)hi);
                 }
         }
         if (dst) {

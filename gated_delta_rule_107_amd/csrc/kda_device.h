@@ -43,16 +43,6 @@ __device__ __forceinline__ float log_decay(float x, int gate) {
     return gate ? gate_from_logit(x) : clamp_log_alpha(x);
 }
 
-// Copies 16 bytes per lane from global memory straight into LDS: lane i writes
-// lds + 16 i (lds wave-uniform); completion is tracked by the vector-memory counter.
-// The builtin exists for the device target only, and a host-pass reference to it
-// would silently drop the calling kernel's launch stub, hence the guard.
-__device__ __forceinline__ void copy16_global_to_lds(const void* src, void* lds) {
-#if __HIP_DEVICE_COMPILE__
-    __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
-#endif
-}
-
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
 

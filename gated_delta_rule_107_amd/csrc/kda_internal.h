@@ -46,7 +46,8 @@ struct ChunkArgs {
     void* o;                // [B,T,H,dv] (mode 0)
     float* s_final;         // [B,H,dk,dv] (mode 0)
     float* s_loc;           // [B,H,P,dk,dv] (mode 1)
-    void* m_tr;             // [B,H,P][2][dk][dk] bf16 (mode 1): M split into high and low parts
+    void* m_tr;             // [B,H,P][2][dk^2] bf16 (mode 1): M split into high and low parts,
+                            // each plane in the scan's operand order (mtr_index)
     int64_t B, T;           // with cu_seqlens: B = number of sequences, T = packed tokens
     int32_t H, dk, dv, chunk;
     int32_t n_seg;          // P
@@ -67,13 +68,23 @@ hipError_t launch_chunk(const ChunkArgs& a, hipStream_t st);
 struct ScanArgs {
     const float* s0;
     const float* s_loc;
-    const void* m_tr;       // [B,H,P][2][dk][dk] bf16: high and low parts of M (hi + lo ~ M)
+    const void* m_tr;       // [B,H,P][2][dk^2] bf16: high and low parts of M (hi + lo ~ M), mtr_index order
     float* starts;
     int64_t B;
     int32_t H, dk, dv, n_seg;
 };
 
 hipError_t launch_scan(const ScanArgs& a, hipStream_t st);
+
+// Position of M[row][k] inside one dk^2 plane of a segment transition: the order in which the
+// scan's MFMA reads its A operand, so that each of its loads is one contiguous run of 64 x 16
+// bytes.  Mixed radix (16-row tile, 32-deep contraction step, granule g * 16 + m, element),
+// where granule (g, m) holds columns 32 t + 8 g .. +7 of row 16 w + m; a (tile, step) pair has
+// 16 min(4, dk / 8) granules, so the plane holds exactly dk^2 elements.
+__host__ __device__ constexpr int mtr_index(int dk, int row, int k) {
+    const int ksteps = (dk + 31) / 32, gpt = 16 * (dk / 8 < 4 ? dk / 8 : 4);
+    return ((((row >> 4) * ksteps + (k >> 5)) * gpt + ((k >> 3) & 3) * 16 + (row & 15)) << 3) + (k & 7);
+}
 
 // Bytes of dynamic LDS the chunk kernel needs (0 if the shape does not fit).
 size_t chunk_lds_bytes(bool bf16, int dk, int chunk, int dv_block);

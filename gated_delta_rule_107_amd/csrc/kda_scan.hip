@@ -13,15 +13,18 @@
 //
 // The step chain is latency-bound, so nothing but the product sits on it:
 //   * M_i arrives already split (the segment pass writes its high and low bf16
-//     planes) and is copied from HBM straight into LDS (global_load_lds, 16 bytes
-//     per lane) one step ahead, into the other of two buffers, with an XOR
-//     swizzle of its 16-byte granules so that the A-operand reads are free of
-//     bank conflicts; S_loc_i is prefetched into registers one step ahead;
+//     planes); each wave loads its 16 rows of it from global memory straight into
+//     registers in the MFMA's A-operand layout, one step ahead (the transitions do
+//     not depend on the chain), so the transition costs no LDS traffic or space;
+//     S_loc_i is prefetched into registers one step ahead;
 //   * the new start state is split once, by the wave that produced it, into
 //     transposed bf16 high / low copies in LDS that every wave reads as its MFMA
-//     B operand with 16-byte loads;
-//   * one extra wave copies each start state (an fp32 copy in LDS) to HBM, so the
-//     product waves' memory counter only tracks their own loads.
+//     B operand with 16-byte loads; they are double-buffered, so a step needs one
+//     barrier;
+//   * one extra wave copies each start state (a row-major fp32 copy in LDS) to HBM,
+//     so the product waves' memory counter only tracks their own loads.
+// A step is bounded by the vector-memory path of the CU: each workgroup needs all of M_i
+// (64 KiB, both planes) per step for its 16 columns.
 // starts[0] receives a copy of S0 (or zeros), so the pass that follows never reads
 // S0 itself (S0 may alias the final state).
 #include "kda_device.h"
@@ -30,29 +33,24 @@
 namespace kda {
 
 // Workgroup barrier for LDS traffic only.  __syncthreads() also carries a workgroup
-// release fence, which waits for every vector-memory operation in flight, the
-// transition copy into LDS included; this barrier waits for this wave's own LDS
-// accesses (lgkmcnt) and, in lds_vm_barrier, for its vector-memory operations.
+// release fence, which waits for every vector-memory operation in flight, the transition
+// loads of the next step included; this barrier waits for this wave's own LDS accesses
+// (lgkmcnt) only.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-__device__ __forceinline__ void lds_vm_barrier() {
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
+
+template <bool V> struct Set { static constexpr bool value = V; };
 
 template <int DK>
 __global__ __launch_bounds__(64 * (DK / 16 + 1)) void scan_kernel(ScanArgs a) {
     constexpr int NW = DK / 16;                   // product waves: one 16-row tile of the state each
     constexpr int KSTEP = (DK + 31) / 32;         // 32-deep MFMA steps over the contraction
     constexpr int LDB = 32 * KSTEP + 8;           // bf16 pitch of the transposed split copies
-    constexpr int LDF = DK + 4;                   // fp32 pitch of the transposed copy (store wave)
-    constexpr int NG = DK / 8;                    // 16-byte granules per row of one plane
-    constexpr int NGX = NG < 8 ? NG : 8;          // swizzle period
-    constexpr int GM = 2 * DK * NG;               // granules of one transition (two planes)
-    constexpr int NI = GM / 64 / NW;              // copy instructions per product wave
-    static_assert(NI * 64 * NW == GM, "transition copy map");
-    __shared__ __attribute__((aligned(16))) bf16 s_hi[16 * LDB];
-    __shared__ __attribute__((aligned(16))) bf16 s_lo[16 * LDB];
-    __shared__ __attribute__((aligned(16))) float s_f[16 * LDF];
-    __shared__ bf16x8 s_m[2 * GM];                // two transition buffers, swizzled granules
+    constexpr int LDR = 20;                       // fp32 pitch of the row-major copy (store wave)
+    // the start state of step i in buffer i & 1: split bf16 copies (transposed) for the
+    // products, a row-major fp32 copy for the store wave
+    __shared__ __attribute__((aligned(16))) bf16 s_hi[2][16 * LDB];
+    __shared__ __attribute__((aligned(16))) bf16 s_lo[2][16 * LDB];
+    __shared__ __attribute__((aligned(16))) float s_f[2][DK * LDR];
 
     // The column tiles of one (batch, head) are 8 block indices apart, so they run on one
     // XCD (workgroups go round-robin over the 8 XCDs) and share its L2 copy of M_i.
@@ -79,119 +77,132 @@ __global__ __launch_bounds__(64 * (DK / 16 + 1)) void scan_kernel(ScanArgs a) {
     const bool storer = w == NW;
 
     // contraction rows past DK (DK = 16) must read as zeros
-    for (int i = threadIdx.x; i < 16 * LDB; i += 64 * (NW + 1)) {
-        s_hi[i] = (bf16)0.f;
-        s_lo[i] = (bf16)0.f;
+    for (int i = threadIdx.x; i < 2 * 16 * LDB; i += 64 * (NW + 1)) {
+        (&s_hi[0][0])[i] = (bf16)0.f;
+        (&s_lo[0][0])[i] = (bf16)0.f;
     }
     lds_barrier();
 
-    // publish rows row0 + 4g .. +3 of column m: fp32 for the store wave, split bf16 for the products
-    auto put = [&](const f32x4& x) {
-        *reinterpret_cast<f32x4*>(s_f + m * LDF + row0 + 4 * g) = x;
+    // publish rows row0 + 4g .. +3 of column m into buffer b: fp32 for the store wave, split
+    // bf16 for the products
+    auto put = [&](const f32x4& x, int b) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s_f[b][(row0 + 4 * g + r) * LDR + m] = x[r];
         bf16x4 hi, lo;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             hi[j] = (bf16)x[j];
             lo[j] = (bf16)(x[j] - (float)hi[j]);
         }
-        *reinterpret_cast<bf16x4*>(s_hi + m * LDB + row0 + 4 * g) = hi;
-        *reinterpret_cast<bf16x4*>(s_lo + m * LDB + row0 + 4 * g) = lo;
+        *reinterpret_cast<bf16x4*>(s_hi[b] + m * LDB + row0 + 4 * g) = hi;
+        *reinterpret_cast<bf16x4*>(s_lo[b] + m * LDB + row0 + 4 * g) = lo;
     };
 
-    // the store wave writes start state i (in s_f) to starts[i]; rows spread over lanes
+    // the store wave writes start state i (in s_f[i & 1]) to starts[i]: 16 bytes of a row
+    // per lane, read as one piece from the row-major copy
     auto store_start = [&](int i) {
+        const float* f = s_f[i & 1];
         float* dst = a.starts + (bh * P + i) * DK * dv + 16 * jb;
+        // every read first, then the stores: one LDS round trip per step, not one per store
+        f32x4 v[DK / 16];
 #pragma unroll
         for (int it = 0; it < DK / 16; ++it) {                    // (row, column quad) pairs
             const int e = lane + 64 * it, row = e >> 2, cq = e & 3;
-            f32x4 v;
+            v[it] = *reinterpret_cast<const f32x4*>(f + row * LDR + 4 * cq);
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) v[j] = s_f[(4 * cq + j) * LDF + row];
-            *reinterpret_cast<f32x4*>(dst + (int64_t)row * dv + 4 * cq) = v;
+        for (int it = 0; it < DK / 16; ++it) {
+            const int e = lane + 64 * it, row = e >> 2, cq = e & 3;
+            *reinterpret_cast<f32x4*>(dst + (int64_t)row * dv + 4 * cq) = v[it];
         }
     };
 
-    if (!storer) {
+    // One barrier per step: the start states are double-buffered, so step i's products read
+    // buffer i & 1 while the new state goes to the other buffer, which every wave finished
+    // reading before this step's barrier (and the store wave before it, too).
+    const int nsteps = P - 1;
+    if (storer) {
+        for (int i = 0; i < P; ++i) {
+            lds_barrier();                        // LDS holds the start of segment i
+            store_start(i);
+        }
+        return;
+    }
+
+    {
         f32x4 cur;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             cur[r] = a.s0 ? a.s0[bh * DK * dv + (int64_t)(row0 + 4 * g + r) * dv + col] : 0.f;
-        put(cur);
+        put(cur, 0);
     }
 
-    // LDS granule q of a buffer holds granule c = (q % NG) ^ (r % NGX) of row r = (q / NG) % DK
-    // of plane q / (DK NG); this lane copies granules (w NI + j) 64 + lane, j < NI
-    const bf16* mt = reinterpret_cast<const bf16*>(a.m_tr);    // [B*H][P][2][DK][DK]
-    unsigned src_off[NI];                                        // bf16 offsets inside one M_i
-#pragma unroll
-    for (int j = 0; j < NI; ++j) {
-        const int q = (w * NI + j) * 64 + lane;
-        const int pl = q / (DK * NG), r = (q / NG) % DK, c = (q % NG) ^ (r % NGX);
-        src_off[j] = (unsigned)((pl * DK + r) * DK + c * 8);
-    }
-    auto copy_m = [&](int i, int buf) {
+    // The A operand (this wave's 16 rows of M_i, high and low planes) goes from global memory
+    // straight into registers in the MFMA's layout (one contiguous 1 KiB run per load, as pass
+    // 1 stores the transitions in that order), one step ahead into the register set of i's
+    // parity: every transition is known before the chain starts, and no LDS traffic or buffer
+    // is spent on them.  The loads are issued on every step (the last transition is re-read
+    // past the end), so the compiler counts them exactly and a step waits only for the loads
+    // of the step before (a load under a branch makes it wait for all of them).
+    const bf16* mt = reinterpret_cast<const bf16*>(a.m_tr);    // [B*H][P][2][DK^2], mtr_index order
+    bf16x8 ma0[2][KSTEP], ma1[2][KSTEP];                        // [plane][step] of M_i: even / odd i
+    f32x4 sl0, sl1;                                             // S_loc_i: even / odd i
+    auto load_m = [&](int i, bf16x8 (&dst)[2][KSTEP]) {
         const bf16* M = mt + (bh * P + i) * 2 * DK * DK;
 #pragma unroll
-        for (int j = 0; j < NI; ++j)
-            copy16_global_to_lds(M + src_off[j], s_m + buf * GM + (w * NI + j) * 64);
+        for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+            for (int t = 0; t < KSTEP; ++t) {
+                const int k0 = 32 * t + 8 * g;
+                dst[pl][t] = k0 < DK ? *reinterpret_cast<const bf16x8*>(M + pl * DK * DK + mtr_index(DK, row0 + m, k0))
+                                     : bf16x8{};
+            }
     };
-    auto a_granule = [&](int buf, int pl, int r, int c) -> bf16x8 {
-        return s_m[buf * GM + (pl * DK + r) * NG + (c ^ (r % NGX))];
-    };
-    f32x4 sl;
-    auto load_sloc = [&](int i) {
+    auto load_sloc = [&](int i, f32x4& dst) {
         const float* L = a.s_loc + (bh * P + i) * DK * dv;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sl[r] = L[(int64_t)(row0 + 4 * g + r) * dv + col];
+        for (int r = 0; r < 4; ++r) dst[r] = L[(int64_t)(row0 + 4 * g + r) * dv + col];
     };
-    const int nsteps = P - 1;
-
-    // The store wave and the product waves run separate loops with the same barriers.
-    if (storer) {
-        for (int i = 0; i < nsteps; ++i) {
-            lds_barrier();                        // LDS holds the start of segment i
-            store_start(i);
-            lds_barrier();
-        }
-        lds_barrier();
-        store_start(P - 1);
-        return;
-    }
     if (nsteps > 0) {
-        copy_m(0, 0);
-        load_sloc(0);
+        load_m(0, ma0);
+        load_sloc(0, sl0);
     }
-    for (int i = 0; i < nsteps; ++i) {
-        const int buf = i & 1;
-        lds_vm_barrier();                         // every share of M_i landed; LDS holds start i
-        // operands into registers first, then the next transition's copy into the other buffer
-        bf16x8 ah[KSTEP], al[KSTEP], bh8[KSTEP], bl8[KSTEP];
+    auto step = [&](int i, auto odd_c) {
+        constexpr bool odd = decltype(odd_c)::value;
+        const int b = odd ? 1 : 0;
+        lds_barrier();                            // LDS holds start i in buffer b
+        // the next step's loads first (kept here by the scheduling barrier: the scheduler would
+        // otherwise sink them below this step's products), then this step's B operands
+        const int nx = i + 1 < nsteps ? i + 1 : nsteps - 1;
+        if (odd) { load_m(nx, ma0); load_sloc(nx, sl0); }
+        else { load_m(nx, ma1); load_sloc(nx, sl1); }
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 bh8[KSTEP], bl8[KSTEP];
 #pragma unroll
         for (int t = 0; t < KSTEP; ++t) {
-            const int c = 4 * t + g;
-            const bool in = 8 * c < DK;
-            const int r = row0 + m;
-            ah[t] = in ? a_granule(buf, 0, r, c) : bf16x8{};
-            al[t] = in ? a_granule(buf, 1, r, c) : bf16x8{};
-            bh8[t] = *reinterpret_cast<const bf16x8*>(s_hi + m * LDB + 32 * t + 8 * g);
-            bl8[t] = *reinterpret_cast<const bf16x8*>(s_lo + m * LDB + 32 * t + 8 * g);
+            bh8[t] = *reinterpret_cast<const bf16x8*>(s_hi[b] + m * LDB + 32 * t + 8 * g);
+            bl8[t] = *reinterpret_cast<const bf16x8*>(s_lo[b] + m * LDB + 32 * t + 8 * g);
         }
-        const f32x4 acc0 = sl;
-        if (i + 1 < nsteps) {
-            copy_m(i + 1, buf ^ 1);
-            load_sloc(i + 1);
-        }
-        f32x4 acc = acc0, acc2 = {0.f, 0.f, 0.f, 0.f};
+        const bf16x8 (&ma)[2][KSTEP] = odd ? ma1 : ma0;
+        // hi*hi, hi*lo and lo*hi in three independent accumulator chains (the dependent chain
+        // is the step's latency)
+        f32x4 acc = odd ? sl1 : sl0, acc2 = {0.f, 0.f, 0.f, 0.f}, acc3 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < KSTEP; ++t) {
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[t], bh8[t], acc, 0, 0, 0);
-            acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[t], bl8[t], acc2, 0, 0, 0);
-            acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[t], bh8[t], acc2, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ma[0][t], bh8[t], acc, 0, 0, 0);
+            acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ma[0][t], bl8[t], acc2, 0, 0, 0);
+            acc3 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ma[1][t], bh8[t], acc3, 0, 0, 0);
         }
-        lds_barrier();                            // every wave has read start i and M_i
-        put(acc + acc2);
+        put(acc + (acc2 + acc3), b ^ 1);
+    };
+    int i = 0;
+    for (; i + 1 < nsteps; i += 2) {
+        step(i, Set<false>{});
+        step(i + 1, Set<true>{});
     }
-    lds_barrier();
+    if (i < nsteps) step(i, Set<false>{});
+    lds_barrier();                                // the last start is in LDS for the store wave
 }
 
 template <int DK>
