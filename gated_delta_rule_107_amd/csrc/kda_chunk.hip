@@ -110,6 +110,28 @@ template <> struct MM<bf16> {
         const bf16x8 b = *reinterpret_cast<const bf16x8*>(Bm + (rb + (lane & 15)) * ldb + k0 + 8 * (lane >> 4));
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
     }
+    // two products that share the right operand (an A tile and the M tile of the same
+    // sub-tile pair), which is read once
+    static __device__ __forceinline__ void nat2(const bf16* A1, const bf16* A2, int lda, int ra, const bf16* Bm,
+                                                int ldb, int rb, int k0, const float* fac, f32x4& acc1,
+                                                f32x4& acc2, int lane) {
+        const bf16x8 b = *reinterpret_cast<const bf16x8*>(Bm + (rb + (lane & 15)) * ldb + k0 + 8 * (lane >> 4));
+        bf16x8 a1 = *reinterpret_cast<const bf16x8*>(A1 + (ra + (lane & 15)) * lda + k0 + 8 * (lane >> 4));
+        bf16x8 a2 = *reinterpret_cast<const bf16x8*>(A2 + (ra + (lane & 15)) * lda + k0 + 8 * (lane >> 4));
+        if (fac) {
+            const f32x4* f4 = reinterpret_cast<const f32x4*>(fac + k0 + 8 * (lane >> 4));
+            const f32x4 lo = f4[0], hi = f4[1];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                a1[j] = (bf16)((float)a1[j] * lo[j]);
+                a1[4 + j] = (bf16)((float)a1[4 + j] * hi[j]);
+                a2[j] = (bf16)((float)a2[j] * lo[j]);
+                a2[4 + j] = (bf16)((float)a2[4 + j] * hi[j]);
+            }
+        }
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b, acc1, 0, 0, 0);
+        acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2, b, acc2, 0, 0, 0);
+    }
 };
 
 template <> struct MM<float> {
@@ -147,6 +169,20 @@ template <> struct MM<float> {
         if (fac) a *= fac[k0 + (lane >> 4)];
         const float b = Bm[(rb + (lane & 15)) * ldb + k0 + (lane >> 4)];
         return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+    }
+    static __device__ __forceinline__ void nat2(const float* A1, const float* A2, int lda, int ra, const float* Bm,
+                                                int ldb, int rb, int k0, const float* fac, f32x4& acc1,
+                                                f32x4& acc2, int lane) {
+        const float b = Bm[(rb + (lane & 15)) * ldb + k0 + (lane >> 4)];
+        float a1 = A1[(ra + (lane & 15)) * lda + k0 + (lane >> 4)];
+        float a2 = A2[(ra + (lane & 15)) * lda + k0 + (lane >> 4)];
+        if (fac) {
+            const float f = fac[k0 + (lane >> 4)];
+            a1 *= f;
+            a2 *= f;
+        }
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b, acc1, 0, 0, 0);
+        acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(a2, b, acc2, 0, 0, 0);
     }
 };
 
@@ -861,22 +897,21 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
                     }
                 }
             }
-            // up to 3 tile tasks per wave; every task's loads and products come before any
-            // of the wave's stores
+            // Tile tasks: sub-tile pairs (p, pp <= p), row by row.  With outputs, a task computes
+            // the A tile and the M tile of its pair, which share the right operand (read once);
+            // every task's loads and products come before any of the wave's stores.
             constexpr int NPAIR = NT * (NT + 1) / 2;
-            constexpr int NTASK = want_o ? 2 * NPAIR : NPAIR;
-            constexpr int NSLOT = (NTASK + 7) / 8;
-            f32x4 acc[NSLOT];
+            constexpr int NSLOT = (NPAIR + 7) / 8;
+            f32x4 acc[NSLOT], accm[NSLOT];
 #pragma unroll
             for (int sl = 0; sl < NSLOT; ++sl) {
                 const int task = wave + 8 * sl;
                 acc[sl] = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (task < NTASK) {
-                    const bool isM = task >= NPAIR;
-                    int pr = isM ? task - NPAIR : task, p = 0;
+                accm[sl] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (task < NPAIR) {
+                    int pr = task, p = 0;
                     while (pr > p) { pr -= p + 1; ++p; }
                     const int pp = pr;                                // pp <= p
-                    const OpT* left = isM ? s_ql : s_kl;
                     const OpT* right = s_rh;
                     int rrow = 16 * pp;
                     const float* fac = nullptr;
@@ -888,19 +923,22 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
                         fac = p == pp ? s_fd + p * DKP : (p - pp >= 2 ? s_fo + pair_fo_index(p, pp) * DKP : nullptr);
                     }
 #pragma unroll
-                    for (int ks = 0; ks < KNAT; ++ks)
-                        acc[sl] = MF::nat(left, LDK, 16 * p, right, LDK, rrow, ks * MF::KS, fac, acc[sl], lane);
+                    for (int ks = 0; ks < KNAT; ++ks) {
+                        if constexpr (want_o)
+                            MF::nat2(s_kl, s_ql, LDK, 16 * p, right, LDK, rrow, ks * MF::KS, fac, acc[sl], accm[sl], lane);
+                        else
+                            acc[sl] = MF::nat(s_kl, LDK, 16 * p, right, LDK, rrow, ks * MF::KS, fac, acc[sl], lane);
+                    }
                 }
             }
 #pragma unroll
             for (int sl = 0; sl < NSLOT; ++sl) {
                 const int task = wave + 8 * sl;
-                if (task < NTASK) {
-                    const bool isM = task >= NPAIR;
-                    int pr = isM ? task - NPAIR : task, p = 0;
+                if (task < NPAIR) {
+                    int pr = task, p = 0;
                     while (pr > p) { pr -= p + 1; ++p; }
                     const int pp = pr;
-                    if (!isM && p == pp) {
+                    if (p == pp) {
                         // diagonal block of beta A, strictly lower, stored transposed: [p][s][t]
                         f32x4 col;
 #pragma unroll
@@ -909,10 +947,16 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
                     } else {
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
+                            const int t = 16 * p + g4 + r, s = 16 * pp + jl;
+                            s_an[t * LC + s] = from_f32<OpT>(-acc[sl][r] * sb_n[t]);
+                        }
+                    }
+                    if constexpr (want_o) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
                             const int tr = g4 + r;
                             const int t = 16 * p + tr, s = 16 * pp + jl;
-                            if (!isM) s_an[t * LC + s] = from_f32<OpT>(-acc[sl][r] * sb_n[t]);
-                            else s_mm[t * LC + s] = from_f32<OpT>((p == pp && jl > tr) ? 0.f : acc[sl][r]);
+                            s_mm[t * LC + s] = from_f32<OpT>((p == pp && jl > tr) ? 0.f : accm[sl][r]);
                         }
                     }
                 }
