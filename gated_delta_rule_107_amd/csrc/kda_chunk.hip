@@ -381,7 +381,6 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
     const int colw = (int)cb * DVB + 16 * wave;      // first (virtual) column of this wave
     const bool chain = 16 * wave < DVB;              // this wave owns state columns
     const bool mcols = MODE == 1 && colw >= dv;      // ... transition columns (start I, V = 0)
-    const bool vcols = chain && !mcols;              // ... value columns (read v, write o)
 
     const OpT* gq = reinterpret_cast<const OpT*>(a.q);
     const OpT* gk = reinterpret_cast<const OpT*>(a.k);
@@ -740,7 +739,6 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
                 }
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const int t = 4 * tq + j;
                     // tokens past the end keep their (clamped, finite) k and q: their beta is 0
                     // and their log-decay 0, so they change neither U, O nor the state
                     float k[4][4], q[4][4];
