@@ -1031,7 +1031,11 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
         if (MODE == 0) {
             if (seg == a.n_seg - 1) { dst = a.s_final + bh * DK * dv; ld = dv; }
         } else if (!mcols) {
-            dst = a.s_loc + (bh * a.n_seg + seg) * DK * dv; ld = dv;
+            // the zero-start state goes to the scan in its accumulator-tile order
+            float* sl = a.s_loc + (bh * a.n_seg + seg) * DK * dv;
+#pragma unroll
+            for (int tau = 0; tau < NCT; ++tau)
+                *reinterpret_cast<f32x4*>(sl + sloc_index(DK, 16 * tau + g4, col)) = Sacc[tau];
         } else {
             // the transition goes to the scan already split into bf16 high and low planes, in
             // the order of the scan's A operand

@@ -45,7 +45,7 @@ struct ChunkArgs {
     const float* starts;    // [B,H,P,dk,dv] start state of every segment (mode 0, n_seg > 1)
     void* o;                // [B,T,H,dv] (mode 0)
     float* s_final;         // [B,H,dk,dv] (mode 0)
-    float* s_loc;           // [B,H,P,dk,dv] (mode 1)
+    float* s_loc;           // [B,H,P][dk dv] (mode 1), each block in sloc_index order
     void* m_tr;             // [B,H,P][2][dk^2] bf16 (mode 1): M split into high and low parts,
                             // each plane in the scan's operand order (mtr_index)
     int64_t B, T;           // with cu_seqlens: B = number of sequences, T = packed tokens
@@ -67,7 +67,7 @@ hipError_t launch_chunk(const ChunkArgs& a, hipStream_t st);
 // starts[0] = s0 (or zeros); writes starts[1 .. P-1].
 struct ScanArgs {
     const float* s0;
-    const float* s_loc;
+    const float* s_loc;     // [B,H,P][dk dv], sloc_index order
     const void* m_tr;       // [B,H,P][2][dk^2] bf16: high and low parts of M (hi + lo ~ M), mtr_index order
     float* starts;
     int64_t B;
@@ -81,6 +81,14 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t st);
 // bytes.  Mixed radix (16-row tile, 32-deep contraction step, granule g * 16 + m, element),
 // where granule (g, m) holds columns 32 t + 8 g .. +7 of row 16 w + m; a (tile, step) pair has
 // 16 min(4, dk / 8) granules, so the plane holds exactly dk^2 elements.
+// Position of S_loc[row][col] inside one segment's dk x dv block: the order of the accumulator
+// tiles (16-column tile, 16-row tile, lane g * 16 + m, element r for row 16 w + 4 g + r, column
+// 16 j + m), so that the segment pass stores, and the scan loads, a lane's four rows as one
+// 16-byte piece and a wave's tile as one contiguous 1 KiB run.
+__host__ __device__ constexpr int sloc_index(int dk, int row, int col) {
+    return (((col >> 4) * (dk >> 4) + (row >> 4)) * 64 + ((row >> 2) & 3) * 16 + (col & 15)) * 4 + (row & 3);
+}
+
 __host__ __device__ constexpr int mtr_index(int dk, int row, int k) {
     const int ksteps = (dk + 31) / 32, gpt = 16 * (dk / 8 < 4 ? dk / 8 : 4);
     return ((((row >> 4) * ksteps + (k >> 5)) * gpt + ((k >> 3) & 3) * 16 + (row & 15)) << 3) + (k & 7);

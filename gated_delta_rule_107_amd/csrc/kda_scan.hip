@@ -160,9 +160,8 @@ __global__ __launch_bounds__(64 * (DK / 16 + 1)) void scan_kernel(ScanArgs a) {
             }
     };
     auto load_sloc = [&](int i, f32x4& dst) {
-        const float* L = a.s_loc + (bh * P + i) * DK * dv;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dst[r] = L[(int64_t)(row0 + 4 * g + r) * dv + col];
+        const float* L = a.s_loc + (bh * P + i) * DK * dv;        // sloc_index order
+        dst = *reinterpret_cast<const f32x4*>(L + sloc_index(DK, row0 + 4 * g, col));
     };
     if (nsteps > 0) {
         load_m(0, ma0);
