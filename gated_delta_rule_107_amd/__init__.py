@@ -22,7 +22,7 @@ import os
 
 import torch
 
-__all__ = ["KdaError", "Plan", "chunk_fwd", "decode_step", "decode_verify", "decode_commit",
+__all__ = ["KdaError", "Plan", "chunk_fwd", "chunk_fwd_noalloc", "decode_step", "decode_verify", "decode_commit",
            "default_plan", "workspace_bytes", "library_path", "ERRORS", "GATE_LOG_DECAY", "GATE_LOGITS"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -61,6 +61,9 @@ def _load():
     lib.kda_chunk_fwd.restype = i32
     lib.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, i32,
                                   ctypes.POINTER(Plan), vp, sz, vp]
+    lib.kda_chunk_fwd_noalloc.restype = i32
+    lib.kda_chunk_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, i32,
+                                          ctypes.POINTER(Plan), vp]
     lib.kda_decode_step.restype = i32
     u32 = ctypes.c_uint32
     lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, u32, vp]
@@ -238,6 +241,34 @@ def chunk_fwd(q, k, v, log_alpha, beta, S0=None, chunk: int = 64, plan: Plan | N
     _check(code)
     if ckpt_stride:
         return o, S_T, state_ckpt
+    return o, S_T
+
+
+def chunk_fwd_noalloc(q, k, v, log_alpha, beta, S0, o, S_T, chunk: int = 64, plan: Plan | None = None):
+    """kda_chunk_fwd_noalloc: chunked prefill into caller-given ``o`` and ``S_T``, with the
+    segment workspace held by the library (KDA_NOALLOC_SCRATCH_BYTES per GPU) instead of
+    passed in.  Allocates nothing.  Plans needing more workspace raise KDA_ERR_WORKSPACE.
+    Calls that may overlap in time on one GPU share that workspace and race."""
+    if q.dim() != 4:
+        raise KdaError(2, "q must be [B,T,H,dk]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise KdaError(2, "tensors must be on a GPU")
+    dt = _dtype_code(q)
+    _require(q, "q", q.dtype, (B, T, H, dk), dev)
+    _require(k, "k", q.dtype, (B, T, H, dk), dev)
+    _require(v, "v", q.dtype, (B, T, H, dv), dev)
+    _require(log_alpha, "log_alpha", torch.float32, (B, T, H, dk), dev)
+    _require(beta, "beta", torch.float32, (B, T, H), dev)
+    if S0 is not None:
+        _require(S0, "S0", torch.float32, (B, H, dk, dv), dev)
+    _require(o, "o", q.dtype, (B, T, H, dv), dev)
+    _require(S_T, "S_T", torch.float32, (B, H, dk, dv), dev)
+    _check(lib().kda_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0),
+                                      _ptr(o), _ptr(S_T), B, T, H, dk, dv, chunk, dt,
+                                      ctypes.byref(plan) if plan is not None else None, _stream(dev)))
     return o, S_T
 
 

@@ -190,11 +190,48 @@ kda_status_t kda_chunk_fwd_workspace_bytes(int64_t B, int64_t T, int32_t H, int3
     return KDA_OK;
 }
 
-kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
-                           const float* beta, const float* S0, void* o, float* S_T, int64_t B,
-                           int64_t T, int32_t H, int32_t dk, int32_t dv, int32_t chunk,
-                           kda_dtype_t dt, const kda_plan_t* plan, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Segment workspace of kda_chunk_fwd_noalloc: device memory the library owns, so that callers
+// that cannot allocate need not pass any.  Every GPU the library runs on holds its own copy
+// until the process ends; host code uses only the per-device address from scratch_address(),
+// never this name.
+static __device__ __align__(256) unsigned char scratch[KDA_NOALLOC_SCRATCH_BYTES];
+
+// Address of the current device's copy of `scratch`, looked up once per device (with that
+// device current) and kept; null with a message on failure.
+void* scratch_address() {
+    static std::mutex mu;
+    static std::vector<void*> addr;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        hip_fail(e, "hipGetDevice");
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lk(mu);
+    if ((int)addr.size() <= dev) addr.resize(dev + 1, nullptr);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+            return nullptr;
+        }
+        addr[dev] = p;
+    }
+    return addr[dev];
+}
+
+// kda_chunk_fwd and kda_chunk_fwd_noalloc: with `library_scratch` the segment workspace is the
+// library's own array (workspace / workspace_bytes are ignored).
+kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, const float* log_alpha,
+                            const float* beta, const float* S0, void* o, float* S_T, int64_t B,
+                            int64_t T, int32_t H, int32_t dk, int32_t dv, int32_t chunk,
+                            kda_dtype_t dt, const kda_plan_t* plan, void* workspace,
+                            size_t workspace_bytes, void* stream, bool library_scratch) {
     kda_status_t s = check_problem(B, T, H, dk, dv, chunk, dt);
     if (s != KDA_OK) return s;
     if (!S_T) return fail(KDA_ERR_NULL, "S_T is NULL");
@@ -222,8 +259,15 @@ kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v, const fl
     s = resolve_plan(B, T, H, dk, dv, chunk, dt, plan, &r);
     if (s != KDA_OK) return s;
     const size_t need = workspace_for(B, H, dk, dv, r);
-    if (need > 0 && (!workspace || workspace_bytes < need))
+    if (library_scratch) {
+        if (need > KDA_NOALLOC_SCRATCH_BYTES)
+            return fail(KDA_ERR_WORKSPACE, "this plan needs %zu bytes of segment workspace; the library holds %zu",
+                        need, (size_t)KDA_NOALLOC_SCRATCH_BYTES);
+        workspace = nullptr;
+        workspace_bytes = 0;
+    } else if (need > 0 && (!workspace || workspace_bytes < need)) {
         return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : (size_t)0);
+    }
 
     const size_t es = dt == KDA_DTYPE_BF16 ? 2 : 4;
     const size_t n_qk = (size_t)(B * T * H) * dk, n_v = (size_t)(B * T * H) * dv;
@@ -252,6 +296,10 @@ kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v, const fl
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     if (plan && plan->launch_events && plan->n_launch_events < 0)
         return fail(KDA_ERR_UNSUPPORTED, "n_launch_events must be >= 0");
+    if (library_scratch && need > 0) {
+        workspace = scratch_address();
+        if (!workspace) return KDA_ERR_HIP;
+    }
     LaunchEvents tm{plan ? plan->launch_events : nullptr, plan ? plan->n_launch_events : 0, 0, st};
     kda::ChunkArgs a{};
     a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta;
@@ -301,6 +349,27 @@ kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v, const fl
     tm.after();
     if (e != hipSuccess) return hip_fail(e, "segment pass-2 launch");
     return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
+                           const float* beta, const float* S0, void* o, float* S_T, int64_t B,
+                           int64_t T, int32_t H, int32_t dk, int32_t dv, int32_t chunk,
+                           kda_dtype_t dt, const kda_plan_t* plan, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    return chunk_fwd_impl(q, k, v, log_alpha, beta, S0, o, S_T, B, T, H, dk, dv, chunk, dt, plan, workspace,
+                          workspace_bytes, stream, false);
+}
+
+kda_status_t kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const float* log_alpha,
+                                   const float* beta, const float* S0, void* o, float* S_T, int64_t B,
+                                   int64_t T, int32_t H, int32_t dk, int32_t dv, int32_t chunk,
+                                   kda_dtype_t dt, const kda_plan_t* plan, void* stream) {
+    return chunk_fwd_impl(q, k, v, log_alpha, beta, S0, o, S_T, B, T, H, dk, dv, chunk, dt, plan, nullptr, 0,
+                          stream, true);
 }
 
 }  // extern "C"

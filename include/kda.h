@@ -169,6 +169,35 @@ kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v,
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * kda_chunk_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, serving loops and harnesses that forbid hipMalloc.  Same
+ * arguments, meaning and errors as kda_chunk_fwd except that there is no
+ * workspace argument: a segmented plan uses a segment workspace the library
+ * owns, one array of KDA_NOALLOC_SCRATCH_BYTES per GPU, kept until the
+ * process ends.  The call itself allocates nothing.
+ *
+ * - A plan whose segment workspace (kda_chunk_fwd_workspace_bytes) exceeds
+ *   KDA_NOALLOC_SCRATCH_BYTES is rejected with KDA_ERR_WORKSPACE before any
+ *   HIP call.  The default plans of B=1, T=4096, H=16 and of B=1,
+ *   T=1,048,576, H=32 (dk = dv = 128) need 48 MiB.
+ * - On the first call on a device that needs the array, the library looks up
+ *   its address on that device (hipGetSymbolAddress); a failure there returns
+ *   KDA_ERR_HIP.
+ * - Every call on one GPU shares that GPU's array: calls that may overlap in
+ *   time on one GPU (different streams, different host threads) race and give
+ *   undefined results.  Calls ordered on one stream are safe.  No part of the
+ *   array needs to start at zero: a call reads only what it wrote earlier.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+kda_status_t kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v,
+                                   const float* log_alpha, const float* beta, const float* S0,
+                                   void* o, float* S_T,
+                                   int64_t B, int64_t T, int32_t H, int32_t dk, int32_t dv,
+                                   int32_t chunk, kda_dtype_t dt, const kda_plan_t* plan,
+                                   void* stream);
+
+/*
  * One recurrent decode step for N independent sequences, state updated in
  * place (orkas.ai "Kimi K3 architecture", section "The cost comes back in the
  * serving stack": the state is updated in place).  Equivalent to
