@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
+#include <cstdlib>
 #include <cstdio>
 #include <cstring>
 #include <mutex>
@@ -32,26 +33,19 @@ bool chunk_ok(int32_t c) { return c == 16 || c == 32 || c == 64; }
 bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 constexpr uint32_t kAllFlags = KDA_GATE_LOGITS | KDA_QK_L2NORM;
 
-// Compute units of the current device, cached per device; 256 (MI355X) if no device is visible.
-int device_cus() {
-    static std::mutex mu;
-    static std::vector<int> cache;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) {
-        (void)hipGetLastError();
-        return 256;
-    }
-    std::lock_guard<std::mutex> lk(mu);
-    if ((int)cache.size() <= dev) cache.resize(dev + 1, 0);
-    if (cache[dev] == 0) {
-        int cus = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
-            (void)hipGetLastError();
-            cus = 256;
-        }
-        cache[dev] = cus;
-    }
-    return cache[dev];
+// Compute units the default plan is sized for: MI355X (gfx950) has 256.  A constant, not a
+// device query: the default plan, and with it the rounding of the results, is the same on
+// every device, and no HIP call is needed before the arguments are validated.  Callers on a
+// partitioned device pass n_segments themselves.
+constexpr int64_t kPlanCUs = 256;
+
+// KDA_TRACE=1 in the environment: every kda_chunk_fwd call prints its resolved plan to stderr.
+bool trace_on() {
+    static const bool on = [] {
+        const char* e = std::getenv("KDA_TRACE");
+        return e && *e && std::strcmp(e, "0") != 0;
+    }();
+    return on;
 }
 
 kda_status_t check_problem(int64_t B, int64_t T, int32_t H, int32_t dk, int32_t dv, int32_t chunk,
@@ -95,7 +89,7 @@ kda_status_t resolve_plan(int64_t B, int64_t T, int32_t H, int32_t dk, int32_t d
         // enough workgroups to cover every compute unit; segments only when (b, h, column
         // block) units alone cannot, and only if each segment keeps at least 2 chunks
         const int64_t units = B * H * (dv / dvb);
-        const int64_t cus = device_cus();
+        const int64_t cus = kPlanCUs;
         nseg = 1;
         if (units < cus && dk % dvb == 0) {
             nseg = (cus + units - 1) / units;
@@ -155,6 +149,7 @@ const char* kda_status_str(kda_status_t s) {
         case KDA_ERR_WORKSPACE: return "workspace too small";
         case KDA_ERR_HIP: return "HIP runtime error";
         case KDA_ERR_ALIAS: return "output overlaps an input";
+        default: break;
     }
     return "unknown status";
 }
@@ -194,35 +189,16 @@ kda_status_t kda_chunk_fwd_workspace_bytes(int64_t B, int64_t T, int32_t H, int3
 
 namespace {
 
-// Segment workspace of kda_chunk_fwd_noalloc: device memory the library owns, so that callers
-// that cannot allocate need not pass any.  Every GPU the library runs on holds its own copy
-// until the process ends; host code uses only the per-device address from scratch_address(),
-// never this name.
-static __device__ __align__(256) unsigned char scratch[KDA_NOALLOC_SCRATCH_BYTES];
-
-// Address of the current device's copy of `scratch`, looked up once per device (with that
-// device current) and kept; null with a message on failure.
+// Address of the current device's copy of the library's segment workspace (kda_scratch.hip),
+// or null with a message.
 void* scratch_address() {
-    static std::mutex mu;
-    static std::vector<void*> addr;
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
+    void* p = nullptr;
+    const hipError_t e = kda::scratch_address(&p);
     if (e != hipSuccess) {
-        hip_fail(e, "hipGetDevice");
+        hip_fail(e, "segment workspace address");
         return nullptr;
     }
-    std::lock_guard<std::mutex> lk(mu);
-    if ((int)addr.size() <= dev) addr.resize(dev + 1, nullptr);
-    if (!addr[dev]) {
-        void* p = nullptr;
-        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
-        if (e != hipSuccess || !p) {
-            hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
-            return nullptr;
-        }
-        addr[dev] = p;
-    }
-    return addr[dev];
+    return p;
 }
 
 // kda_chunk_fwd and kda_chunk_fwd_noalloc: with `library_scratch` the segment workspace is the
@@ -311,6 +287,16 @@ kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, const f
     a.flags = flags;
     if (cu) a.B = n_seq;                      // units and state rows are sequences
     a.bf16 = dt == KDA_DTYPE_BF16;
+    if (trace_on()) {
+        std::fprintf(stderr,
+                     "kda_chunk_fwd%s: B=%lld T=%lld H=%d dk=%d dv=%d chunk=%d dtype=%s sequences=%lld "
+                     "n_segments=%d seg_len=%lld dv_block=%d workspace=%zu flags=0x%x checkpoints=%s "
+                     "launches=%s\n",
+                     library_scratch ? "_noalloc" : "", (long long)B, (long long)T, H, dk, dv, chunk,
+                     dt == KDA_DTYPE_BF16 ? "bf16" : "f32", (long long)n_seq, r.n_seg, (long long)r.seg_len,
+                     r.dv_block, need, flags, ckpt ? "yes" : "no",
+                     r.n_seg == 1 ? "chunk" : "segment-pass-1,scan,segment-pass-2");
+    }
     hipError_t e;
     if (r.n_seg == 1) {
         a.mode = 0;

@@ -40,6 +40,8 @@
 //
 // bf16 inputs use v_mfma_f32_16x16x32_bf16 / v_mfma_f32_16x16x16_bf16 with
 // fp32 accumulation; float32 inputs use v_mfma_f32_16x16x4_f32 throughout.
+#include <mutex>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -242,49 +244,6 @@ template <> struct Ld4<float> {
     static __device__ __forceinline__ V zero() { return V{0.f, 0.f, 0.f, 0.f}; }
 };
 
-// ---------------------------------------------------------------- LDS layout
-// bf16 operands (RV): the A / M tiles take their decay factors on the right operand, which
-// is stored in one variant per distance between the sub-tiles (RD for the diagonal, RH for
-// adjacent sub-tiles, RF for two and three apart).  float32 operands instead scale the left
-// operand in registers by per-channel factors (fd, fo), which keeps their LDS footprint small.
-struct Lds {
-    int kt, qt, kl, ql, rh, rd, rf, kht, an, mm, ad, fd, fo, egc, beta, total;
-};
-
-__host__ __device__ constexpr int align16(int x) { return (x + 15) & ~15; }
-
-// E: bytes per operand element
-__host__ __device__ constexpr Lds lds_layout(int E, int DK, int C) {
-    const bool RV = E == 2;
-    const int PADE = 16 / E;
-    const int NT = C / 16;
-    const int DKP = DK < 32 ? 32 : DK;            // bf16 natural loads read 32 channels at a time
-    const int LDK = DKP + PADE;
-    const int LKQ = DKP + 16 / E / (E == 2 ? 2 : 1);
-    const int LC = C + 16 / E / (E == 2 ? 2 : 1);
-    Lds L{};
-    int off = 0;
-    L.kt = off;   off += align16(C * LKQ * E);
-    L.qt = off;   off += align16(C * LKQ * E);
-    L.kl = off;   off += align16(C * LDK * E);
-    L.ql = off;   off += align16(C * LDK * E);
-    L.rh = off;   off += align16(C * LDK * E);
-    L.rd = off;   off += RV ? align16(C * LDK * E) : 0;
-    L.rf = off;   off += (RV && NT == 4) ? align16(48 * LDK * E) : 0;
-    // the Kt..RF region also holds the v staging tile (C rows, up to 128 columns)
-    if (off - L.kt < C * (128 + PADE) * E) off = L.kt + align16(C * (128 + PADE) * E);
-    L.kht = off;  off += align16(DK * LC * E);
-    L.an = off;   off += align16(C * LC * E);
-    L.mm = off;   off += align16(C * LC * E);
-    L.ad = off;   off += align16(NT * 16 * 16 * 4);
-    L.fd = off;   off += RV ? 0 : align16(NT * DKP * 4);
-    L.fo = off;   off += RV ? 0 : align16(3 * DKP * 4);
-    L.egc = off;  off += align16(2 * DKP * 4);   // two slots: chunk n and chunk n+1
-    L.beta = off; off += align16(2 * C * 4);
-    L.total = off;
-    return L;
-}
-
 __host__ __device__ constexpr int pair_fo_index(int p, int pp) {   // p - pp >= 2, p <= 3
     return p == 2 ? 0 : (pp == 0 ? 1 : 2);                          // (2,0) (3,0) (3,1)
 }
@@ -432,7 +391,7 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
         const OpT* k_b = gk + base;
         const OpT* q_b = gq + base;
         if (tlim == C - 1) {
-            unsigned off = __umul24(4 * tq, tok_k) + gc0;
+            unsigned off = tok_elem_off(4 * tq, tok_k, gc0);
 #pragma unroll
             for (int j = 0; j < 4; ++j, off += tok_k) {
                 pla[j] = *at_bytes(reinterpret_cast<const f32x4*>(la_b), off * 4u);
@@ -442,13 +401,13 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
         } else {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const unsigned off = __umul24(min(4 * tq + j, tlim), tok_k) + gc0;
+                const unsigned off = tok_elem_off(min(4 * tq + j, tlim), tok_k, gc0);
                 pla[j] = *at_bytes(reinterpret_cast<const f32x4*>(la_b), off * 4u);
                 pk[j] = *at_bytes(reinterpret_cast<const V4*>(k_b), off * (unsigned)E);
                 if (want_o) pq[j] = *at_bytes(reinterpret_cast<const V4*>(q_b), off * (unsigned)E);
             }
         }
-        if (tid < C) pbeta = *at_bytes(a.beta + (b * T + t0) * H + h, __umul24(min(tid, tlim), H) * 4u);
+        if (tid < C) pbeta = *at_bytes(a.beta + (b * T + t0) * H + h, tok_elem_off(min(tid, tlim), H, 0) * 4u);
     };
     // v for the chain as 16-byte granules (GPR per row); rows past the end read a clamped row
     // and are multiplied by beta = 0 later, transition columns are zeroed when staged
@@ -472,7 +431,7 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
             int row, gc;
             granule(gi2, row, gc);
             const int col = min(gc * VG, dv - (int)cb * DVB - VG);
-            if (row < C) pv[u] = *at_bytes(reinterpret_cast<const g16*>(v_b), (__umul24(min(row, tlim), tok_v) + col) * (unsigned)E);
+            if (row < C) pv[u] = *at_bytes(reinterpret_cast<const g16*>(v_b), tok_elem_off(min(row, tlim), tok_v, col) * (unsigned)E);
         }
     };
     // staging tile for the next chunk's v, over the Kt..RF region, which is dead between the
@@ -661,8 +620,8 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
                 const int ra = 16 * p + g4 + (odd ? 2 : 0);
                 const typename P2::V w0 = odd ? P2::make(n0, QS[p][2]) : P2::make(QS[p][0], n0);
                 const typename P2::V w1 = odd ? P2::make(n1, QS[p][3]) : P2::make(QS[p][1], n1);
-                if (chain && ra < Tc) *at_bytes(o_w, (__umul24(ra, tok_v) + cpair) * (unsigned)E) = w0;
-                if (chain && ra + 1 < Tc) *at_bytes(o_w, (__umul24(ra + 1, tok_v) + cpair) * (unsigned)E) = w1;
+                if (chain && ra < Tc) *at_bytes(o_w, tok_elem_off(ra, tok_v, cpair) * (unsigned)E) = w0;
+                if (chain && ra + 1 < Tc) *at_bytes(o_w, tok_elem_off(ra + 1, tok_v, cpair) * (unsigned)E) = w1;
             }
         }
 
@@ -1061,20 +1020,18 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
 }
 
 // ---------------------------------------------------------------- launch
-size_t chunk_lds_bytes(bool bf16_, int dk, int chunk, int /*dv_block*/) {
-    return (size_t)lds_layout(bf16_ ? 2 : 4, dk, chunk).total;
-}
-
 template <typename OpT, int DK, int C, int MODE, bool EXT>
 static hipError_t launch_chunk_m(const ChunkArgs& a, hipStream_t st) {
     constexpr size_t lds = (size_t)lds_layout(sizeof(OpT), DK, C).total;
     auto kern = chunk_kernel<OpT, DK, C, MODE, EXT>;
-    static bool attr_set = false;   // per instantiation; the attribute is device-independent
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 163840);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    // once per instantiation (the attribute belongs to the function, not to a device); calls
+    // from several host threads wait for the first
+    static std::once_flag once;
+    static hipError_t attr_err = hipSuccess;
+    std::call_once(once, [&] {
+        attr_err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 163840);
+    });
+    if (attr_err != hipSuccess) return attr_err;
     const int ncols = MODE == 0 ? a.dv : a.dv + DK;
     const int nseg_grid = MODE == 0 ? a.n_seg : a.n_seg - 1;
     const int64_t nblk = a.B * a.H * (int64_t)nseg_grid * (ncols / a.dv_block);

@@ -94,7 +94,77 @@ __host__ __device__ constexpr int mtr_index(int dk, int row, int k) {
     return ((((row >> 4) * ksteps + (k >> 5)) * gpt + ((k >> 3) & 3) * 16 + (row & 15)) << 3) + (k & 7);
 }
 
-// Bytes of dynamic LDS the chunk kernel needs (0 if the shape does not fit).
-size_t chunk_lds_bytes(bool bf16, int dk, int chunk, int dv_block);
+// ---------------------------------------------------------------- chunk kernel LDS layout
+// Byte offsets of the chunk kernel's LDS arrays.  bf16 operands (RV): the A / M tiles take
+// their decay factors on the right operand, which is stored in one variant per distance
+// between the sub-tiles (RD for the diagonal, RH for adjacent sub-tiles, RF for two and three
+// apart).  float32 operands instead scale the left operand in registers by per-channel
+// factors (fd, fo), which keeps their LDS footprint small.
+struct Lds {
+    int kt, qt, kl, ql, rh, rd, rf, kht, an, mm, ad, fd, fo, egc, beta, total;
+};
+
+__host__ __device__ constexpr int align16(int x) { return (x + 15) & ~15; }
+
+// E: bytes per operand element
+__host__ __device__ constexpr Lds lds_layout(int E, int DK, int C) {
+    const bool RV = E == 2;
+    const int PADE = 16 / E;
+    const int NT = C / 16;
+    const int DKP = DK < 32 ? 32 : DK;            // bf16 natural loads read 32 channels at a time
+    const int LDK = DKP + PADE;
+    const int LKQ = DKP + 16 / E / (E == 2 ? 2 : 1);
+    const int LC = C + 16 / E / (E == 2 ? 2 : 1);
+    Lds L{};
+    int off = 0;
+    L.kt = off;   off += align16(C * LKQ * E);
+    L.qt = off;   off += align16(C * LKQ * E);
+    L.kl = off;   off += align16(C * LDK * E);
+    L.ql = off;   off += align16(C * LDK * E);
+    L.rh = off;   off += align16(C * LDK * E);
+    L.rd = off;   off += RV ? align16(C * LDK * E) : 0;
+    L.rf = off;   off += (RV && NT == 4) ? align16(48 * LDK * E) : 0;
+    // the Kt..RF region also holds the v staging tile (C rows, up to 128 columns)
+    if (off - L.kt < C * (128 + PADE) * E) off = L.kt + align16(C * (128 + PADE) * E);
+    L.kht = off;  off += align16(DK * LC * E);
+    L.an = off;   off += align16(C * LC * E);
+    L.mm = off;   off += align16(C * LC * E);
+    L.ad = off;   off += align16(NT * 16 * 16 * 4);
+    L.fd = off;   off += RV ? 0 : align16(NT * DKP * 4);
+    L.fo = off;   off += RV ? 0 : align16(3 * DKP * 4);
+    L.egc = off;  off += align16(2 * DKP * 4);   // two slots: chunk n and chunk n+1
+    L.beta = off; off += align16(2 * C * 4);
+    L.total = off;
+    return L;
+}
+
+// Bytes of dynamic LDS the chunk kernel needs for one workgroup.
+inline size_t chunk_lds_bytes(bool bf16, int dk, int chunk, int /*dv_block*/) {
+    return (size_t)lds_layout(bf16 ? 2 : 4, dk, chunk).total;
+}
+
+// ---------------------------------------------------------------- per-lane global offsets
+// The chunk kernel addresses a token-major tensor as a 64-bit, wave-uniform base at the
+// chunk's first token plus a 32-bit per-lane byte offset (the form scalar-base addressing
+// takes, with no 64-bit arithmetic per access).  Token strides are 24-bit products: the ABI
+// bounds H * max(dk, dv) below 2^24, and a lane's token lies less than 64 tokens past the
+// base, so (tok * stride + col) * esize stays below 63 * (2^24 - 1) * 4 + 512 < 2^32.
+__host__ __device__ inline unsigned mul24(unsigned a, unsigned b) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __umul24(a, b);
+#else
+    return (a & 0xFFFFFFu) * (b & 0xFFFFFFu);     // what v_mul_u32_u24 computes
+#endif
+}
+
+// element offset of column `col` of token `tok` (tokens `stride` elements apart)
+__host__ __device__ inline unsigned tok_elem_off(unsigned tok, unsigned stride, unsigned col) {
+    return mul24(tok, stride) + col;
+}
+
+// ---------------------------------------------------------------- library-owned workspace
+// Address of the current device's copy of the segment workspace that kda_chunk_fwd_noalloc
+// uses (KDA_NOALLOC_SCRATCH_BYTES per GPU), looked up once per device.
+hipError_t scratch_address(void** out);
 
 }  // namespace kda

@@ -28,7 +28,8 @@
  * - Layouts are dense row-major (C order), base pointers 16-byte aligned.
  * - Argument errors are detected before any HIP call: the call returns the
  *   code, writes nothing and records a message for kda_last_error().  Input
- *   values are not checked: NaN / Inf propagate.
+ *   values are not checked: NaN / Inf propagate.  (Device-side arrays, such
+ *   as cu_seqlens and n_accept, are read on the device: see each call.)
  * - A failed kernel launch returns KDA_ERR_HIP (text via kda_last_error()).
  * - Supported sizes: dk, dv in {16, 32, 64, 128}; chunk in {16, 32, 64};
  *   any T >= 0 (a partial last chunk is masked); B, N, H >= 1 with
@@ -49,8 +50,11 @@ extern "C" {
 
 #define KDA_ABI_VERSION 1
 
-/* Storage type of q, k, v and o.  log_alpha, beta and every state are float32. */
-typedef enum { KDA_DTYPE_F32 = 0, KDA_DTYPE_BF16 = 1 } kda_dtype_t;
+/* Storage type of q, k, v and o.  log_alpha, beta and every state are float32.
+ * (KDA_DTYPE_FORCE_INT32 is not a dtype: it makes every non-negative int32 a valid value of
+ * the type, so an unknown code passed from C is rejected with KDA_ERR_DTYPE rather than being
+ * an out-of-range enum value in the library's C++.) */
+typedef enum { KDA_DTYPE_F32 = 0, KDA_DTYPE_BF16 = 1, KDA_DTYPE_FORCE_INT32 = 0x7fffffff } kda_dtype_t;
 
 /* Input options of every call, bit flags (kda_plan_t.flags for kda_chunk_fwd, the `flags`
  * argument of the decode calls); 0 = none.
@@ -73,7 +77,8 @@ typedef enum {
     KDA_ERR_UNSUPPORTED = 5,   /* dk / dv / chunk / plan outside the supported set  */
     KDA_ERR_WORKSPACE = 6,     /* workspace missing or smaller than required        */
     KDA_ERR_HIP = 7,           /* the HIP runtime reported an error                 */
-    KDA_ERR_ALIAS = 8          /* an output overlaps an input it must not alias     */
+    KDA_ERR_ALIAS = 8,         /* an output overlaps an input it must not alias     */
+    KDA_STATUS_FORCE_INT32 = 0x7fffffff   /* not a status: widens the type (see kda_dtype_t) */
 } kda_status_t;
 
 /*
@@ -127,9 +132,15 @@ typedef struct {
     uint32_t flags;
 } kda_plan_t;
 
-/* Fills *plan with the library's default for this problem on the current
- * device (uses the device's compute-unit count).  Returns KDA_OK or an
- * argument error.  Never launches work. */
+/* Fills *plan with the library's default for this problem: one pass when the
+ * (batch, head) units alone cover MI355X's 256 compute units, otherwise enough
+ * segments to cover them (at least two chunks per segment).  The default is
+ * the same on every device (it does not query the device), so results round
+ * the same everywhere; on a partitioned device pass n_segments yourself.
+ * Returns KDA_OK or an argument error.  Makes no HIP call.
+ * With KDA_TRACE=1 in the environment, every kda_chunk_fwd call prints its
+ * resolved plan (segments, segment length, column block, workspace, launches)
+ * to stderr. */
 kda_status_t kda_chunk_fwd_default_plan(int64_t B, int64_t T, int32_t H, int32_t dk,
                                         int32_t dv, int32_t chunk, kda_dtype_t dt,
                                         kda_plan_t* plan);
@@ -141,7 +152,15 @@ kda_status_t kda_chunk_fwd_workspace_bytes(int64_t B, int64_t T, int32_t H, int3
                                            const kda_plan_t* plan, size_t* bytes);
 
 /*
- * Chunked prefill.
+ * Chunked prefill: the recurrence above over T tokens per sequence, evaluated
+ * chunk by chunk.  Within a chunk the decays enter as ratios of cumulative
+ * decays; the floor keeps a 16-token tile's cumulative log-decay in [-80, 0],
+ * so every intra-chunk tile, the diagonal ones included, is an ordinary dense
+ * matrix product (orkas.ai "Kimi K3 architecture", section "The floor that
+ * removed a GPU code path").  With n_segments > 1 the sequence is split into
+ * (cumulative transition, zero-start state) pairs composed by a prefix scan
+ * (same page, section "The cost comes back in the serving stack").  The
+ * result does not depend on chunk or plan beyond rounding.
  *
  *   q, k       [B, T, H, dk]  dt
  *   v          [B, T, H, dv]  dt

@@ -1,17 +1,27 @@
 """C-ABI checks that need no GPU: the library loads, exports every function the
 header declares, and rejects bad arguments with the documented codes before
-touching the HIP runtime (fake, never-dereferenced device addresses are used)."""
+touching the HIP runtime (fake, never-dereferenced device addresses are used).
+
+The ABI layer is also built on its own with g++ under AddressSanitizer and
+UndefinedBehaviorSanitizer, with recording stubs in place of the kernel
+launchers (tests/host_abi_check.cpp), and run here: every error path, the launch
+sequence of accepted calls, the KDA_TRACE plan line, and the kernels' 32-bit
+per-lane offset formula at the ABI's size limits."""
 import ctypes
 import os
 import re
+import shutil
+import subprocess
 
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kda.h")
 LIBPATH = os.path.join(ROOT, "gated_delta_rule_107_amd", "libkda.so")
+CSRC = os.path.join(ROOT, "gated_delta_rule_107_amd", "csrc")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
-pytestmark = pytest.mark.skipif(not os.path.exists(LIBPATH), reason="libkda.so not built")
+needs_lib = pytest.mark.skipif(not os.path.exists(LIBPATH), reason="libkda.so not built")
 
 OK, NULL, SHAPE, DTYPE, ALIGN, UNSUP, WS, HIP, ALIAS = range(9)
 F32, BF16 = 0, 1
@@ -25,8 +35,55 @@ def declared_functions():
 
 @pytest.fixture(scope="module")
 def lib():
+    if not os.path.exists(LIBPATH):
+        pytest.skip("libkda.so not built")
     import gated_delta_rule_107_amd as g
     return g.lib()
+
+
+# ------------------------------------------------------------------ sanitized host build of the ABI layer
+
+@pytest.fixture(scope="module")
+def host_check(tmp_path_factory):
+    gxx = shutil.which("g++")
+    if gxx is None or not os.path.exists(os.path.join(ROCM, "include", "hip", "hip_runtime.h")):
+        pytest.skip("g++ or the HIP headers are missing")
+    exe = str(tmp_path_factory.mktemp("host_abi") / "host_abi_check")
+    cmd = [gxx, "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+           "-D__HIP_PLATFORM_AMD__", f"-I{ROCM}/include", f"-I{ROOT}/include", f"-I{CSRC}",
+           os.path.join(ROOT, "tests", "host_abi_check.cpp"), os.path.join(CSRC, "kda_api.cpp"),
+           f"-L{ROCM}/lib", "-lamdhip64", f"-Wl,-rpath,{ROCM}/lib", "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-4000:]
+    return exe
+
+
+def _run_host_check(exe, *args, env=None):
+    e = dict(os.environ)
+    e.pop("KDA_TRACE", None)
+    e.update(env or {})
+    e.setdefault("ASAN_OPTIONS", "abort_on_error=0:halt_on_error=1")
+    e.setdefault("UBSAN_OPTIONS", "print_stacktrace=1:halt_on_error=1")
+    return subprocess.run([exe, *args], capture_output=True, text=True, env=e, timeout=120)
+
+
+def test_abi_layer_under_sanitizers(host_check):
+    r = _run_host_check(host_check)
+    assert r.returncode == 0 and "ok: 0 failed checks" in r.stdout, r.stdout[-4000:] + r.stderr[-4000:]
+    assert "runtime error" not in r.stderr and "AddressSanitizer" not in r.stderr, r.stderr[-4000:]
+
+
+def test_trace_prints_the_resolved_plan(host_check):
+    r = _run_host_check(host_check, "trace", env={"KDA_TRACE": "1"})
+    assert r.returncode == 0, r.stderr[-4000:]
+    line = [ln for ln in r.stderr.splitlines() if ln.startswith("kda_chunk_fwd_noalloc:")]
+    assert len(line) == 1, r.stderr
+    for field in ("B=1", "T=4096", "H=16", "n_segments=16", "seg_len=256", "dv_block=128",
+                  "workspace=50331648", "launches=segment-pass-1,scan,segment-pass-2"):
+        assert field in line[0], (field, line[0])
+    quiet = _run_host_check(host_check, "trace")
+    assert "kda_chunk_fwd" not in quiet.stderr
 
 
 def test_exports_every_declared_function(lib):
@@ -42,6 +99,7 @@ def test_abi_version_and_status_strings(lib):
     for code in range(9):
         assert lib.kda_status_str(code).decode() not in ("", "unknown status")
     assert lib.kda_status_str(99) == b"unknown status"
+    assert lib.kda_status_str(-1) == b"unknown status"
 
 
 # fake device addresses: 16-byte aligned, far apart, never dereferenced
@@ -201,6 +259,7 @@ def test_input_flag_errors(lib):
     assert g._flags(g.GATE_LOGITS, True) == g.FLAG_GATE_LOGITS | g.FLAG_QK_L2NORM
 
 
+@needs_lib
 def test_python_binding_rejects_cpu_tensors():
     import gated_delta_rule_107_amd as g
     import torch

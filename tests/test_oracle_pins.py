@@ -127,6 +127,66 @@ def test_small_beta_is_gla_limit():
     assert 1.5 < err2 / err < 2.5
 
 
+# ---------------------------------------------------------------- the reductions' own definitions
+
+def test_gla_loop_against_decayed_causal_sum():
+    """gla_loop against its closed form, written as a double sum over position pairs with the
+    decay as an explicit product of per-step factors (no cumulative sums of logs):
+    o_t = sum_c q_tc [ (prod_{r<=t} a_rc) S0[c,:] + sum_{s<=t} (prod_{s<r<=t} a_rc) k_sc v_s ]."""
+    q, k, v, la, _, S0 = rnd_inputs(21, B=1, T=9, H=2, dk=4, dv=3)
+    a = np.exp(np.clip(la, -5.0, 0.0))
+    B, T, H, dk = q.shape
+    o_ref = np.zeros(v.shape)
+    for h in range(H):
+        for t in range(T):
+            for c in range(dk):
+                prod_all = np.prod(a[0, :t + 1, h, c])
+                acc = prod_all * S0[0, h, c]
+                for s in range(t + 1):
+                    acc = acc + np.prod(a[0, s + 1:t + 1, h, c]) * k[0, s, h, c] * v[0, s, h]
+                o_ref[0, t, h] += q[0, t, h, c] * acc
+    o = oracle.gla_loop(q, k, v, la, S0)
+    assert rel_fro(o, o_ref) < 1e-13
+
+
+def test_gdn_loop_against_matrix_products():
+    """gdn_loop against explicit dk x dk matrices: S_t = a_t (I - b_t k_t k_t^T) S_{t-1} + b_t k_t v_t^T
+    with the products formed as np.outer / np.eye, and a hand-checked two-step case."""
+    q, k, v, la, beta, S0 = rnd_inputs(22, B=1, T=6, H=1, dk=4, dv=2)
+    la_h = la[..., 0]
+    a = np.exp(np.clip(la_h, -5.0, 0.0))
+    S = S0[0, 0].copy()
+    o_ref = np.empty((6, 2))
+    for t in range(6):
+        P = a[0, t, 0] * (np.eye(4) - beta[0, t, 0] * np.outer(k[0, t, 0], k[0, t, 0]))
+        S = P @ S + beta[0, t, 0] * np.outer(k[0, t, 0], v[0, t, 0])
+        o_ref[t] = q[0, t, 0] @ S
+    o, S_T = oracle.gdn_loop(q, k, v, la_h, beta, S0)
+    assert rel_fro(o[0, :, 0], o_ref) < 1e-13 and rel_fro(S_T[0, 0], S) < 1e-13
+    # dk = 1, dv = 1 by hand: a = 1/2, b = 1, k = 1: S1 = 0.5 (1 - 1) S0 + v1 = v1; S2 = 0.5 * 0 + v2
+    one = np.ones((1, 2, 1, 1))
+    o2, S2 = oracle.gdn_loop(one, one, np.array([3.0, -2.0]).reshape(1, 2, 1, 1),
+                             np.full((1, 2, 1), np.log(0.5)), np.ones((1, 2, 1)), np.full((1, 1, 1, 1), 7.0))
+    assert np.allclose(o2.ravel(), [3.0, -2.0], atol=1e-15) and np.allclose(S2.ravel(), [-2.0], atol=1e-15)
+
+
+def test_rel_fro_is_normalised_by_the_reference():
+    """Every parity claim uses rel_fro: pin it by hand.  ref = 3 e1 and x = ref + 4 e2 give
+    ||x - ref|| / ||ref|| = 4 / 3 (normalising by ||x|| = 5 would give 4 / 5)."""
+    ref = np.array([3.0, 0.0])
+    x = ref + np.array([0.0, 4.0])
+    assert rel_fro(x, ref) == pytest.approx(4.0 / 3.0, rel=1e-15)
+    assert rel_fro(ref, x) == pytest.approx(4.0 / 5.0, rel=1e-15)      # the arguments are not symmetric
+    assert rel_fro(ref, ref) == 0.0
+    # over a whole tensor, not per row: rows [3, 0] and [0, 4] against [3, 4] and [0, 0]
+    assert rel_fro(np.array([[3.0, 0.0], [0.0, 4.0]]), np.array([[3.0, 4.0], [0.0, 0.0]])) == \
+        pytest.approx(math.sqrt(4.0 ** 2 + 4.0 ** 2) / 5.0, rel=1e-15)
+    # bf16-stored inputs: the float32 holder of a bf16 value is read exactly
+    assert rel_fro(np.float32(1.0078125), np.float64(1.0)) == pytest.approx(0.0078125, rel=1e-15)
+    # a zero reference returns the plain norm of the difference
+    assert rel_fro(np.array([0.0, 2.0]), np.zeros(2)) == pytest.approx(2.0)
+
+
 # ---------------------------------------------------------------- P3 GDN reduction
 
 def test_scalar_gate_is_gated_deltanet():
