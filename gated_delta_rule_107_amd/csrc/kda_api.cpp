@@ -91,14 +91,12 @@ kda_status_t resolve_plan(int64_t B, int64_t T, int32_t H, int32_t dk, int32_t d
         const int64_t units = B * H * (dv / dvb);
         const int64_t cus = kPlanCUs;
         nseg = 1;
-        if (units < cus && dk % dvb == 0) {
+        if (units < cus) {
             nseg = (cus + units - 1) / units;
             if (nseg > nchunks / 2) nseg = nchunks / 2;
             if (nseg < 1) nseg = 1;
         }
     }
-    if (nseg > 1 && dk % dvb != 0)
-        return fail(KDA_ERR_UNSUPPORTED, "segments need dv_block (%d) to divide dk (%d)", dvb, dk);
     if (nseg > 65535) return fail(KDA_ERR_UNSUPPORTED, "too many segments");
     int64_t seg_chunks = nchunks == 0 ? 1 : (nchunks + nseg - 1) / nseg;
     if (seg_chunks < 1) seg_chunks = 1;

@@ -277,6 +277,9 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
     constexpr int LC = C + (E == 2 ? 4 : 4);
     constexpr int KNAT = (E == 2) ? (DK + 31) / 32 : DK / 4;   // natural-order steps over channels
     constexpr bool want_o = MODE == 0;
+    // state column groups per wave: one in MODE 0; in MODE 1 the widened state [S | M] as two,
+    // 16 value columns (S, from 0, values v) and 16 transition columns (M, from I, values 0)
+    constexpr int NG = MODE == 1 ? 2 : 1;
     constexpr Lds L = lds_layout(E, DK, C);
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -301,9 +304,10 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
 
     // ---- which (batch, head, segment, column block) this workgroup owns.  Column blocks of
     // one unit are 8 block indices apart, so they share an XCD (blocks go round-robin over 8).
-    const int H = a.H, dv = a.dv, DVB = a.dv_block;
-    const int ncols = MODE == 0 ? dv : dv + DK;
-    const int ncb = ncols / DVB;
+    // MODE 1 has one block: every wave holds both of its column groups.
+    const int H = a.H, dv = a.dv;
+    const int DVB = MODE == 0 ? a.dv_block : dv;    // value columns of this workgroup
+    const int ncb = MODE == 0 ? dv / DVB : 1;
     const int nseg_grid = MODE == 0 ? a.n_seg : a.n_seg - 1;
     int64_t unit, cb;
     {
@@ -337,9 +341,9 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
         t_end = t_begin + a.seg_len < T ? t_begin + a.seg_len : T;
     }
 
-    const int colw = (int)cb * DVB + 16 * wave;      // first (virtual) column of this wave
-    const bool chain = 16 * wave < DVB;              // this wave owns state columns
-    const bool mcols = MODE == 1 && colw >= dv;      // ... transition columns (start I, V = 0)
+    const int colw = (int)cb * DVB + 16 * wave;      // first value column of this wave
+    const bool chain = 16 * wave < DVB;              // this wave owns value columns
+    const bool mchain = MODE == 1 && 16 * wave < DK; // ... transition columns 16w.. of M (MODE 1)
 
     const OpT* gq = reinterpret_cast<const OpT*>(a.q);
     const OpT* gk = reinterpret_cast<const OpT*>(a.k);
@@ -420,9 +424,7 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
         row = (int)__umulhi((unsigned)gi2, gpr_magic);
         gc = gi2 - row * GPR;
     };
-    const bool vblk = MODE == 0 || (int)cb * DVB < dv;   // the block holds value columns
     auto prefetch_v = [&](int64_t t0, int tid) {
-        if (!vblk) return;
         const int tlim = (int)(t_end - 1 - t0 < C - 1 ? t_end - 1 - t0 : C - 1);
         const OpT* v_b = gv + ((b * T + t0) * H + h) * (int64_t)dv + (int)cb * DVB;   // uniform
 #pragma unroll
@@ -440,8 +442,9 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
     OpT* s_v = s_kt;
     static_assert(C * LVO * E <= L.kht - L.kt, "v staging tile exceeds the dead operand region");
 
-    // ---- start state into accumulator layout: Sacc[tau][r] = S[16 tau + g4 + r][colw + jl]
-    f32x4 Sacc[NCT];
+    // ---- start state into accumulator layout: Sacc[G][tau][r] = S[16 tau + g4 + r][colw + jl]
+    // (group 1: M[16 tau + g4 + r][16 w + jl], from the identity)
+    f32x4 Sacc[NG][NCT];
     {
         const int lane = threadIdx.x & 63, g4 = 4 * (lane >> 4), jl = lane & 15;
         const float* src = nullptr;
@@ -456,12 +459,8 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = 16 * tau + g4 + r;
-                float x = 0.f;
-                if (chain) {
-                    if (src) x = src[row * dv + colw + jl];
-                    else if (mcols) x = (row == colw + jl - dv) ? 1.f : 0.f;
-                }
-                Sacc[tau][r] = x;
+                Sacc[0][tau][r] = (chain && src) ? src[row * dv + colw + jl] : 0.f;
+                if constexpr (NG == 2) Sacc[1][tau][r] = (mchain && row == 16 * wave + jl) ? 1.f : 0.f;
             }
     }
 
@@ -518,8 +517,8 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
     //   (4) v(n+1) into registers in the accumulator layout.
     // beta and e^Gamma_C of chunk n are read in (1) while gate prep writes chunk n+1's, so
     // they have two slots (chunk n uses slot n & 1); Khat^T(n+1) waits in registers until (2).
-    f32x4 X[NT], QS[NT];                             // Kt S, Qt S of the chunk chained next
-    B16 vr[NT];                                      // its v
+    f32x4 X[NG][NT], QS[NT];                         // Kt S, Qt S of the chunk chained next
+    B16 vr[NT];                                      // its v (value columns)
     V4 khr[4];                                       // Khat^T(n+1): 4 channels x 4 tokens
 
     // state checkpoints (pass 2 / one pass): tokens into this unit's range that end the next
@@ -588,17 +587,22 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
         }
 
         // ================= (1a) chain of chunk n: R_p = beta (V - X); U_p = N_pp (R_p - sum_{q<p} Ab_pq U_q)
-        B16 ub[NT];
+        // (the transition columns of MODE 1 have V = 0)
+        B16 ub[NG][NT];
         if constexpr (cur) {
 #pragma unroll
             for (int p = 0; p < NT; ++p) {
-                f32x4 R;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) R[r] = sb_c[16 * p + g4 + r] * ((float)vr[p][r] - X[p][r]);
+                for (int G = 0; G < NG; ++G) {
+                    f32x4 R;
 #pragma unroll
-                for (int q = 0; q < p; ++q) R = MF::k16(s_an, LC, 16 * p, 16 * q, ub[q], R, lane);
-                const f32x4 U = MF::k16(s_an, LC, 16 * p, 16 * p, MF::b16(R), f32x4{0.f, 0.f, 0.f, 0.f}, lane);
-                ub[p] = MF::b16(U);
+                    for (int r = 0; r < 4; ++r)
+                        R[r] = sb_c[16 * p + g4 + r] * ((G == 0 ? (float)vr[p][r] : 0.f) - X[G][p][r]);
+#pragma unroll
+                    for (int q = 0; q < p; ++q) R = MF::k16(s_an, LC, 16 * p, 16 * q, ub[G][q], R, lane);
+                    const f32x4 U = MF::k16(s_an, LC, 16 * p, 16 * p, MF::b16(R), f32x4{0.f, 0.f, 0.f, 0.f}, lane);
+                    ub[G][p] = MF::b16(U);
+                }
             }
         }
 
@@ -614,7 +618,7 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
 #pragma unroll
             for (int p = 0; p < NT; ++p) {
 #pragma unroll
-                for (int qq = 0; qq <= p; ++qq) QS[p] = MF::k16(s_mm, LC, 16 * p, 16 * qq, ub[qq], QS[p], lane);
+                for (int qq = 0; qq <= p; ++qq) QS[p] = MF::k16(s_mm, LC, 16 * p, 16 * qq, ub[0][qq], QS[p], lane);
                 const float n0 = swap_adjacent(odd ? QS[p][0] : QS[p][2]);
                 const float n1 = swap_adjacent(odd ? QS[p][1] : QS[p][3]);
                 const int ra = 16 * p + g4 + (odd ? 2 : 0);
@@ -763,19 +767,28 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
             }
         }
 
-        // ================= (1e) S <- Diag(e^Gamma_C) S + Khat^T U for chunk n
+        // ================= (1e) S <- Diag(e^Gamma_C) S + Khat^T U for chunk n (every column
+        // group from one load of each Khat^T tile)
         if constexpr (cur) {
 #pragma unroll
             for (int tau = 0; tau < NCT; ++tau) {
                 const f32x4 eg = *reinterpret_cast<const f32x4*>(eg_c + 16 * tau + g4);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) Sacc[tau][r] *= eg[r];
+                for (int G = 0; G < NG; ++G)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) Sacc[G][tau][r] *= eg[r];
                 if constexpr (NT == 1) {
-                    Sacc[tau] = MF::k16(s_kht, LC, 16 * tau, 0, ub[0], Sacc[tau], lane);
+#pragma unroll
+                    for (int G = 0; G < NG; ++G)
+                        Sacc[G][tau] = MF::k16(s_kht, LC, 16 * tau, 0, ub[G][0], Sacc[G][tau], lane);
                 } else {
 #pragma unroll
-                    for (int s2 = 0; s2 < NT / 2; ++s2)
-                        Sacc[tau] = MF::k32(s_kht, LC, 16 * tau, 32 * s2, ub[2 * s2], ub[2 * s2 + 1], Sacc[tau], lane);
+                    for (int s2 = 0; s2 < NT / 2; ++s2) {
+                        const typename MF::A32 kh = MF::ld32(s_kht, LC, 16 * tau, 32 * s2, lane);
+#pragma unroll
+                        for (int G = 0; G < NG; ++G)
+                            Sacc[G][tau] = MF::mma32(kh, ub[G][2 * s2], ub[G][2 * s2 + 1], Sacc[G][tau]);
+                    }
                 }
             }
         }
@@ -791,7 +804,7 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
 #pragma unroll
                     for (int tau = 0; tau < NCT; ++tau)
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) ck_ptr[(16 * tau + g4 + r) * dv + jl] = Sacc[tau][r];
+                        for (int r = 0; r < 4; ++r) ck_ptr[(16 * tau + g4 + r) * dv + jl] = Sacc[0][tau][r];
                 }
                 ck_rel += (int)a.ckpt_stride;
                 ck_ptr += (int64_t)H * DK * dv;
@@ -805,24 +818,32 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
                 for (int e = 0; e < 4; ++e) *reinterpret_cast<V4*>(s_kht + (gc0 + e) * LC + 4 * tq) = khr[e];
             }
             {
-                B16 sb[NCT];
+                B16 sb[NG][NCT];
 #pragma unroll
-                for (int tau = 0; tau < NCT; ++tau) sb[tau] = MF::b16(Sacc[tau]);
+                for (int G = 0; G < NG; ++G)
+#pragma unroll
+                    for (int tau = 0; tau < NCT; ++tau) sb[G][tau] = MF::b16(Sacc[G][tau]);
                 if constexpr (NCT == 1 || E == 4) {
                     // (float32 operands are 4x larger: no room to hold a second sub-tile's)
 #pragma unroll
                     for (int p = 0; p < NT; ++p) {
-                        X[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int G = 0; G < NG; ++G) X[G][p] = f32x4{0.f, 0.f, 0.f, 0.f};
                         QS[p] = f32x4{0.f, 0.f, 0.f, 0.f};
                         if constexpr (NCT == 1) {
-                            X[p] = MF::k16(s_kt, LKQ, 16 * p, 0, sb[0], X[p], lane);
-                            if (want_o) QS[p] = MF::k16(s_qt, LKQ, 16 * p, 0, sb[0], QS[p], lane);
+#pragma unroll
+                            for (int G = 0; G < NG; ++G) X[G][p] = MF::k16(s_kt, LKQ, 16 * p, 0, sb[G][0], X[G][p], lane);
+                            if (want_o) QS[p] = MF::k16(s_qt, LKQ, 16 * p, 0, sb[0][0], QS[p], lane);
                         } else {
 #pragma unroll
                             for (int s2 = 0; s2 < NCT / 2; ++s2) {
-                                X[p] = MF::k32(s_kt, LKQ, 16 * p, 32 * s2, sb[2 * s2], sb[2 * s2 + 1], X[p], lane);
+#pragma unroll
+                                for (int G = 0; G < NG; ++G)
+                                    X[G][p] = MF::k32(s_kt, LKQ, 16 * p, 32 * s2, sb[G][2 * s2], sb[G][2 * s2 + 1],
+                                                      X[G][p], lane);
                                 if (want_o)
-                                    QS[p] = MF::k32(s_qt, LKQ, 16 * p, 32 * s2, sb[2 * s2], sb[2 * s2 + 1], QS[p], lane);
+                                    QS[p] = MF::k32(s_qt, LKQ, 16 * p, 32 * s2, sb[0][2 * s2], sb[0][2 * s2 + 1], QS[p],
+                                                    lane);
                             }
                         }
                     }
@@ -843,12 +864,15 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
                     for (int p = 0; p < NT; ++p) {
                         if (p + 1 < NT) load(p + 1, (p + 1) & 1);
                         __builtin_amdgcn_sched_barrier(0);
-                        X[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int G = 0; G < NG; ++G) X[G][p] = f32x4{0.f, 0.f, 0.f, 0.f};
                         QS[p] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                         for (int s2 = 0; s2 < NCT / 2; ++s2) {
-                            X[p] = MF::mma32(ax[p & 1][s2], sb[2 * s2], sb[2 * s2 + 1], X[p]);
-                            if (want_o) QS[p] = MF::mma32(aq[p & 1][s2], sb[2 * s2], sb[2 * s2 + 1], QS[p]);
+#pragma unroll
+                            for (int G = 0; G < NG; ++G)
+                                X[G][p] = MF::mma32(ax[p & 1][s2], sb[G][2 * s2], sb[G][2 * s2 + 1], X[G][p]);
+                            if (want_o) QS[p] = MF::mma32(aq[p & 1][s2], sb[0][2 * s2], sb[0][2 * s2 + 1], QS[p]);
                         }
                         __builtin_amdgcn_sched_barrier(0);
                     }
@@ -956,7 +980,7 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
                 const int gi2 = tid + 512 * u;
                 int row, gc;
                 granule(gi2, row, gc);
-                if (row < C) *reinterpret_cast<g16*>(s_v + row * LVO + gc * VG) = vblk ? pv[u] : g16{0.f, 0.f, 0.f, 0.f};
+                if (row < C) *reinterpret_cast<g16*>(s_v + row * LVO + gc * VG) = pv[u];
             }
             if (n + 2 < nchunks) prefetch_v(t1 + C, tid);
         }
@@ -982,39 +1006,40 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
     }
 
     // ---- final state of this unit
-    if (chain) {
+    {
         const int lane = threadIdx.x & 63, g4 = 4 * (lane >> 4), jl = lane & 15;
-        float* dst = nullptr;
-        int64_t ld = 0;
         const int col = colw + jl;
-        if (MODE == 0) {
-            if (seg == a.n_seg - 1) { dst = a.s_final + bh * DK * dv; ld = dv; }
-        } else if (!mcols) {
-            // the zero-start state goes to the scan in its accumulator-tile order
-            float* sl = a.s_loc + (bh * a.n_seg + seg) * DK * dv;
+        if constexpr (MODE == 0) {
+            if (chain && seg == a.n_seg - 1) {
+                float* dst = a.s_final + bh * DK * dv;
 #pragma unroll
-            for (int tau = 0; tau < NCT; ++tau)
-                *reinterpret_cast<f32x4*>(sl + sloc_index(DK, 16 * tau + g4, col)) = Sacc[tau];
+                for (int tau = 0; tau < NCT; ++tau)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) dst[(16 * tau + g4 + r) * dv + col] = Sacc[0][tau][r];
+            }
         } else {
-            // the transition goes to the scan already split into bf16 high and low planes, in
-            // the order of the scan's A operand
-            bf16* mh = reinterpret_cast<bf16*>(a.m_tr) + (bh * a.n_seg + seg) * 2 * DK * DK;
+            if (chain) {
+                // the zero-start state goes to the scan in its accumulator-tile order
+                float* sl = a.s_loc + (bh * a.n_seg + seg) * DK * dv;
 #pragma unroll
-            for (int tau = 0; tau < NCT; ++tau)
+                for (int tau = 0; tau < NCT; ++tau)
+                    *reinterpret_cast<f32x4*>(sl + sloc_index(DK, 16 * tau + g4, col)) = Sacc[0][tau];
+            }
+            if (mchain) {
+                // the transition goes to the scan already split into bf16 high and low planes, in
+                // the order of the scan's A operand
+                bf16* mh = reinterpret_cast<bf16*>(a.m_tr) + (bh * a.n_seg + seg) * 2 * DK * DK;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float x = Sacc[tau][r];
-                    const bf16 hi = (bf16)x;
-                    const int at = mtr_index(DK, 16 * tau + g4 + r, col - dv);
-                    mh[at] = hi;
-                    mh[DK * DK + at] = (bf16)(x - (float)hi);
-                }
-        }
-        if (dst) {
+                for (int tau = 0; tau < NCT; ++tau)
 #pragma unroll
-            for (int tau = 0; tau < NCT; ++tau)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) dst[(16 * tau + g4 + r) * ld + col] = Sacc[tau][r];
+                    for (int r = 0; r < 4; ++r) {
+                        const float x = Sacc[NG - 1][tau][r];
+                        const bf16 hi = (bf16)x;
+                        const int at = mtr_index(DK, 16 * tau + g4 + r, 16 * wave + jl);
+                        mh[at] = hi;
+                        mh[DK * DK + at] = (bf16)(x - (float)hi);
+                    }
+            }
         }
     }
 }
@@ -1032,9 +1057,10 @@ static hipError_t launch_chunk_m(const ChunkArgs& a, hipStream_t st) {
         attr_err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 163840);
     });
     if (attr_err != hipSuccess) return attr_err;
-    const int ncols = MODE == 0 ? a.dv : a.dv + DK;
+    // MODE 1: one workgroup per (batch, head, segment) holds every column of [S | M]
+    const int nblk_col = MODE == 0 ? a.dv / a.dv_block : 1;
     const int nseg_grid = MODE == 0 ? a.n_seg : a.n_seg - 1;
-    const int64_t nblk = a.B * a.H * (int64_t)nseg_grid * (ncols / a.dv_block);
+    const int64_t nblk = a.B * a.H * (int64_t)nseg_grid * nblk_col;
     if (nblk <= 0) return hipSuccess;
     hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(512), lds, st, a);
     return hipGetLastError();

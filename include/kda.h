@@ -90,10 +90,11 @@ typedef enum {
  *   back in the serving stack": pass 1 builds every segment's (cumulative
  *   transition, zero-start state) pair, a prefix scan gives each segment's
  *   true start state, pass 2 reruns the segments in parallel from those.
- * dv_block: value columns per workgroup, a multiple of 16 dividing dv.  The
- *   recurrence is independent per state column, so column blocks run in
- *   parallel; the shared per-chunk work (gates, WY transform) is repeated
- *   per block.
+ * dv_block: value columns per workgroup of the one-pass / pass-2 launch, a
+ *   multiple of 16 dividing dv.  The recurrence is independent per state
+ *   column, so column blocks run in parallel; the shared per-chunk work
+ *   (gates, WY transform) is repeated per block.  Pass 1 of a segmented plan
+ *   always holds all dv + dk columns of its widened state in one workgroup.
  * state_ckpt / ckpt_stride: optional state checkpoints for prefix reuse
  *   (orkas.ai "Kimi K3 architecture", section "The cost comes back in the
  *   serving stack": the recurrent state is checkpointed sparsely, at some of
