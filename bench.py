@@ -1,25 +1,31 @@
 """Benchmark of the KDA hot path on one MI355X (gfx950).
 
-    python bench.py [--steps K] [--warmup W] [--workload N] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--workload N] [--side 1,2] [--gpus 1]
 
-One step = one kda_chunk_fwd over the timed prefill workload with the
+One step = one kda_chunk_fwd over the headline prefill workload with the
 library's default plan: gate prep, WY/UT transform, intra-chunk outputs and
 the inter-chunk state pass, plus the segment passes and prefix scan when the
-plan splits the sequence.  The default workload is the single-sequence
-prefill B=1, T=4096, H=16, dk=dv=128, chunk 64, bf16 q/k/v with float32 gates
-and state.  Inputs are seeded synthetic tensors already resident in HBM when
-the timed region starts.
+plan splits the sequence.  The headline workload is the largest one that fits
+one GPU, the single 1,048,576-token sequence: B=1, T=1,048,576, H=32,
+dk=dv=128, chunk 64, bf16 q/k/v/o with float32 gates and state (default plan:
+8 segments, so segment pass 1, prefix scan and pass 2).  Inputs are seeded
+synthetic tensors already resident in HBM when the timed region starts.
 
-The prefill block also reports the same step with state checkpoints every 512
-tokens (the prefix-reuse output of kda_plan_t.state_ckpt), the same step
-reading raw gate logits (KDA_GATE_LOGITS) and with q / k normalised inside the
-kernels (KDA_QK_L2NORM).  The same JSON line
-also carries the decode figure (256 sequences x 32 heads,
-128x128 float32 state, 64 consecutive in-place steps) with the speculative
-verify of 4 drafts per sequence and the commit of all 4, the roofline of the
-dominant prefill kernel (algorithmic bytes per launch / its mean duration,
-taken from HIP events the library records around each launch on the stream
-the kernels run on), and the float64 CPU oracle timed on the host cores.
+The same JSON line carries side figures, each timed the same way:
+  * the other prefill workloads (B=1 T=4096 H=16 with 16 segments; the B=8
+    T=8192 H=32 floor-stress batch in one pass), with their per-launch times
+    and whole-step rooflines;
+  * the headline step with state checkpoints every 512 tokens, with raw gate
+    logits (KDA_GATE_LOGITS) and with q / k normalised in the kernels;
+  * decode: 256 sequences x 32 heads, 128x128 float32 state, 64 consecutive
+    in-place steps, plus the speculative verify of 4 drafts and their commit.
+Rooflines: `roofline` is the dominant launch of the headline step (its
+algorithmic bytes over its mean duration, from HIP events the library records
+around each launch on the stream the kernels run on) with the whole step's
+beside it; executed MFMA figures come from the committed rocprofv3 counter
+table of the workload while the library sources match the ones it was taken
+on.  `cpu_baseline` is the float64 oracle timed on the host cores on a
+bounded sample of the headline workload.
 
 Prints exactly one JSON line on stdout; progress goes to stderr.
 """
@@ -151,8 +157,26 @@ def cpu_model():
     return platform.machine()
 
 
+CPU_SHARE = 16                        # host cores one GPU's share of the box provides
+
+
 def cpu_workers():
-    return max(1, min(16, os.cpu_count() or 1))
+    """Worker processes for the oracle: every core this process may run on, up to the
+    16-core share of the host that goes with one GPU."""
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    return max(1, min(CPU_SHARE, avail))
+
+
+def host_cores():
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = None
+    return {"host_cpu_count": os.cpu_count(), "affinity_cpus": affinity, "cpu_share_per_gpu": CPU_SHARE,
+            "cpu_model": cpu_model()}
 
 
 HOST_GEN_LIMIT = 1 << 23              # token-heads above which inputs are drawn on the device
@@ -177,11 +201,13 @@ def cpu_baseline_prefill(r, x):
             break
         reps = int(min(512, max(2 * reps, np.ceil(reps * 12.0 / max(wall * workers, 1e-3)))))
     tok = r.B * r.T * reps
-    return {"value": tok / wall, "unit": "tokens/s", "cores": workers, "kind": "oracle",
-            "sample": (f"first {r.T} tokens of every head" if sampled else "whole workload")
-                      + f" (B={r.B} T={r.T} H={r.H}) x{reps}, float64 chunked form "
-                      f"(chunk {r.chunk}), one (b, h) per task", "seconds": wall,
-            "cpu_model": cpu_model()}
+    out = {"value": tok / wall, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+           "sample": (f"first {r.T} tokens of every head" if sampled else "whole workload")
+                     + f" (B={r.B} T={r.T} H={r.H}) x{reps}, float64 chunked form "
+                     f"(chunk {r.chunk}), one (b, h) per task; tokens/s of the sample",
+           "seconds": wall}
+    out.update(host_cores())
+    return out
 
 
 def cpu_baseline_decode(rd, d, n_seq):
@@ -207,21 +233,30 @@ def make_events(torch, n):
     return evs
 
 
-def bench_prefill(g, torch, r, x, steps, warmup):
-    dev = torch.device("cuda:0")
+def prefill_inputs(torch, r, x, dev):
+    """Device tensors of a prefill workload: uploaded from host arrays ``x``, or drawn on the
+    device when the workload is too large for host copies (x is None)."""
     dt = torch.bfloat16 if r.dtype == "bf16" else torch.float32
-    es = 2 if r.dtype == "bf16" else 4
-    if x is None:                        # too large for host arrays: drawn on the device
+    if x is None:
         t = time.perf_counter()
         xd = ks.make_prefill_device(r, dev)
         torch.cuda.synchronize()
-        log(f"generated prefill inputs on the device in {time.perf_counter() - t:.1f}s")
-        q, k, v, la, beta, S0 = xd["q"], xd["k"], xd["v"], xd["log_alpha"], xd["beta"], xd["S0"]
-    else:
-        T_ = lambda a, t: torch.from_numpy(np.ascontiguousarray(a)).to(dev, t)  # noqa: E731
-        q, k, v = T_(x["q"], dt), T_(x["k"], dt), T_(x["v"], dt)
-        la, beta = T_(x["log_alpha"], torch.float32), T_(x["beta"], torch.float32)
-        S0 = None if x["S0"] is None else T_(x["S0"], torch.float32)
+        log(f"generated {r.name} inputs on the device in {time.perf_counter() - t:.1f}s")
+        return xd
+    T_ = lambda a, t: torch.from_numpy(np.ascontiguousarray(a)).to(dev, t)  # noqa: E731
+    return {"q": T_(x["q"], dt), "k": T_(x["k"], dt), "v": T_(x["v"], dt),
+            "log_alpha": T_(x["log_alpha"], torch.float32), "beta": T_(x["beta"], torch.float32),
+            "S0": None if x["S0"] is None else T_(x["S0"], torch.float32)}
+
+
+def time_prefill(g, torch, r, xd, steps, warmup, options=False):
+    """Times `steps` default-plan kda_chunk_fwd calls (after `warmup`), then the same number with
+    the library recording HIP events around every launch; returns the figures as a dict.  With
+    ``options`` also the step with state checkpoints, gate logits and q / k normalisation."""
+    dev = torch.device("cuda:0")
+    dt = torch.bfloat16 if r.dtype == "bf16" else torch.float32
+    es = 2 if r.dtype == "bf16" else 4
+    q, k, v, la, beta, S0 = xd["q"], xd["k"], xd["v"], xd["log_alpha"], xd["beta"], xd["S0"]
     plan = g.default_plan(r.B, r.T, r.H, r.dk, r.dv, r.chunk, dt)
     nws = g.workspace_bytes(r.B, r.T, r.H, r.dk, r.dv, r.chunk, dt, plan)
     ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
@@ -229,84 +264,90 @@ def bench_prefill(g, torch, r, x, steps, warmup):
     S_T = torch.empty((r.B, r.H, r.dk, r.dv), dtype=torch.float32, device=dev)
     log(f"prefill {r.name}: plan {plan}, workspace {nws} B")
 
-    def step(p):
-        g.chunk_fwd(q, k, v, la, beta, S0, chunk=r.chunk, plan=p, o=o, S_T=S_T, workspace=ws)
+    def run(n, p=None, **kw):
+        for _ in range(n):
+            g.chunk_fwd(q, k, v, la, beta, S0, chunk=r.chunk, plan=plan if p is None else p, o=o, S_T=S_T,
+                        workspace=ws, **kw)
 
-    for _ in range(warmup):
-        step(plan)
-    torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for _ in range(steps):
-        step(plan)
-    t1.record()
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / steps
+    def timed(**kw):
+        run(warmup, **kw)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        run(steps, **kw)
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps
+
+    ms = timed()
 
     # per-launch durations from events the library records around each launch
     lb = launch_bytes(r, plan, es)
     nl = len(lb)
     evs = make_events(torch, 2 * nl * steps)
-    arrs = []
-    for i in range(steps):
-        arr = (ctypes.c_void_p * (2 * nl))(*[evs[2 * nl * i + j].cuda_event for j in range(2 * nl)])
-        arrs.append(arr)
+    arrs = [(ctypes.c_void_p * (2 * nl))(*[evs[2 * nl * i + j].cuda_event for j in range(2 * nl)])
+            for i in range(steps)]
     torch.cuda.synchronize()
     for i in range(steps):
         p = g.Plan(plan.n_segments, plan.dv_block, ctypes.cast(arrs[i], ctypes.POINTER(ctypes.c_void_p)), 2 * nl)
-        step(p)
+        run(1, p=p)
     torch.cuda.synchronize()
     per_launch = []
     for j, (name, nbytes) in enumerate(lb):
         d = [evs[2 * nl * i + 2 * j].elapsed_time(evs[2 * nl * i + 2 * j + 1]) for i in range(steps)]
         per_launch.append({"kernel": name, "ms": float(np.mean(d)), "bytes": int(nbytes),
                            "GBps": nbytes / (np.mean(d) * 1e-3) / 1e9})
-    log("prefill per launch:", json.dumps(per_launch))
+    log(f"prefill {r.name} per launch:", json.dumps(per_launch))
+
+    token_heads = r.B * r.T * r.H
+    flops = token_heads * prefill_flops_per_token_head(r.dk, r.dv, r.chunk)
+    nbytes = token_heads * prefill_bytes_per_token_head(r.dk, r.dv, es)
+    sec = ms * 1e-3
+    peak_mf = PEAK_BF16_TFLOPS if r.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
+    step_bytes = sum(b for _, b in lb)
+    dom = max(per_launch, key=lambda e: e["ms"])
+    res = {
+        "workload": r.name, "B": r.B, "T": r.T, "H": r.H, "dk": r.dk, "dv": r.dv, "chunk": r.chunk,
+        "plan": {"n_segments": plan.n_segments, "dv_block": plan.dv_block},
+        "ms_per_step": round(ms, 5), "tokens_per_s": round(r.B * r.T / sec, 1),
+        "roofline": {"bound": "hbm", "kernel": dom["kernel"], "achieved": round(dom["GBps"], 1),
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(dom["GBps"] / PEAK_HBM_GBPS, 4),
+                     "traffic": measured_traffic(r.name, dom["kernel"]), "launch_ms": round(dom["ms"], 5),
+                     "launch_bytes": dom["bytes"]},
+        "whole_step": {"bound": "hbm", "alg_bytes": int(step_bytes),
+                       "achieved": round(step_bytes / sec / 1e9, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                       "frac": round(step_bytes / sec / 1e9 / PEAK_HBM_GBPS, 4),
+                       "single_pass_bytes": int(nbytes),
+                       "single_pass_frac": round(nbytes / sec / (PEAK_HBM_GBPS * 1e9), 4)},
+        "mfma_frac_alg": round(flops / sec / (peak_mf * 1e12), 4),
+        "hbm_frac_alg": round(nbytes / sec / (PEAK_HBM_GBPS * 1e9), 4),
+        "roofline_frac": round(max(flops / (peak_mf * 1e12), nbytes / (PEAK_HBM_GBPS * 1e9)) / sec, 4),
+        "alg_gflop": round(flops / 1e9, 3), "alg_mb": round(nbytes / 1e6, 2),
+        "launches": per_launch,
+    }
+    ex = executed_mfma(r.name, per_launch, sec, peak_mf)
+    if ex is not None:
+        res["mfma_executed"] = ex
+    if not options:
+        return res
 
     # the same step with state checkpoints every CKPT_STRIDE tokens (prefix reuse)
-    ckpt = None
     if r.T >= CKPT_STRIDE and CKPT_STRIDE % r.chunk == 0:
         nck = r.T // CKPT_STRIDE
         sck = torch.empty((r.B, nck, r.H, r.dk, r.dv), dtype=torch.float32, device=dev)
-        for _ in range(warmup):
-            g.chunk_fwd(q, k, v, la, beta, S0, chunk=r.chunk, plan=plan, o=o, S_T=S_T, workspace=ws,
-                        ckpt_stride=CKPT_STRIDE, state_ckpt=sck)
-        torch.cuda.synchronize()
-        t0.record()
-        for _ in range(steps):
-            g.chunk_fwd(q, k, v, la, beta, S0, chunk=r.chunk, plan=plan, o=o, S_T=S_T, workspace=ws,
-                        ckpt_stride=CKPT_STRIDE, state_ckpt=sck)
-        t1.record()
-        torch.cuda.synchronize()
-        ms_ck = t0.elapsed_time(t1) / steps
-        ckpt = {"stride": CKPT_STRIDE, "checkpoints": nck, "ms_per_step": round(ms_ck, 5),
-                "overhead": round(ms_ck / ms - 1.0, 4), "extra_bytes": int(sck.numel() * 4)}
-        log("prefill with state checkpoints:", json.dumps(ckpt))
-    # the same step reading log_alpha as raw gate logits (-5 sigmoid formed in gate prep)
-    for _ in range(warmup):
-        g.chunk_fwd(q, k, v, la, beta, S0, chunk=r.chunk, plan=plan, o=o, S_T=S_T, workspace=ws, gate=g.GATE_LOGITS)
-    torch.cuda.synchronize()
-    t0.record()
-    for _ in range(steps):
-        g.chunk_fwd(q, k, v, la, beta, S0, chunk=r.chunk, plan=plan, o=o, S_T=S_T, workspace=ws, gate=g.GATE_LOGITS)
-    t1.record()
-    torch.cuda.synchronize()
-    ms_gate = t0.elapsed_time(t1) / steps
-    gate = {"ms_per_step": round(ms_gate, 5), "overhead": round(ms_gate / ms - 1.0, 4)}
-    log("prefill from gate logits:", json.dumps(gate))
-    # ... and normalising q and k inside the kernels
-    for _ in range(warmup):
-        g.chunk_fwd(q, k, v, la, beta, S0, chunk=r.chunk, plan=plan, o=o, S_T=S_T, workspace=ws, qk_norm=True)
-    torch.cuda.synchronize()
-    t0.record()
-    for _ in range(steps):
-        g.chunk_fwd(q, k, v, la, beta, S0, chunk=r.chunk, plan=plan, o=o, S_T=S_T, workspace=ws, qk_norm=True)
-    t1.record()
-    torch.cuda.synchronize()
-    ms_norm = t0.elapsed_time(t1) / steps
-    gate["with_qk_norm"] = {"ms_per_step": round(ms_norm, 5), "overhead": round(ms_norm / ms - 1.0, 4)}
-    log("prefill with q/k normalisation:", json.dumps(gate["with_qk_norm"]))
-    return ms, plan, per_launch, ckpt, gate
+        ms_ck = timed(ckpt_stride=CKPT_STRIDE, state_ckpt=sck)
+        res["with_state_checkpoints"] = {"stride": CKPT_STRIDE, "checkpoints": nck, "ms_per_step": round(ms_ck, 5),
+                                         "overhead": round(ms_ck / ms - 1.0, 4), "extra_bytes": int(sck.numel() * 4)}
+        del sck
+        log("prefill with state checkpoints:", json.dumps(res["with_state_checkpoints"]))
+    # reading log_alpha as raw gate logits (-5 sigmoid formed in gate prep), then also
+    # normalising q and k inside the kernels
+    ms_gate = timed(gate=g.GATE_LOGITS)
+    ms_norm = timed(qk_norm=True)
+    res["from_gate_logits"] = {"ms_per_step": round(ms_gate, 5), "overhead": round(ms_gate / ms - 1.0, 4)}
+    res["with_qk_norm"] = {"ms_per_step": round(ms_norm, 5), "overhead": round(ms_norm / ms - 1.0, 4)}
+    log("prefill options:", json.dumps({k: res[k] for k in ("from_gate_logits", "with_qk_norm")}))
+    return res
 
 
 def bench_speculative(g, torch, rd, d, n, reps):
@@ -438,13 +479,49 @@ def copy_bandwidth(torch, nbytes=1 << 30, reps=10):
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
+def executed_mfma(workload, per_launch, step_sec, peak_tflops):
+    """Executed MFMA work of one step from the committed rocprofv3 counter table of
+    ``workload`` (SQ_INSTS_VALU_MFMA_MOPS_BF16 / _F32 per dispatch, x 512 flops), over the
+    live step time; None when there is no table or the library sources changed since."""
+    path = os.path.join(PROFILES, f"mfma__{workload}.md")
+    if not os.path.exists(path):
+        return None
+    digest, rows = None, {}
+    for line in open(path):
+        line = line.strip()
+        if line.startswith("source digest:"):
+            digest = line.split(":", 1)[1].strip().strip("`")
+        elif line.startswith("| ") and not line.startswith(("| kernel", "|---")):
+            cells = [c.strip() for c in line.strip("|").split("|")]
+            try:
+                col = 2 if peak_tflops == PEAK_BF16_TFLOPS else 3            # bf16 or f32 MFMA flops
+                rows[cells[0]] = (float(cells[col].replace(",", "")), float(cells[4].rstrip(" %")))
+            except (ValueError, IndexError):
+                pass
+    if digest != library_source_digest():
+        return None
+    flops, busy = 0.0, {}
+    for e in per_launch:
+        if e["kernel"] not in rows:
+            return None
+        flops += rows[e["kernel"]][0]
+        busy[e["kernel"]] = rows[e["kernel"]][1]
+    return {"label": "executed (rocprofv3 counters: MFMA ops incl. masked halves and recompute)",
+            "tflop_per_step": round(flops / 1e12, 4),
+            "frac": round(flops / step_sec / (peak_tflops * 1e12), 4),
+            "mfma_busy_pct_per_kernel": busy, "table": os.path.relpath(path, ROOT)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=1, choices=[0, 1, 2, 3],
-                    help="prefill workload (0 tiny fp32, 1 B1 T4096 H16, 2 B8 T8192 H32, 3 B1 T1M H32)")
+    ap.add_argument("--workload", type=int, default=3, choices=[0, 1, 2, 3],
+                    help="headline prefill workload (0 tiny fp32, 1 B1 T4096 H16, 2 B8 T8192 H32, 3 B1 T1M H32)")
+    ap.add_argument("--side", default="1,2", help="other prefill workloads timed as side figures ('' for none)")
+    ap.add_argument("--no-options", action="store_true",
+                    help="skip the checkpoint / gate-logit / q-k norm figures of the headline step")
     ap.add_argument("--decode-reps", type=int, default=5)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -458,11 +535,16 @@ def main():
 
     r = ks.WORKLOADS[args.workload]
     rd = ks.WORKLOADS[DECODE_WORKLOAD]
-    x = None
-    if r.B * r.T * r.H <= HOST_GEN_LIMIT:
-        t = time.perf_counter()
-        x = ks.make_prefill(r)
-        log(f"generated prefill inputs in {time.perf_counter() - t:.1f}s")
+    side = [int(w) for w in args.side.split(",") if w.strip() and int(w) != args.workload]
+    hosts = {}
+    for w in [args.workload] + side:
+        rw = ks.WORKLOADS[w]
+        if rw.B * rw.T * rw.H <= HOST_GEN_LIMIT:
+            t = time.perf_counter()
+            hosts[w] = ks.make_prefill(rw)
+            log(f"generated {rw.name} inputs in {time.perf_counter() - t:.1f}s")
+        else:
+            hosts[w] = None
     d = None
     if not args.no_decode:
         t = time.perf_counter()
@@ -472,7 +554,7 @@ def main():
     # CPU baseline first: the worker processes fork before the GPU is touched
     cpu_pre = cpu_dec = None
     if not args.no_cpu_baseline:
-        cpu_pre = cpu_baseline_prefill(r, x)
+        cpu_pre = cpu_baseline_prefill(r, hosts[args.workload])
         log("cpu baseline prefill:", json.dumps(cpu_pre))
         if d is not None:
             cpu_dec = cpu_baseline_decode(rd, d, 128)
@@ -482,21 +564,21 @@ def main():
     import gated_delta_rule_107_amd as g
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
     props = torch.cuda.get_device_properties(0)
     log(f"device: {props.name} {getattr(props, 'gcnArchName', '')} CUs={props.multi_processor_count}")
 
-    ms, plan, per_launch, ckpt, gate = bench_prefill(g, torch, r, x, args.steps, args.warmup)
-    es = 2 if r.dtype == "bf16" else 4
-    token_heads = r.B * r.T * r.H
-    flops = token_heads * prefill_flops_per_token_head(r.dk, r.dv, r.chunk)
-    nbytes = token_heads * prefill_bytes_per_token_head(r.dk, r.dv, es)
-    sec = ms * 1e-3
-    peak_mf = PEAK_BF16_TFLOPS if r.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
-    dom = max(per_launch, key=lambda e: e["ms"])
-    roofline = {"bound": "hbm", "kernel": dom["kernel"], "achieved": round(dom["GBps"], 1),
-                "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(dom["GBps"] / PEAK_HBM_GBPS, 4),
-                "traffic": measured_traffic(r.name, dom["kernel"]), "launch_ms": round(dom["ms"], 5),
-                "launch_bytes": dom["bytes"]}
+    xd = prefill_inputs(torch, r, hosts.pop(args.workload), dev)
+    head = time_prefill(g, torch, r, xd, args.steps, args.warmup, options=not args.no_options)
+    del xd
+    torch.cuda.empty_cache()
+    sides = {}
+    for w in side:
+        rw = ks.WORKLOADS[w]
+        xw = prefill_inputs(torch, rw, hosts.pop(w), dev)
+        sides[rw.name] = time_prefill(g, torch, rw, xw, max(args.steps, 10), args.warmup)
+        del xw
+        torch.cuda.empty_cache()
 
     dec = None
     if d is not None:
@@ -513,28 +595,30 @@ def main():
         log("decode:", json.dumps(dec))
     copy_gbps = copy_bandwidth(torch)
 
+    prefill = {k: head[k] for k in ("mfma_frac_alg", "hbm_frac_alg", "roofline_frac", "alg_gflop", "alg_mb",
+                                     "whole_step", "launches")}
+    for k in ("mfma_executed", "with_state_checkpoints", "from_gate_logits", "with_qk_norm"):
+        if k in head:
+            prefill[k] = head[k]
     out = {
         "metric": METRIC,
-        "value": round(r.B * r.T / sec, 1),
+        "value": head["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 5),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": r.dtype,
         "data": "synthetic",
         "config": {"workload": r.name, "B": r.B, "T": r.T, "H": r.H, "dk": r.dk, "dv": r.dv,
-                   "chunk": r.chunk, "plan": {"n_segments": plan.n_segments, "dv_block": plan.dv_block}},
-        "roofline": roofline,
+                   "chunk": r.chunk, "plan": head["plan"]},
+        "roofline": head["roofline"],
         "cpu_baseline": cpu_pre,
-        "prefill": {"mfma_frac_alg": round(flops / sec / (peak_mf * 1e12), 4),
-                    "hbm_frac_alg": round(nbytes / sec / (PEAK_HBM_GBPS * 1e9), 4),
-                    "roofline_frac": round(max(flops / (peak_mf * 1e12), nbytes / (PEAK_HBM_GBPS * 1e9)) / sec, 4),
-                    "alg_gflop": round(flops / 1e9, 3), "alg_mb": round(nbytes / 1e6, 2),
-                    "launches": per_launch, "with_state_checkpoints": ckpt, "from_gate_logits": gate},
+        "prefill": prefill,
+        "side_prefill": sides,
         "decode": dec,
         "hbm_copy_GBps": round(copy_gbps, 1),
     }
