@@ -31,7 +31,10 @@
 // 16x16 diagonal blocks of (I + Diag(beta) A) are inverted by fp32 forward
 // substitution; then the state chain runs per wave on its 16 state columns: the
 // block triangular solve for U on MFMA straight from registers
-// (U_p = N_pp (R_p - sum_q Ab_pq U_q)), O, and the state update.  The loop is
+// (U_p = N_pp (R_p - sum_q Ab_pq U_q)), O, and the state update.  In the solve N_pp,
+// Ab_pq = -beta A_pq and U are bf16 operands, but R_p enters the N_pp product split into
+// bf16 high and low parts: rounding R_p alone carried nearly all of the solve's rounding
+// error into U and the state.  The loop is
 // software-pipelined by one chunk: the chain of chunk n (MFMA latency) shares its
 // barrier interval with the gate prep of chunk n+1 (VALU work).  The fp32 state
 // stays in MFMA accumulators for the whole sequence; accumulator tiles feed the next
@@ -77,6 +80,22 @@ template <> struct MM<bf16> {
         const bf16x4 a = *reinterpret_cast<const bf16x4*>(A + (r0 + (lane & 15)) * ld + c0 + 4 * (lane >> 4));
         return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
                                                          __builtin_bit_cast(i16x4, b), acc, 0, 0, 0);
+    }
+    // A[r0 + m][c0 + kk] * R[kk][n] over kk < 16 with R given in float32 (accumulator layout) and
+    // kept to about 16 bits: R = hi + lo, both bf16, two products from one load of A.  Used for
+    // the diagonal blocks of the WY solve, U_p = N_pp R_p, where rounding R_p to bf16 would
+    // carry most of the solve's rounding error into U and the state.
+    static __device__ __forceinline__ f32x4 k16_split(const bf16* A, int ld, int r0, int c0, const f32x4& R,
+                                                      int lane) {
+        const bf16x4 a = *reinterpret_cast<const bf16x4*>(A + (r0 + (lane & 15)) * ld + c0 + 4 * (lane >> 4));
+        const B16 hi = b16(R);
+        const B16 lo = pack_bf16x4(R[0] - (float)hi[0], R[1] - (float)hi[1], R[2] - (float)hi[2],
+                                   R[3] - (float)hi[3]);
+        const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
+        const f32x4 u = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
+                                                                 __builtin_bit_cast(i16x4, hi), z, 0, 0, 0);
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a), __builtin_bit_cast(i16x4, lo),
+                                                         u, 0, 0, 0);
     }
     // the same over 32 contraction rows given as two tiles (rows c0.. and c0+16..), as a load
     // of the A operand and the product, so that callers can have several loads in flight
@@ -152,6 +171,10 @@ template <> struct MM<float> {
                                                 f32x4 acc, int lane) {
         acc = k16(A, ld, r0, c0, b0, acc, lane);
         return k16(A, ld, r0, c0 + 16, b1, acc, lane);
+    }
+    static __device__ __forceinline__ f32x4 k16_split(const float* A, int ld, int r0, int c0, const f32x4& R,
+                                                      int lane) {
+        return k16(A, ld, r0, c0, R, f32x4{0.f, 0.f, 0.f, 0.f}, lane);
     }
     struct A32 { f32x4 lo, hi; };
     static __device__ __forceinline__ A32 ld32(const float* A, int ld, int r0, int c0, int lane) {
@@ -600,8 +623,7 @@ __global__ __launch_bounds__(512) void chunk_kernel(ChunkArgs a) {
                         R[r] = sb_c[16 * p + g4 + r] * ((G == 0 ? (float)vr[p][r] : 0.f) - X[G][p][r]);
 #pragma unroll
                     for (int q = 0; q < p; ++q) R = MF::k16(s_an, LC, 16 * p, 16 * q, ub[G][q], R, lane);
-                    const f32x4 U = MF::k16(s_an, LC, 16 * p, 16 * p, MF::b16(R), f32x4{0.f, 0.f, 0.f, 0.f}, lane);
-                    ub[G][p] = MF::b16(U);
+                    ub[G][p] = MF::b16(MF::k16_split(s_an, LC, 16 * p, 16 * p, R, lane));
                 }
             }
         }
