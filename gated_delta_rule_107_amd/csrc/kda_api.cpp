@@ -64,10 +64,14 @@ kda_status_t check_problem(int64_t B, int64_t T, int32_t H, int32_t dk, int32_t 
 }
 
 struct Resolved {
-    int32_t n_seg;
-    int64_t seg_len;
+    int32_t n_seg;          // segments per sequence; packed sequences: slots of the segment table
+    int64_t seg_len;        // tokens per segment, a multiple of the chunk
     int32_t dv_block;
+    bool packed_seg;        // packed sequences cut into segments (segment tables in the workspace)
+    int32_t n_seqs;         // packed sequences (0 without cu_seqlens)
 };
+
+constexpr int64_t kMaxSlots = 1 << 22;   // segment-table entries of one packed call
 
 kda_status_t resolve_plan(int64_t B, int64_t T, int32_t H, int32_t dk, int32_t dv, int32_t chunk,
                           kda_dtype_t dt, const kda_plan_t* plan, Resolved* out) {
@@ -81,9 +85,34 @@ kda_status_t resolve_plan(int64_t B, int64_t T, int32_t H, int32_t dk, int32_t d
     const int64_t nchunks = (T + chunk - 1) / chunk;
     int64_t nseg = p.n_segments;
     if (nseg < 0) return fail(KDA_ERR_UNSUPPORTED, "n_segments must be >= 0");
+    out->packed_seg = false;
+    out->n_seqs = 0;
+    out->dv_block = dvb;
     if (p.cu_seqlens) {
-        if (nseg > 1) return fail(KDA_ERR_UNSUPPORTED, "packed sequences (cu_seqlens) run in one pass");
-        nseg = 1;
+        // Packed sequences: n_segments is the number of segments the packed row is cut into;
+        // every sequence is split into segments of that length (whole chunks, at least two), so
+        // only the sequences longer than it are split.  Default: one pass when the (sequence,
+        // head, column block) units cover the compute units, else enough segments to cover them.
+        const int64_t ns = p.n_seqs;
+        if (ns < 1) return fail(KDA_ERR_SHAPE, "n_seqs must be >= 1 (got %lld)", (long long)ns);
+        out->n_seqs = (int32_t)ns;
+        const int64_t per_slot = (int64_t)H * (dv / dvb);
+        if (nseg == 0) nseg = ns * per_slot < kPlanCUs ? (kPlanCUs + per_slot - 1) / per_slot : 1;
+        int64_t seg_chunks = nchunks == 0 ? 1 : (nchunks + nseg - 1) / nseg;
+        if (seg_chunks < 2) seg_chunks = 2;
+        if (nseg > 1 && seg_chunks < nchunks) {
+            if (T >= ((int64_t)1 << 31)) return fail(KDA_ERR_UNSUPPORTED, "packed sequences with segments need T < 2^31");
+            const int64_t seg_len = seg_chunks * chunk;
+            const int64_t slots = (T + seg_len - 1) / seg_len + ns;
+            if (slots > kMaxSlots) return fail(KDA_ERR_UNSUPPORTED, "too many segments for packed sequences");
+            out->packed_seg = true;
+            out->n_seg = (int32_t)slots;
+            out->seg_len = seg_len;
+            return KDA_OK;
+        }
+        out->n_seg = 1;
+        out->seg_len = nchunks * chunk;
+        return KDA_OK;
     }
     if (nseg == 0) {
         // enough workgroups to cover every compute unit; segments only when (b, h, column
@@ -106,9 +135,15 @@ kda_status_t resolve_plan(int64_t B, int64_t T, int32_t H, int32_t dk, int32_t d
     return KDA_OK;
 }
 
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Segment workspace: S_loc, M (two bf16 planes, the bytes of one float plane) and the start
+// states of every (sequence or slot, head, segment), then the segment tables of packed sequences.
 size_t workspace_for(int64_t B, int32_t H, int32_t dk, int32_t dv, const Resolved& r) {
-    if (r.n_seg <= 1) return 0;
-    return (size_t)B * H * r.n_seg * ((size_t)2 * dk * dv + (size_t)dk * dk) * sizeof(float);
+    if (r.n_seg <= 1 && !r.packed_seg) return 0;
+    size_t n = (size_t)B * H * r.n_seg * ((size_t)2 * dk * dv + (size_t)dk * dk) * sizeof(float);
+    if (r.packed_seg) n = align256(n) + align256((size_t)r.n_seg * 16) + (size_t)r.n_seqs * 8;
+    return n;
 }
 
 // Records the caller's timing events around each kernel launch of one call.
@@ -288,15 +323,17 @@ kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, const f
     if (trace_on()) {
         std::fprintf(stderr,
                      "kda_chunk_fwd%s: B=%lld T=%lld H=%d dk=%d dv=%d chunk=%d dtype=%s sequences=%lld "
-                     "n_segments=%d seg_len=%lld dv_block=%d workspace=%zu flags=0x%x checkpoints=%s "
+                     "%s=%d seg_len=%lld dv_block=%d workspace=%zu flags=0x%x checkpoints=%s "
                      "launches=%s\n",
                      library_scratch ? "_noalloc" : "", (long long)B, (long long)T, H, dk, dv, chunk,
-                     dt == KDA_DTYPE_BF16 ? "bf16" : "f32", (long long)n_seq, r.n_seg, (long long)r.seg_len,
+                     dt == KDA_DTYPE_BF16 ? "bf16" : "f32", (long long)n_seq,
+                     r.packed_seg ? "segment_slots" : "n_segments", r.n_seg, (long long)r.seg_len,
                      r.dv_block, need, flags, ckpt ? "yes" : "no",
-                     r.n_seg == 1 ? "chunk" : "segment-pass-1,scan,segment-pass-2");
+                     r.packed_seg ? "segment-table,segment-pass-1,scan,segment-pass-2"
+                                  : (r.n_seg == 1 ? "chunk" : "segment-pass-1,scan,segment-pass-2"));
     }
     hipError_t e;
-    if (r.n_seg == 1) {
+    if (r.n_seg == 1 && !r.packed_seg) {
         a.mode = 0;
         a.s0 = S0;
         tm.before();
@@ -310,6 +347,21 @@ kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, const f
     float* s_loc = ws;
     float* m_tr = s_loc + per * dk * dv;
     float* starts = m_tr + per * dk * dk;
+    const int2* seq_table = nullptr;
+    if (r.packed_seg) {
+        // packed sequences: the segment tables, built on the device from cu_seqlens
+        char* tab = reinterpret_cast<char*>(workspace) + align256(per * (2 * (size_t)dk * dv + (size_t)dk * dk) * 4);
+        kda::SegTableArgs t{cu, T, r.seg_len, r.n_seqs, r.n_seg, reinterpret_cast<int4*>(tab),
+                            reinterpret_cast<int2*>(tab + align256((size_t)r.n_seg * 16))};
+        tm.before();
+        e = kda::launch_seg_table(t, st);
+        tm.after();
+        if (e != hipSuccess) return hip_fail(e, "segment table launch");
+        a.seg_table = t.seg_table;
+        a.cu_seqlens = nullptr;
+        a.B = 1;
+        seq_table = t.seq_table;
+    }
     // pass 1: segment pairs
     a.mode = 1;
     a.s_loc = s_loc;
@@ -319,7 +371,7 @@ kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, const f
     tm.after();
     if (e != hipSuccess) return hip_fail(e, "segment pass-1 launch");
     // prefix scan over the pairs
-    kda::ScanArgs sc{S0, s_loc, m_tr, starts, B, H, dk, dv, r.n_seg};
+    kda::ScanArgs sc{S0, s_loc, m_tr, starts, r.packed_seg ? (int64_t)r.n_seqs : B, H, dk, dv, r.n_seg, seq_table};
     tm.before();
     e = kda::launch_scan(sc, st);
     tm.after();

@@ -54,6 +54,10 @@ struct ChunkArgs {
     int64_t seg_len;        // tokens per segment, a multiple of chunk
     int32_t dv_block;       // columns per workgroup (16 per wave)
     const int32_t* cu_seqlens;  // [B + 1] packed sequence offsets into one batch row, or null
+    // packed sequences with segments (seg_table non-null; B = 1, n_seg = the table's length):
+    // entry g = {sequence or -1, t_begin, t_end, SEG_FIRST | SEG_LAST}; state rows are
+    // sequences, and pairs / start states of slot g of head h sit at index h * n_seg + g
+    const int4* seg_table;
     float* ckpt;            // [B, T / ckpt_stride, H, dk, dv] state checkpoints (mode 0) or null
     int64_t ckpt_stride;    // tokens between checkpoints, a multiple of chunk
     uint32_t flags;         // kda_input_flag_t bits (gate logits, q/k L2 normalisation)
@@ -64,17 +68,34 @@ struct ChunkArgs {
 hipError_t launch_chunk(const ChunkArgs& a, hipStream_t st);
 
 // Prefix scan over segment pairs: starts[i+1] = M_i starts[i] + S_loc_i,
-// starts[0] = s0 (or zeros); writes starts[1 .. P-1].
+// starts[0] = s0 (or zeros); writes starts[0 .. P-1].
 struct ScanArgs {
     const float* s0;
     const float* s_loc;     // [B,H,P][dk dv], sloc_index order
     const void* m_tr;       // [B,H,P][2][dk^2] bf16: high and low parts of M (hi + lo ~ M), mtr_index order
     float* starts;
-    int64_t B;
+    int64_t B;              // (packed sequences: the number of sequences)
     int32_t H, dk, dv, n_seg;
+    // packed sequences with segments: entry i = {first slot, number of segments} of sequence i;
+    // its pairs and starts for head h sit at h * n_seg + first slot + j
+    const int2* seq_table;
 };
 
 hipError_t launch_scan(const ScanArgs& a, hipStream_t st);
+
+// Segment tables of packed sequences (see ChunkArgs::seg_table, ScanArgs::seq_table): sequence
+// i covers tokens [cu[i], cu[i+1]) clamped into [end of sequence i-1, T], cut into segments of
+// seg_len tokens (at least one, also when empty); slots past the last segment get sequence -1.
+constexpr int SEG_FIRST = 1, SEG_LAST = 2;
+struct SegTableArgs {
+    const int32_t* cu_seqlens;  // [n_seqs + 1]
+    int64_t T, seg_len;
+    int32_t n_seqs, n_slots;    // n_slots >= ceil(T / seg_len) + n_seqs
+    int4* seg_table;            // [n_slots]
+    int2* seq_table;            // [n_seqs]
+};
+
+hipError_t launch_seg_table(const SegTableArgs& a, hipStream_t st);
 
 // Position of M[row][k] inside one dk^2 plane of a segment transition: the order in which the
 // scan's MFMA reads its A operand, so that each of its loads is one contiguous run of 64 x 16

@@ -69,7 +69,15 @@ __global__ __launch_bounds__(64 * (DK / 16 + 1)) void scan_kernel(ScanArgs a) {
             jb = (int)(r2 / ntail);
         }
     }
-    const int P = a.n_seg, dv = a.dv;
+    // this (sequence, head)'s segments: P of them, pairs and starts at base + i
+    int P = a.n_seg;
+    int64_t base = bh * P;
+    if (a.seq_table) {
+        const int2 e = a.seq_table[bh / a.H];
+        P = e.y;
+        base = (bh % a.H) * (int64_t)a.n_seg + e.x;
+    }
+    const int dv = a.dv;
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int m = lane & 15, g = lane >> 4;
     const int col = 16 * jb + m;                  // state column of this lane (B / C layouts)
@@ -102,7 +110,7 @@ __global__ __launch_bounds__(64 * (DK / 16 + 1)) void scan_kernel(ScanArgs a) {
     // per lane, read as one piece from the row-major copy
     auto store_start = [&](int i) {
         const float* f = s_f[i & 1];
-        float* dst = a.starts + (bh * P + i) * DK * dv + 16 * jb;
+        float* dst = a.starts + (base + i) * DK * dv + 16 * jb;
         // every read first, then the stores: one LDS round trip per step, not one per store
         f32x4 v[DK / 16];
 #pragma unroll
@@ -149,7 +157,7 @@ __global__ __launch_bounds__(64 * (DK / 16 + 1)) void scan_kernel(ScanArgs a) {
     bf16x8 ma0[2][KSTEP], ma1[2][KSTEP];                        // [plane][step] of M_i: even / odd i
     f32x4 sl0, sl1;                                             // S_loc_i: even / odd i
     auto load_m = [&](int i, bf16x8 (&dst)[2][KSTEP]) {
-        const bf16* M = mt + (bh * P + i) * 2 * DK * DK;
+        const bf16* M = mt + (base + i) * 2 * DK * DK;
 #pragma unroll
         for (int pl = 0; pl < 2; ++pl)
 #pragma unroll
@@ -160,7 +168,7 @@ __global__ __launch_bounds__(64 * (DK / 16 + 1)) void scan_kernel(ScanArgs a) {
             }
     };
     auto load_sloc = [&](int i, f32x4& dst) {
-        const float* L = a.s_loc + (bh * P + i) * DK * dv;        // sloc_index order
+        const float* L = a.s_loc + (base + i) * DK * dv;          // sloc_index order
         dst = *reinterpret_cast<const f32x4*>(L + sloc_index(DK, row0 + 4 * g, col));
     };
     if (nsteps > 0) {
@@ -202,6 +210,62 @@ __global__ __launch_bounds__(64 * (DK / 16 + 1)) void scan_kernel(ScanArgs a) {
     }
     if (i < nsteps) step(i, Set<false>{});
     lds_barrier();                                // the last start is in LDS for the store wave
+}
+
+// Segment tables of packed sequences: one wave walks the sequences 64 at a time.  A sequence's
+// range starts no earlier than the previous one's end (clamped into [0, T]), so the segments
+// of any offsets array, valid or not, fit the n_slots >= ceil(T / seg_len) + n_seqs entries.
+__global__ __launch_bounds__(64) void seg_table_kernel(SegTableArgs a) {
+    const int lane = threadIdx.x;
+    int64_t prev_end = 0;                        // end of the sequence before this group of 64
+    int g0 = 0;                                  // first slot of this group's first sequence
+    for (int i0 = 0; i0 < a.n_seqs; i0 += 64) {
+        const int i = i0 + lane;
+        const bool on = i < a.n_seqs;
+        int64_t c0 = on ? a.cu_seqlens[i] : a.T, c1 = on ? a.cu_seqlens[i + 1] : a.T;
+        c1 = c1 < 0 ? 0 : (c1 > a.T ? a.T : c1);
+        c0 = c0 < 0 ? 0 : (c0 > a.T ? a.T : c0);
+        if (c1 < c0) c1 = c0;
+        // monotone ends: end_i = max over j <= i of c1_j (inclusive scan of maxima); begin_i =
+        // max(c0_i, end_{i-1})
+        int64_t end = c1;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int64_t o = __shfl_up(end, d, 64);
+            if (lane >= d && o > end) end = o;
+        }
+        if (prev_end > end) end = prev_end;
+        int64_t before = __shfl_up(end, 1, 64);
+        if (lane == 0) before = prev_end;
+        const int64_t beg = c0 > before ? (c0 < end ? c0 : end) : before;
+        const int64_t len = end - beg;
+        const int cnt = on ? (int)(len > 0 ? (len + a.seg_len - 1) / a.seg_len : 1) : 0;
+        // exclusive scan of the counts
+        int incl = cnt;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int o = __shfl_up(incl, d, 64);
+            if (lane >= d) incl += o;
+        }
+        const int first = g0 + incl - cnt;
+        if (on) {
+            a.seq_table[i] = make_int2(first, cnt);
+            for (int j = 0; j < cnt; ++j) {
+                const int64_t tb = beg + (int64_t)j * a.seg_len;
+                const int64_t te = tb + a.seg_len < end ? tb + a.seg_len : end;
+                const int flags = (j == 0 ? SEG_FIRST : 0) | (j == cnt - 1 ? SEG_LAST : 0);
+                if (first + j < a.n_slots) a.seg_table[first + j] = make_int4(i, (int)tb, (int)te, flags);
+            }
+        }
+        g0 += __shfl(incl, 63, 64);
+        prev_end = __shfl(end, 63, 64);
+    }
+    for (int g = g0 + lane; g < a.n_slots; g += 64) a.seg_table[g] = make_int4(-1, 0, 0, 0);
+}
+
+hipError_t launch_seg_table(const SegTableArgs& a, hipStream_t st) {
+    hipLaunchKernelGGL(seg_table_kernel, dim3(1), dim3(64), 0, st, a);
+    return hipGetLastError();
 }
 
 template <int DK>

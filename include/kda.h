@@ -108,10 +108,17 @@ typedef enum {
  *   cu_seqlens is not NULL the call takes B == 1 and n_seqs sequences packed
  *   along T: sequence i owns tokens [cu_seqlens[i], cu_seqlens[i+1]) (device
  *   int32 array of n_seqs + 1 nondecreasing offsets from 0 to T; chunks start
- *   at each sequence's first token), and S0 / S_T are [n_seqs, H, dk, dv].  One
- *   pass only (n_segments 0 or 1) and no state checkpoints.  The offsets are
- *   read on the device: values outside [0, T] are clamped, other invalid
- *   arrays give unspecified (but in-bounds) results.
+ *   at each sequence's first token), and S0 / S_T are [n_seqs, H, dk, dv].  No
+ *   state checkpoints.  The offsets are read on the device: values outside
+ *   [0, T] are clamped, other invalid arrays give unspecified (but in-bounds)
+ *   results.  With packed sequences n_segments > 1 cuts the packed row into
+ *   that many segments: every sequence is split into segments of
+ *   ceil(T / n_segments) tokens (rounded up to whole chunks, at least two
+ *   chunks), so only sequences longer than that are split, each with its own
+ *   prefix scan; 0 = one pass when the (sequence, head, column block) units
+ *   cover MI355X's 256 compute units, else enough segments to cover them
+ *   (needs T < 2^31; the segment tables are built on the device from
+ *   cu_seqlens inside the workspace).
  * flags: kda_input_flag_t bits (0 = log-decays, q and k used as given).
  * A zeroed plan (all fields 0 / NULL) means "library default" for each field.
  */

@@ -45,6 +45,10 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t) {
     g_launches.push_back({"decode", a.mode, a.N, a.n_tok, 0, 0, 0, nullptr});
     return hipSuccess;
 }
+hipError_t launch_seg_table(const SegTableArgs& a, hipStream_t) {
+    g_launches.push_back({"segtable", -1, a.n_seqs, a.T, a.n_slots, a.seg_len, 0, a.seg_table});
+    return hipSuccess;
+}
 hipError_t scratch_address(void** out) {
     *out = g_scratch_stub;
     return hipSuccess;
@@ -170,6 +174,40 @@ void chunk_launches() {
     kda_plan_t p{};
     CHECK(kda_chunk_fwd_default_plan(1, 1 << 20, 32, 128, 128, 64, KDA_DTYPE_BF16, &p) == KDA_OK, "plan query");
     CHECK(p.n_segments == 8 && p.dv_block == 128, "1M plan %d / %d", p.n_segments, p.dv_block);
+    // packed sequences with segments: segment table, pass 1, scan, pass 2; segments of
+    // ceil(T / n_segments) tokens rounded up to whole chunks; ceil(T / seg_len) + n_seqs slots
+    Call pk;
+    pk.T = 70000; pk.H = 4; pk.dk = pk.dv = 128; pk.chunk = 64; pk.dt = KDA_DTYPE_BF16;
+    pk.plan.n_segments = 0;
+    pk.plan.cu_seqlens = P<int32_t>(10);
+    pk.plan.n_seqs = 5;
+    pk.S0 = P<float>(5);
+    size_t need_pk = 0;
+    CHECK(kda_chunk_fwd_workspace_bytes(1, 70000, 4, 128, 128, 64, KDA_DTYPE_BF16, &pk.plan, &need_pk) == KDA_OK,
+          "packed ws query: %s", kda_last_error());
+    expect_reject(pk, KDA_ERR_WORKSPACE, "packed segments without a workspace");
+    pk.ws = A(8);
+    pk.wsb = need_pk;
+    g_launches.clear();
+    CHECK(pk.run() == KDA_OK, "packed segments: %s", kda_last_error());
+    CHECK(g_launches.size() == 4, "packed segments: %zu launches", g_launches.size());
+    if (g_launches.size() == 4) {
+        // 64 target segments over 70,000 tokens: 1094 -> 18 chunks = 1152 tokens; 61 + 5 slots
+        CHECK(g_launches[0].what == "segtable" && g_launches[0].seg_len == 1152 && g_launches[0].n_seg == 66,
+              "table: seg_len %lld slots %d", (long long)g_launches[0].seg_len, g_launches[0].n_seg);
+        CHECK(g_launches[1].what == "pass1" && g_launches[1].n_seg == 66 && g_launches[1].B == 1, "packed pass 1");
+        CHECK(g_launches[2].what == "scan" && g_launches[2].B == 5 && g_launches[2].n_seg == 66, "packed scan");
+        CHECK(g_launches[3].what == "chunk" && g_launches[3].mode == 0, "packed pass 2");
+        CHECK(need_pk == 256 * ((66u * 4 * 3 * 128 * 128 * 4 + 255) / 256) + 256 * ((66 * 16 + 255) / 256) + 5 * 8,
+              "packed workspace %zu", need_pk);
+    }
+    // packed sequences that already cover the compute units: one pass
+    Call pk1 = pk;
+    pk1.plan.n_seqs = 64;
+    pk1.ws = nullptr;
+    pk1.wsb = 0;
+    g_launches.clear();
+    CHECK(pk1.run() == KDA_OK && g_launches.size() == 1, "64 packed sequences x 4 heads: one pass");
     // T = 0: one launch that copies S0 into S_T
     Call z;
     z.T = 0;

@@ -173,7 +173,7 @@ def test_chunk_fwd_packed_sequence_errors(lib):
         return p
     assert call_chunk(lib, B=2, plan=plan_cu(3)) == SHAPE           # packed means one batch row
     assert call_chunk(lib, plan=plan_cu(0)) == SHAPE
-    assert call_chunk(lib, plan=plan_cu(3, nseg=2)) == UNSUP        # one pass only
+    assert call_chunk(lib, plan=plan_cu(3, nseg=2)) == WS           # segments need the workspace
     assert call_chunk(lib, plan=plan_cu(3, ck=A[9])) == UNSUP       # no checkpoints
     p = plan_cu(3)
     p.cu_seqlens = A[10] + 2

@@ -512,6 +512,53 @@ def test_packed_sequences(g, dtype, lens, H, dk, dv, chunk):
         check(o[:, a:b], S[i:i + 1], o_ref, S_ref, TOL[dtype], f"sequence {i} ({b - a} tokens)")
 
 
+@pytest.mark.parametrize("dtype,lens,H,dk,dv,chunk,nseg", [
+    # one long sequence among short ones, the default plan (segments of the long one only)
+    ("bf16", [65536, 300, 0, 1, 2000, 64, 129], 2, 128, 128, 64, 0),
+    # an explicit segment count, fewer value columns than key channels, float32
+    ("f32", [200, 17, 0, 90, 33], 2, 32, 16, 16, 4),
+], ids=["bf16-long-and-short", "f32-explicit"])
+def test_packed_sequences_with_segments(g, dtype, lens, H, dk, dv, chunk, nseg):
+    """Packed batch (cu_seqlens) whose long sequences are cut into segments, each sequence with
+    its own prefix scan (orkas.ai page, section "The cost comes back in the serving stack"):
+    every sequence's o and final state against the oracle run on that sequence alone; the long
+    sequence also chunk by chunk."""
+    import torch
+    T = sum(lens)
+    r = small_recipe(dtype, 1, T, H, dk, dv, chunk)
+    _say(f"case: packed sequences with segments {lens} {dtype} H{H} {dk}/{dv} chunk {chunk} n_segments {nseg}")
+    x = ks.make_prefill(r)
+    N = len(lens)
+    rs = r.with_shape(s0_std=0.05)
+    S0 = np.stack([np.stack([ks.gen_state(rs, i, h) for h in range(H)]) for i in range(N)])
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    args = [dev_tensor(x[n], dt) for n in ("q", "k", "v")]
+    args += [dev_tensor(x["log_alpha"], torch.float32), dev_tensor(x["beta"], torch.float32),
+             dev_tensor(S0, torch.float32)]
+    cu_d = torch.from_numpy(cu).cuda()
+    plan = g.Plan(nseg, 0)
+    plan.cu_seqlens, plan.n_seqs = cu_d.data_ptr(), N
+    nws = g.workspace_bytes(1, T, H, dk, dv, chunk, dt, plan)
+    assert nws > 0, "the plan should cut the long sequences into segments"
+    o, S = g.chunk_fwd(*args, chunk=chunk, plan=g.Plan(nseg, 0), cu_seqlens=cu_d)
+    torch.cuda.synchronize()
+    o, S = to_np(o), to_np(S)
+    for i in range(N):
+        a, b = int(cu[i]), int(cu[i + 1])
+        if b == a:
+            assert np.array_equal(S[i:i + 1], S0[i:i + 1].astype(np.float64)), "an empty sequence keeps its state"
+            continue
+        sl = lambda t: t[:, a:b]  # noqa: E731
+        o_ref, S_ref = oracle.kda_chunked(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["log_alpha"]),
+                                          sl(x["beta"]), S0[i:i + 1], chunk=chunk)
+        what = f"sequence {i} ({b - a} tokens)"
+        if b - a >= 4 * 64:
+            check_full(o[:, a:b], S[i:i + 1], o_ref, S_ref, TOL[dtype], CHUNK_TOL[dtype], what, chunk=chunk)
+        else:
+            check(o[:, a:b], S[i:i + 1], o_ref, S_ref, TOL[dtype], what)
+
+
 # ------------------------------------------------------------------ gate activation with a floor
 
 @pytest.mark.parametrize("dtype,B,T,H,dk,dv,chunk,nseg", [
