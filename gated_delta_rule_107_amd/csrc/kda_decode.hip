@@ -23,9 +23,9 @@
 
 namespace kda {
 
-template <int DK, int DV> struct DecodeMap {
+template <int DK, int DV, int MAXT = 1024> struct DecodeMap {
     static constexpr int CG = DV / 4;                                  // float4 column groups
-    static constexpr int RG = (DK < 1024 / CG) ? DK : 1024 / CG;       // row groups
+    static constexpr int RG = (DK < MAXT / CG) ? DK : MAXT / CG;       // row groups
     static constexpr int RPT = DK / RG;                                // rows per thread
     static constexpr int NT = CG * RG;                                 // threads
     static constexpr int NTB = NT < WAVE ? WAVE : NT;                  // block (whole waves)
@@ -218,6 +218,219 @@ __global__ __launch_bounds__((DecodeMap<DK, DV>::NTB)) __attribute__((amdgpu_wav
     }
 }
 
+// positions of A_ts (s < t) and M_ts (s <= t) among a group's small products
+__host__ __device__ constexpr int a_index(int t, int s) { return t * (t - 1) / 2 + s; }
+__host__ __device__ constexpr int m_index(int t, int s) { return 6 + t * (t + 1) / 2 + s; }
+
+// Speculative verify in chunk form.  Verify never writes the state, so instead of n
+// successive steps (three barriers each) it evaluates its drafts in groups of up to VG as one
+// chunk from the state in registers, with Gamma_t the cumulative log-decay over the group's
+// drafts 0..t:
+//     X_t = S^T (k_t e^Gamma_t),  Y_t = S^T (q_t e^Gamma_t)                 (one pass over S)
+//     A_ts = sum_c k_tc k_sc e^(Gamma_tc - Gamma_sc)  (s < t),  M_ts = ... q_tc ...  (s <= t)
+//     u_t = beta_t (v_t - X_t - sum_{s<t} A_ts u_s),  o_t = Y_t + sum_{s<=t} M_ts u_s
+// which is the token recurrence unrolled over the group (the chunk equations at chunk length
+// VG).  A group costs two barriers: after the per-draft vectors and small products, and after
+// the partial column sums.  Longer draft lists advance the register state between groups,
+// S <- Diag(e^Gamma_last) S + sum_t (k_t e^(Gamma_last - Gamma_t)) u_t^T, so no cumulative
+// decay spans more than VG drafts.  With normalisation the raw k, q are used and the norms
+// scale the results in the reducer.
+// 512 threads per (n, h), 8 state rows each, at up to 128 VGPRs (4 waves per SIMD): two
+// workgroups per CU, so as much of the state is in flight as with the step kernel.
+constexpr int VERIFY_THREADS = 512;
+template <typename ET, int DK, int DV, bool NORM>
+__global__ __launch_bounds__((DecodeMap<DK, DV, VERIFY_THREADS>::NTB)) __attribute__((amdgpu_waves_per_eu(4))) void verify_kernel(
+    const float* __restrict__ state, const ET* __restrict__ q, const ET* __restrict__ k,
+    const ET* __restrict__ v, const float* __restrict__ log_alpha, const float* __restrict__ beta,
+    ET* __restrict__ o, int H, int n_tok, unsigned flags) {
+    using DM = DecodeMap<DK, DV, VERIFY_THREADS>;
+    constexpr int CG = DM::CG, RG = DM::RG, RPT = DM::RPT, NT = DM::NT, NWV = DM::NWV;
+    constexpr int VG = 4;                                // drafts per group
+    constexpr int NA = VG * (VG - 1) / 2, NM = VG * (VG + 1) / 2;
+    constexpr int NSM = NA + NM + 2 * VG;                // small products per channel
+    static_assert(m_index(0, 0) == NA, "small-product positions assume groups of 4");
+    constexpr int NCW = (DK + WAVE - 1) / WAVE;          // waves of the channel threads
+    static_assert(DK % RG == 0 && DK <= NT && 4 * CG <= NT && DV <= NT, "verify thread map");
+
+    const size_t unit = blockIdx.x;                      // n H + h
+    const size_t n = unit / (unsigned)H, h = unit - n * (unsigned)H;
+    const int tid = threadIdx.x;
+    const bool act = tid < NT;
+    const int cg = tid % CG, rg = tid / CG;
+    const int w = tid / WAVE, lane = tid & (WAVE - 1);
+    const int gate = flags & FLAG_GATE_LOGITS;
+
+    __shared__ float s_kt[VG][DK], s_qt[VG][DK], s_kh[VG][DK], s_eg[DK];
+    __shared__ float s_sm[NCW * 4][NSM];                 // per 16-lane row sums of the small products
+    __shared__ f32x4 s_xy[NWV][2 * VG][CG];              // per-wave partial column sums of X_t, Y_t
+    __shared__ float s_u[VG][DV];                        // the group's u (scaled by 1/|k|), between groups
+
+    const f32x4* S = reinterpret_cast<const f32x4*>(state + unit * (size_t)(DK * DV));
+    f32x4 sv[RPT];
+    if (act) {
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) sv[i] = __builtin_nontemporal_load(&S[(rg + i * RG) * CG + cg]);
+    }
+
+    for (int j0 = 0; j0 < n_tok; j0 += VG) {
+        const int ng = n_tok - j0 < VG ? n_tok - j0 : VG;
+        if (j0 > 0) __syncthreads();                     // the previous group's readers are done
+        // ---- (1) per-draft vectors of channel c = tid, and the small products
+        if (w < NCW) {
+            const int c = tid;
+            const bool on = c < DK;
+            float kk[VG], qq[VG], gm[VG], gam = 0.f;
+#pragma unroll
+            for (int t = 0; t < VG; ++t) {
+                kk[t] = qq[t] = 0.f;
+                if (on && t < ng) {
+                    const size_t th = (n * (unsigned)n_tok + j0 + t) * (unsigned)H + h;
+                    gam += log_decay(log_alpha[th * DK + c], gate);
+                    kk[t] = to_f32(k[th * DK + c]);
+                    qq[t] = to_f32(q[th * DK + c]);
+                }
+                gm[t] = gam;
+            }
+            float sm[NSM];
+#pragma unroll
+            for (int t = 0; t < VG; ++t) {
+#pragma unroll
+                for (int s2 = 0; s2 <= t; ++s2) {
+                    const float d = fast_exp(gm[t] - gm[s2]);          // <= 1
+                    if (s2 < t) sm[a_index(t, s2)] = kk[t] * kk[s2] * d;
+                    sm[m_index(t, s2)] = qq[t] * kk[s2] * d;
+                }
+                sm[NA + NM + t] = kk[t] * kk[t];
+                sm[NA + NM + VG + t] = qq[t] * qq[t];
+            }
+            if (on) {
+                const float egl = fast_exp(gm[VG - 1]);
+#pragma unroll
+                for (int t = 0; t < VG; ++t) {
+                    const float e = fast_exp(gm[t]);
+                    s_kt[t][c] = kk[t] * e;
+                    s_qt[t][c] = qq[t] * e;
+                    s_kh[t][c] = kk[t] * (egl / e);
+                }
+                s_eg[c] = egl;
+            }
+            // sums over each 16-lane row (DPP row shifts); the row's last lane holds the sum
+#pragma unroll
+            for (int i = 0; i < NSM; ++i) {
+                float x = sm[i];
+                x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x111, 0xF, 0xF, true));
+                x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x112, 0xF, 0xF, true));
+                x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x114, 0xF, 0xF, true));
+                x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x118, 0xF, 0xF, true));
+                if ((lane & 15) == 15) s_sm[w * 4 + (lane >> 4)][i] = x;
+            }
+        }
+        __syncthreads();
+
+        // ---- (2) partial column sums of X_t = S^T kt_t and Y_t = S^T qt_t over this thread's rows
+        if (act) {
+#pragma unroll
+            for (int t = 0; t < VG; ++t) {
+                if (t >= ng) break;
+                f32x4 x = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int i = 0; i < RPT; ++i) {
+                    const int row = rg + i * RG;
+                    x += sv[i] * s_kt[t][row];
+                    y += sv[i] * s_qt[t][row];
+                }
+#pragma unroll
+                for (int m = CG; m < WAVE; m <<= 1) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        x[e] += __shfl_xor(x[e], m);
+                        y[e] += __shfl_xor(y[e], m);
+                    }
+                }
+                if (lane < CG) {
+                    s_xy[w][2 * t][cg] = x;
+                    s_xy[w][2 * t + 1][cg] = y;
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---- (3) one thread per value column: the group's solve and outputs
+        if (tid < DV) {
+            const int rc = tid >> 2, re = tid & 3;
+            // a small product: the sum of its row partials (the same LDS word for every lane)
+            auto small = [&](int i) {
+                float x = 0.f;
+#pragma unroll
+                for (int r = 0; r < NCW * 4; ++r) x += s_sm[r][i];
+                return x;
+            };
+            float ik[VG], iq[VG];
+#pragma unroll
+            for (int t = 0; t < VG; ++t) {
+                ik[t] = NORM ? __builtin_amdgcn_rsqf(small(NA + NM + t) + QK_NORM_EPS) : 1.f;
+                iq[t] = NORM ? __builtin_amdgcn_rsqf(small(NA + NM + VG + t) + QK_NORM_EPS) : 1.f;
+            }
+            float u[VG];
+#pragma unroll
+            for (int t = 0; t < VG; ++t) {
+                u[t] = 0.f;
+                if (t < ng) {
+                    float X = 0.f, Y = 0.f;
+#pragma unroll
+                    for (int ww = 0; ww < NWV; ++ww) {
+                        X += s_xy[ww][2 * t][rc][re];
+                        Y += s_xy[ww][2 * t + 1][rc][re];
+                    }
+                    const size_t th = (n * (unsigned)n_tok + j0 + t) * (unsigned)H + h;
+                    float acc = to_f32(v[th * DV + tid]) - X * ik[t];
+#pragma unroll
+                    for (int s2 = 0; s2 < t; ++s2) acc -= small(a_index(t, s2)) * ik[t] * ik[s2] * u[s2];
+                    u[t] = beta[th] * acc;
+                    float ot = Y * iq[t];
+#pragma unroll
+                    for (int s2 = 0; s2 <= t; ++s2) ot += small(m_index(t, s2)) * iq[t] * ik[s2] * u[s2];
+                    o[th * DV + tid] = from_f32<ET>(ot);
+                }
+            }
+            if (j0 + VG < n_tok) {
+#pragma unroll
+                for (int t = 0; t < VG; ++t) s_u[t][tid] = u[t] * ik[t];   // the update adds raw k
+            }
+        }
+        if (j0 + VG < n_tok) {
+            __syncthreads();
+            // ---- (4) advance the register state over the group
+            if (act) {
+#pragma unroll
+                for (int i = 0; i < RPT; ++i) {
+                    const int row = rg + i * RG;
+                    sv[i] *= s_eg[row];
+#pragma unroll
+                    for (int t = 0; t < VG; ++t) {
+                        const f32x4 ut = *reinterpret_cast<const f32x4*>(&s_u[t][4 * cg]);
+                        sv[i] += s_kh[t][row] * ut;
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <typename ET, int DK, int DV>
+static hipError_t launch_verify(const DecodeArgs& a, hipStream_t st) {
+    const unsigned nblk = (unsigned)(a.N * a.H);
+    if (a.flags & FLAG_QK_L2NORM)
+        hipLaunchKernelGGL((verify_kernel<ET, DK, DV, true>), dim3(nblk), dim3(DecodeMap<DK, DV, VERIFY_THREADS>::NTB), 0, st,
+                           a.state, (const ET*)a.q, (const ET*)a.k, (const ET*)a.v, a.log_alpha, a.beta, (ET*)a.o,
+                           (int)a.H, (int)a.n_tok, a.flags);
+    else
+        hipLaunchKernelGGL((verify_kernel<ET, DK, DV, false>), dim3(nblk), dim3(DecodeMap<DK, DV, VERIFY_THREADS>::NTB), 0, st,
+                           a.state, (const ET*)a.q, (const ET*)a.k, (const ET*)a.v, a.log_alpha, a.beta, (ET*)a.o,
+                           (int)a.H, (int)a.n_tok, a.flags);
+    return hipGetLastError();
+}
+
 template <typename ET, int DK, int DV, int MODE>
 static hipError_t launch_decode_m(const DecodeArgs& a, hipStream_t st) {
     const unsigned nblk = (unsigned)(a.N * a.H);
@@ -236,7 +449,7 @@ template <typename ET, int DK, int DV>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
     switch (a.mode) {
         case DECODE_STEP: return launch_decode_m<ET, DK, DV, DECODE_STEP>(a, st);
-        case DECODE_VERIFY: return launch_decode_m<ET, DK, DV, DECODE_VERIFY>(a, st);
+        case DECODE_VERIFY: return launch_verify<ET, DK, DV>(a, st);
         case DECODE_COMMIT: return launch_decode_m<ET, DK, DV, DECODE_COMMIT>(a, st);
     }
     return hipErrorInvalidValue;
