@@ -236,7 +236,9 @@ __host__ __device__ constexpr int m_index(int t, int s) { return 6 + t * (t + 1)
 // decay spans more than VG drafts.  With normalisation the raw k, q are used and the norms
 // scale the results in the reducer.
 // 512 threads per (n, h), 8 state rows each, at up to 128 VGPRs (4 waves per SIMD): two
-// workgroups per CU, so as much of the state is in flight as with the step kernel.
+// workgroups per CU, so as much of the state is in flight as with the step kernel.  A group's
+// per-draft inputs are loaded before the state (the first group) or during the previous
+// group, so that neither the small products nor the solve wait for memory.
 constexpr int VERIFY_THREADS = 512;
 template <typename ET, int DK, int DV, bool NORM>
 __global__ __launch_bounds__((DecodeMap<DK, DV, VERIFY_THREADS>::NTB)) __attribute__((amdgpu_waves_per_eu(4))) void verify_kernel(
@@ -251,6 +253,7 @@ __global__ __launch_bounds__((DecodeMap<DK, DV, VERIFY_THREADS>::NTB)) __attribu
     static_assert(m_index(0, 0) == NA, "small-product positions assume groups of 4");
     constexpr int NCW = (DK + WAVE - 1) / WAVE;          // waves of the channel threads
     static_assert(DK % RG == 0 && DK <= NT && 4 * CG <= NT && DV <= NT, "verify thread map");
+    static_assert(NSM <= WAVE, "one lane per small product sums its row partials");
 
     const size_t unit = blockIdx.x;                      // n H + h
     const size_t n = unit / (unsigned)H, h = unit - n * (unsigned)H;
@@ -262,8 +265,35 @@ __global__ __launch_bounds__((DecodeMap<DK, DV, VERIFY_THREADS>::NTB)) __attribu
 
     __shared__ float s_kt[VG][DK], s_qt[VG][DK], s_kh[VG][DK], s_eg[DK];
     __shared__ float s_sm[NCW * 4][NSM];                 // per 16-lane row sums of the small products
+    __shared__ float s_smt[NSM];                         // the small products
     __shared__ f32x4 s_xy[NWV][2 * VG][CG];              // per-wave partial column sums of X_t, Y_t
     __shared__ float s_u[VG][DV];                        // the group's u (scaled by 1/|k|), between groups
+
+    // A group's inputs in their storage types: gate, k, q of channel tid (tid < DK) and v of
+    // column tid, beta (tid < DV).  Token-head addresses are a uniform base plus a 32-bit lane
+    // offset; beta goes through a lane-varying zero offset so that it is a vector load.
+    const unsigned ut = (unsigned)tid;
+    unsigned zero = 0;
+    asm volatile("" : "+v"(zero));
+    float la_g[VG], b_g[VG];
+    ET k_g[VG], q_g[VG], v_g[VG];
+    auto load_group = [&](int j0) {
+#pragma unroll
+        for (int t = 0; t < VG; ++t) {
+            const bool in = j0 + t < n_tok;
+            const size_t th = (n * (unsigned)n_tok + (in ? j0 + t : 0)) * (unsigned)H + h;
+            if (tid < DK && in) {
+                la_g[t] = (log_alpha + th * DK)[ut];
+                k_g[t] = (k + th * DK)[ut];
+                q_g[t] = (q + th * DK)[ut];
+            }
+            if (tid < DV && in) {
+                v_g[t] = (v + th * DV)[ut];
+                b_g[t] = (beta + th)[zero];
+            }
+        }
+    };
+    load_group(0);
 
     const f32x4* S = reinterpret_cast<const f32x4*>(state + unit * (size_t)(DK * DV));
     f32x4 sv[RPT];
@@ -274,6 +304,7 @@ __global__ __launch_bounds__((DecodeMap<DK, DV, VERIFY_THREADS>::NTB)) __attribu
 
     for (int j0 = 0; j0 < n_tok; j0 += VG) {
         const int ng = n_tok - j0 < VG ? n_tok - j0 : VG;
+        const bool more = j0 + VG < n_tok;
         if (j0 > 0) __syncthreads();                     // the previous group's readers are done
         // ---- (1) per-draft vectors of channel c = tid, and the small products
         if (w < NCW) {
@@ -284,10 +315,9 @@ __global__ __launch_bounds__((DecodeMap<DK, DV, VERIFY_THREADS>::NTB)) __attribu
             for (int t = 0; t < VG; ++t) {
                 kk[t] = qq[t] = 0.f;
                 if (on && t < ng) {
-                    const size_t th = (n * (unsigned)n_tok + j0 + t) * (unsigned)H + h;
-                    gam += log_decay(log_alpha[th * DK + c], gate);
-                    kk[t] = to_f32(k[th * DK + c]);
-                    qq[t] = to_f32(q[th * DK + c]);
+                    gam += log_decay(la_g[t], gate);
+                    kk[t] = to_f32(k_g[t]);
+                    qq[t] = to_f32(q_g[t]);
                 }
                 gm[t] = gam;
             }
@@ -327,7 +357,8 @@ __global__ __launch_bounds__((DecodeMap<DK, DV, VERIFY_THREADS>::NTB)) __attribu
         }
         __syncthreads();
 
-        // ---- (2) partial column sums of X_t = S^T kt_t and Y_t = S^T qt_t over this thread's rows
+        // ---- (2) partial column sums of X_t = S^T kt_t and Y_t = S^T qt_t over this thread's
+        // rows; lanes of the last wave also sum the small products' row partials
         if (act) {
 #pragma unroll
             for (int t = 0; t < VG; ++t) {
@@ -353,23 +384,35 @@ __global__ __launch_bounds__((DecodeMap<DK, DV, VERIFY_THREADS>::NTB)) __attribu
                 }
             }
         }
+        if (w == NWV - 1 && lane < NSM) {
+            float x = 0.f;
+#pragma unroll
+            for (int r = 0; r < NCW * 4; ++r) x += s_sm[r][lane];
+            s_smt[lane] = x;
+        }
+        // the next group's gates, k and q (read in (1) above, before the barrier)
+        if (more && tid < DK) {
+#pragma unroll
+            for (int t = 0; t < VG; ++t) {
+                const int j = j0 + VG + t;
+                if (j < n_tok) {
+                    const size_t th = (n * (unsigned)n_tok + j) * (unsigned)H + h;
+                    la_g[t] = (log_alpha + th * DK)[ut];
+                    k_g[t] = (k + th * DK)[ut];
+                    q_g[t] = (q + th * DK)[ut];
+                }
+            }
+        }
         __syncthreads();
 
         // ---- (3) one thread per value column: the group's solve and outputs
         if (tid < DV) {
             const int rc = tid >> 2, re = tid & 3;
-            // a small product: the sum of its row partials (the same LDS word for every lane)
-            auto small = [&](int i) {
-                float x = 0.f;
-#pragma unroll
-                for (int r = 0; r < NCW * 4; ++r) x += s_sm[r][i];
-                return x;
-            };
             float ik[VG], iq[VG];
 #pragma unroll
             for (int t = 0; t < VG; ++t) {
-                ik[t] = NORM ? __builtin_amdgcn_rsqf(small(NA + NM + t) + QK_NORM_EPS) : 1.f;
-                iq[t] = NORM ? __builtin_amdgcn_rsqf(small(NA + NM + VG + t) + QK_NORM_EPS) : 1.f;
+                ik[t] = NORM ? __builtin_amdgcn_rsqf(s_smt[NA + NM + t] + QK_NORM_EPS) : 1.f;
+                iq[t] = NORM ? __builtin_amdgcn_rsqf(s_smt[NA + NM + VG + t] + QK_NORM_EPS) : 1.f;
             }
             float u[VG];
 #pragma unroll
@@ -382,23 +425,35 @@ __global__ __launch_bounds__((DecodeMap<DK, DV, VERIFY_THREADS>::NTB)) __attribu
                         X += s_xy[ww][2 * t][rc][re];
                         Y += s_xy[ww][2 * t + 1][rc][re];
                     }
-                    const size_t th = (n * (unsigned)n_tok + j0 + t) * (unsigned)H + h;
-                    float acc = to_f32(v[th * DV + tid]) - X * ik[t];
+                    float acc = to_f32(v_g[t]) - X * ik[t];
 #pragma unroll
-                    for (int s2 = 0; s2 < t; ++s2) acc -= small(a_index(t, s2)) * ik[t] * ik[s2] * u[s2];
-                    u[t] = beta[th] * acc;
+                    for (int s2 = 0; s2 < t; ++s2) acc -= s_smt[a_index(t, s2)] * ik[t] * ik[s2] * u[s2];
+                    u[t] = b_g[t] * acc;
                     float ot = Y * iq[t];
 #pragma unroll
-                    for (int s2 = 0; s2 <= t; ++s2) ot += small(m_index(t, s2)) * iq[t] * ik[s2] * u[s2];
-                    o[th * DV + tid] = from_f32<ET>(ot);
+                    for (int s2 = 0; s2 <= t; ++s2) ot += s_smt[m_index(t, s2)] * iq[t] * ik[s2] * u[s2];
+                    const size_t th = (n * (unsigned)n_tok + j0 + t) * (unsigned)H + h;
+                    (o + th * DV)[ut] = from_f32<ET>(ot);
                 }
             }
-            if (j0 + VG < n_tok) {
+            if (more) {
 #pragma unroll
                 for (int t = 0; t < VG; ++t) s_u[t][tid] = u[t] * ik[t];   // the update adds raw k
             }
         }
-        if (j0 + VG < n_tok) {
+        if (more) {
+            // the next group's v and beta
+            if (tid < DV) {
+#pragma unroll
+                for (int t = 0; t < VG; ++t) {
+                    const int j = j0 + VG + t;
+                    if (j < n_tok) {
+                        const size_t th = (n * (unsigned)n_tok + j) * (unsigned)H + h;
+                        v_g[t] = (v + th * DV)[ut];
+                        b_g[t] = (beta + th)[zero];
+                    }
+                }
+            }
             __syncthreads();
             // ---- (4) advance the register state over the group
             if (act) {
@@ -408,8 +463,8 @@ __global__ __launch_bounds__((DecodeMap<DK, DV, VERIFY_THREADS>::NTB)) __attribu
                     sv[i] *= s_eg[row];
 #pragma unroll
                     for (int t = 0; t < VG; ++t) {
-                        const f32x4 ut = *reinterpret_cast<const f32x4*>(&s_u[t][4 * cg]);
-                        sv[i] += s_kh[t][row] * ut;
+                        const f32x4 ut4 = *reinterpret_cast<const f32x4*>(&s_u[t][4 * cg]);
+                        sv[i] += s_kh[t][row] * ut4;
                     }
                 }
             }
