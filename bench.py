@@ -8,7 +8,8 @@ the inter-chunk state pass, plus the segment passes and prefix scan when the
 plan splits the sequence.  The headline workload is the largest one that fits
 one GPU, the single 1,048,576-token sequence: B=1, T=1,048,576, H=32,
 dk=dv=128, chunk 64, bf16 q/k/v/o with float32 gates and state (default plan:
-8 segments, so segment pass 1, prefix scan and pass 2).  Inputs are seeded
+the lead form of 9 segments: segment 0 beside segment pass 1 over segments 1-7
+in one launch, the prefix scan from segment 1, and pass 2 over segments 1-8).  Inputs are seeded
 synthetic tensors already resident in HBM when the timed region starts.
 
 The same JSON line carries side figures, each timed the same way:
@@ -79,10 +80,24 @@ def launch_bytes(r, plan, es):
     if plan.n_segments <= 1:
         return [("chunk_kernel (one pass)", B * T * H * prefill_bytes_per_token_head(dk, dv, es) + s0 + st)]
     P = plan.n_segments
+    pair = B * H * (dk * dv + dk * dk) * 4
+    summ = dk * es + dv * es + 4 * dk + 4                               # k, v, log_alpha, beta
+    full = prefill_bytes_per_token_head(dk, dv, es)
+    if plan.seg0_len > 0:
+        # lead form: segment 0 in pass-2 form (its end state to the start states) beside pass 1
+        # over segments 1 .. P-2; the scan from segment 1; pass 2 over segments 1 .. P-1
+        seg0 = plan.seg0_len
+        lc = -(-(-(-T // r.chunk) - seg0 // r.chunk) // (P - 1))
+        t1 = min(T - seg0, (P - 2) * lc * r.chunk)
+        out = [("chunk_lead_kernel (segment 0 beside segment pass 1)",
+                B * seg0 * H * full + s0 + st + B * t1 * H * summ + (P - 2) * pair)]
+        if P > 2:
+            out.append(("scan_kernel", (P - 2) * pair + st + (P - 2) * st))
+        out.append(("chunk_kernel (pass 2)", B * (T - seg0) * H * full + (P - 1) * st + st))
+        return out
     seg_len = -(-(-(-T // r.chunk)) // P) * r.chunk
     t1 = min(T, (P - 1) * seg_len)                                       # tokens pass 1 summarises
-    pair = B * H * (dk * dv + dk * dk) * 4
-    pass1 = B * t1 * H * (dk * es + dv * es + 4 * dk + 4) + (P - 1) * pair
+    pass1 = B * t1 * H * summ + (P - 1) * pair
     scan = (P - 1) * pair + s0 + P * st
     pass2 = B * T * H * prefill_bytes_per_token_head(dk, dv, es) + P * st + st
     return [("chunk_kernel (segment pass 1)", pass1), ("scan_kernel", scan), ("chunk_kernel (pass 2)", pass2)]
@@ -290,6 +305,7 @@ def time_prefill(g, torch, r, xd, steps, warmup, options=False):
     torch.cuda.synchronize()
     for i in range(steps):
         p = g.Plan(plan.n_segments, plan.dv_block, ctypes.cast(arrs[i], ctypes.POINTER(ctypes.c_void_p)), 2 * nl)
+        p.seg0_len = plan.seg0_len
         run(1, p=p)
     torch.cuda.synchronize()
     per_launch = []
@@ -308,7 +324,7 @@ def time_prefill(g, torch, r, xd, steps, warmup, options=False):
     dom = max(per_launch, key=lambda e: e["ms"])
     res = {
         "workload": r.name, "B": r.B, "T": r.T, "H": r.H, "dk": r.dk, "dv": r.dv, "chunk": r.chunk,
-        "plan": {"n_segments": plan.n_segments, "dv_block": plan.dv_block},
+        "plan": {"n_segments": plan.n_segments, "dv_block": plan.dv_block, "seg0_len": plan.seg0_len},
         "ms_per_step": round(ms, 5), "tokens_per_s": round(r.B * r.T / sec, 1),
         "roofline": {"bound": "hbm", "kernel": dom["kernel"], "achieved": round(dom["GBps"], 1),
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(dom["GBps"] / PEAK_HBM_GBPS, 4),

@@ -43,14 +43,16 @@ class KdaError(RuntimeError):
 
 class Plan(ctypes.Structure):
     """kda_plan_t: segmentation, column blocking, optional launch-timing events, optional
-    state checkpoints, packed sequences and the input flags."""
+    state checkpoints, packed sequences, the input flags and the lead form's segment-0 length."""
     _fields_ = [("n_segments", ctypes.c_int32), ("dv_block", ctypes.c_int32),
                 ("launch_events", ctypes.POINTER(ctypes.c_void_p)), ("n_launch_events", ctypes.c_int32),
                 ("state_ckpt", ctypes.c_void_p), ("ckpt_stride", ctypes.c_int64),
-                ("cu_seqlens", ctypes.c_void_p), ("n_seqs", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+                ("cu_seqlens", ctypes.c_void_p), ("n_seqs", ctypes.c_int32), ("flags", ctypes.c_uint32),
+                ("seg0_len", ctypes.c_int64)]
 
     def __repr__(self):
-        return f"Plan(n_segments={self.n_segments}, dv_block={self.dv_block})"
+        lead = f", seg0_len={self.seg0_len}" if self.seg0_len else ""
+        return f"Plan(n_segments={self.n_segments}, dv_block={self.dv_block}{lead})"
 
 
 def _load():

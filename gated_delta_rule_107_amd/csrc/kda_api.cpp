@@ -69,7 +69,15 @@ struct Resolved {
     int32_t dv_block;
     bool packed_seg;        // packed sequences cut into segments (segment tables in the workspace)
     int32_t n_seqs;         // packed sequences (0 without cu_seqlens)
+    int64_t seg0_len;       // lead form: tokens of segment 0 (0 = equal segments)
 };
+
+// Default lead form: a pass-1 chunk (the widened state [S | M], no q, no o) takes about this
+// fraction of a pass-2 chunk's time on MI355X (bf16, 128 x 128: 6.0 vs 8.5 us in the 1M-token
+// plan), so segment 0, run in pass-2 form beside pass 1, gets this fraction of the others'
+// length; only when the segments are long enough for the rounding to whole chunks not to matter.
+constexpr double kLeadRatio = 0.7;
+constexpr int64_t kLeadMinChunks = 16;
 
 constexpr int64_t kMaxSlots = 1 << 22;   // segment-table entries of one packed call
 
@@ -88,6 +96,9 @@ kda_status_t resolve_plan(int64_t B, int64_t T, int32_t H, int32_t dk, int32_t d
     out->packed_seg = false;
     out->n_seqs = 0;
     out->dv_block = dvb;
+    out->seg0_len = 0;
+    if (p.seg0_len < 0) return fail(KDA_ERR_UNSUPPORTED, "seg0_len must be >= 0");
+    if (p.seg0_len > 0 && p.cu_seqlens) return fail(KDA_ERR_UNSUPPORTED, "seg0_len applies to unpacked batches only");
     if (p.cu_seqlens) {
         // Packed sequences: n_segments is the number of segments the packed row is cut into;
         // every sequence is split into segments of that length (whole chunks, at least two), so
@@ -114,6 +125,21 @@ kda_status_t resolve_plan(int64_t B, int64_t T, int32_t H, int32_t dk, int32_t d
         out->seg_len = nchunks * chunk;
         return KDA_OK;
     }
+    if (p.seg0_len > 0) {
+        // the lead form as asked: segment 0 of seg0_len tokens, the rest in nseg - 1 segments
+        if (p.seg0_len % chunk != 0 || p.seg0_len >= T)
+            return fail(KDA_ERR_UNSUPPORTED, "seg0_len (%lld) must be a multiple of chunk (%d) below T (%lld)",
+                        (long long)p.seg0_len, chunk, (long long)T);
+        if (nseg < 2) return fail(KDA_ERR_UNSUPPORTED, "seg0_len needs n_segments >= 2 (got %lld)", (long long)nseg);
+        if (nseg > 65535) return fail(KDA_ERR_UNSUPPORTED, "too many segments");
+        const int64_t rest = nchunks - p.seg0_len / chunk;           // >= 1
+        const int64_t lc = (rest + nseg - 2) / (nseg - 1);
+        out->seg0_len = p.seg0_len;
+        out->seg_len = lc * chunk;
+        out->n_seg = (int32_t)(1 + (rest + lc - 1) / lc);
+        return KDA_OK;
+    }
+    const bool dflt = nseg == 0;
     if (nseg == 0) {
         // enough workgroups to cover every compute unit; segments only when (b, h, column
         // block) units alone cannot, and only if each segment keeps at least 2 chunks
@@ -132,6 +158,17 @@ kda_status_t resolve_plan(int64_t B, int64_t T, int32_t H, int32_t dk, int32_t d
     out->seg_len = seg_chunks * chunk;
     out->n_seg = nchunks == 0 ? 1 : (int32_t)((nchunks + seg_chunks - 1) / seg_chunks);
     out->dv_block = dvb;
+    if (dflt && out->n_seg >= 2) {
+        // lead form: one segment more, segment 0 kLeadRatio of the others' length, so that
+        // the launch running it beside pass 1 ends together and pass 2 covers one segment fewer
+        const int64_t S = out->n_seg;
+        const int64_t lc = (int64_t)((double)nchunks / ((double)S + kLeadRatio));
+        if (lc >= kLeadMinChunks) {
+            out->seg0_len = (nchunks - S * lc) * chunk;              // >= kLeadRatio lc chunks
+            out->seg_len = lc * chunk;
+            out->n_seg = (int32_t)(S + 1);
+        }
+    }
     return KDA_OK;
 }
 
@@ -202,6 +239,7 @@ kda_status_t kda_chunk_fwd_default_plan(int64_t B, int64_t T, int32_t H, int32_t
     *plan = kda_plan_t{};
     plan->n_segments = r.n_seg;
     plan->dv_block = r.dv_block;
+    plan->seg0_len = r.seg0_len;
     return KDA_OK;
 }
 
@@ -314,7 +352,7 @@ kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, const f
     a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta;
     a.o = o; a.s_final = S_T;
     a.B = B; a.T = T; a.H = H; a.dk = dk; a.dv = dv; a.chunk = chunk;
-    a.n_seg = r.n_seg; a.seg_len = r.seg_len; a.dv_block = r.dv_block;
+    a.n_seg = r.n_seg; a.seg_len = r.seg_len; a.seg0_len = r.seg0_len; a.dv_block = r.dv_block;
     a.ckpt = ckpt; a.ckpt_stride = ckpt_stride;
     a.cu_seqlens = cu;
     a.flags = flags;
@@ -323,19 +361,23 @@ kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, const f
     if (trace_on()) {
         std::fprintf(stderr,
                      "kda_chunk_fwd%s: B=%lld T=%lld H=%d dk=%d dv=%d chunk=%d dtype=%s sequences=%lld "
-                     "%s=%d seg_len=%lld dv_block=%d workspace=%zu flags=0x%x checkpoints=%s "
+                     "%s=%d seg_len=%lld seg0_len=%lld dv_block=%d workspace=%zu flags=0x%x checkpoints=%s "
                      "launches=%s\n",
                      library_scratch ? "_noalloc" : "", (long long)B, (long long)T, H, dk, dv, chunk,
                      dt == KDA_DTYPE_BF16 ? "bf16" : "f32", (long long)n_seq,
                      r.packed_seg ? "segment_slots" : "n_segments", r.n_seg, (long long)r.seg_len,
-                     r.dv_block, need, flags, ckpt ? "yes" : "no",
+                     (long long)r.seg0_len, r.dv_block, need, flags, ckpt ? "yes" : "no",
                      r.packed_seg ? "segment-table,segment-pass-1,scan,segment-pass-2"
-                                  : (r.n_seg == 1 ? "chunk" : "segment-pass-1,scan,segment-pass-2"));
+                     : r.seg0_len > 0 ? (r.n_seg > 2 ? "lead(segment-0+segment-pass-1),scan,segment-pass-2"
+                                                     : "lead(segment-0),segment-pass-2")
+                     : (r.n_seg == 1 ? "chunk" : "segment-pass-1,scan,segment-pass-2"));
     }
     hipError_t e;
     if (r.n_seg == 1 && !r.packed_seg) {
         a.mode = 0;
         a.s0 = S0;
+        a.seg_lo = 0;
+        a.seg_cnt = 1;
         tm.before();
         e = kda::launch_chunk(a, st);
         tm.after();
@@ -362,16 +404,55 @@ kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, const f
         a.B = 1;
         seq_table = t.seq_table;
     }
-    // pass 1: segment pairs
+    if (r.seg0_len > 0) {
+        // lead form: segment 0 (from S0, in pass-2 form, its final state into starts[.., 1])
+        // in one launch with pass 1 over segments 1 .. P-2; the scan from segment 1; pass 2
+        // over segments 1 .. P-1
+        kda::ChunkArgs a0 = a, a1 = a;
+        a0.mode = 0;
+        a0.s0 = S0;
+        a0.starts = starts;
+        a0.seg_lo = 0;
+        a0.seg_cnt = 1;
+        a1.mode = 1;
+        a1.s_loc = s_loc;
+        a1.m_tr = m_tr;
+        a1.seg_lo = 1;
+        a1.seg_cnt = r.n_seg - 2;
+        tm.before();
+        e = kda::launch_chunk_lead(a0, a1, st);
+        tm.after();
+        if (e != hipSuccess) return hip_fail(e, "lead launch");
+        if (r.n_seg > 2) {
+            kda::ScanArgs sc{S0, s_loc, m_tr, starts, B, H, dk, dv, r.n_seg, 1, nullptr};
+            tm.before();
+            e = kda::launch_scan(sc, st);
+            tm.after();
+            if (e != hipSuccess) return hip_fail(e, "segment scan launch");
+        }
+        a.mode = 0;
+        a.s0 = nullptr;
+        a.starts = starts;
+        a.seg_lo = 1;
+        a.seg_cnt = r.n_seg - 1;
+        tm.before();
+        e = kda::launch_chunk(a, st);
+        tm.after();
+        if (e != hipSuccess) return hip_fail(e, "segment pass-2 launch");
+        return KDA_OK;
+    }
+    // pass 1: segment pairs (packed sequences: every slot; the kernel skips last segments)
     a.mode = 1;
     a.s_loc = s_loc;
     a.m_tr = m_tr;
+    a.seg_lo = 0;
+    a.seg_cnt = r.packed_seg ? r.n_seg : r.n_seg - 1;
     tm.before();
     e = kda::launch_chunk(a, st);
     tm.after();
     if (e != hipSuccess) return hip_fail(e, "segment pass-1 launch");
     // prefix scan over the pairs
-    kda::ScanArgs sc{S0, s_loc, m_tr, starts, r.packed_seg ? (int64_t)r.n_seqs : B, H, dk, dv, r.n_seg, seq_table};
+    kda::ScanArgs sc{S0, s_loc, m_tr, starts, r.packed_seg ? (int64_t)r.n_seqs : B, H, dk, dv, r.n_seg, 0, seq_table};
     tm.before();
     e = kda::launch_scan(sc, st);
     tm.after();
@@ -380,6 +461,8 @@ kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, const f
     a.mode = 0;
     a.s0 = nullptr;
     a.starts = starts;
+    a.seg_lo = 0;
+    a.seg_cnt = r.n_seg;
     tm.before();
     e = kda::launch_chunk(a, st);
     tm.after();

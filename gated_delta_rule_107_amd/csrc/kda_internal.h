@@ -42,7 +42,8 @@ struct ChunkArgs {
     const void *q, *k, *v;
     const float *log_alpha, *beta;
     const float* s0;        // [B,H,dk,dv] or null (zeros): start state when n_seg == 1 (mode 0)
-    const float* starts;    // [B,H,P,dk,dv] start state of every segment (mode 0, n_seg > 1)
+    float* starts;          // [B,H,P,dk,dv] start state of every segment (read by mode 0 when
+                            // n_seg > 1; the lead form's segment 0 writes the start of segment 1)
     void* o;                // [B,T,H,dv] (mode 0)
     float* s_final;         // [B,H,dk,dv] (mode 0)
     float* s_loc;           // [B,H,P][dk dv] (mode 1), each block in sloc_index order
@@ -52,6 +53,9 @@ struct ChunkArgs {
     int32_t H, dk, dv, chunk;
     int32_t n_seg;          // P
     int64_t seg_len;        // tokens per segment, a multiple of chunk
+    int64_t seg0_len;       // tokens of segment 0 in the lead form (then segment i > 0 starts at
+                            // seg0_len + (i - 1) seg_len), 0 = every segment seg_len long
+    int32_t seg_lo, seg_cnt;  // this launch covers segments seg_lo .. seg_lo + seg_cnt - 1
     int32_t dv_block;       // columns per workgroup (16 per wave)
     const int32_t* cu_seqlens;  // [B + 1] packed sequence offsets into one batch row, or null
     // packed sequences with segments (seg_table non-null; B = 1, n_seg = the table's length):
@@ -67,8 +71,14 @@ struct ChunkArgs {
 
 hipError_t launch_chunk(const ChunkArgs& a, hipStream_t st);
 
-// Prefix scan over segment pairs: starts[i+1] = M_i starts[i] + S_loc_i,
-// starts[0] = s0 (or zeros); writes starts[0 .. P-1].
+// Lead form of a segmented plan, one launch: a0 (mode 0) runs segment 0 of every (batch, head,
+// column block) from S0 and writes its final state to starts[.., 1]; a1 (mode 1) runs pass 1 over
+// segments 1 .. P-2.  a1.seg_cnt may be 0.
+hipError_t launch_chunk_lead(const ChunkArgs& a0, const ChunkArgs& a1, hipStream_t st);
+
+// Prefix scan over segment pairs: starts[i+1] = M_i starts[i] + S_loc_i.  first = 0: starts[0]
+// = s0 (or zeros), writes starts[0 .. P-1]; first = 1 (lead form): starts[1] is given, writes
+// starts[2 .. P-1] from pairs 1 .. P-2.
 struct ScanArgs {
     const float* s0;
     const float* s_loc;     // [B,H,P][dk dv], sloc_index order
@@ -76,6 +86,7 @@ struct ScanArgs {
     float* starts;
     int64_t B;              // (packed sequences: the number of sequences)
     int32_t H, dk, dv, n_seg;
+    int32_t first;          // 0 or 1 (see above; 0 with seq_table)
     // packed sequences with segments: entry i = {first slot, number of segments} of sequence i;
     // its pairs and starts for head h sit at h * n_seg + first slot + j
     const int2* seq_table;

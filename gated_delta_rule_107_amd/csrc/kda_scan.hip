@@ -26,7 +26,8 @@
 // A step is bounded by the vector-memory path of the CU: each workgroup needs all of M_i
 // (64 KiB, both planes) per step for its 16 columns.
 // starts[0] receives a copy of S0 (or zeros), so the pass that follows never reads
-// S0 itself (S0 may alias the final state).
+// S0 itself (S0 may alias the final state).  In the lead form of a plan the chain starts
+// at segment 1 from the start state the lead launch wrote (first = 1).
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -77,6 +78,9 @@ __global__ __launch_bounds__(64 * (DK / 16 + 1)) void scan_kernel(ScanArgs a) {
         P = e.y;
         base = (bh % a.H) * (int64_t)a.n_seg + e.x;
     }
+    // lead form: the chain starts at segment 1, whose start state the lead launch wrote
+    P -= a.first;
+    base += a.first;
     const int dv = a.dv;
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int m = lane & 15, g = lane >> 4;
@@ -133,16 +137,17 @@ __global__ __launch_bounds__(64 * (DK / 16 + 1)) void scan_kernel(ScanArgs a) {
     if (storer) {
         for (int i = 0; i < P; ++i) {
             lds_barrier();                        // LDS holds the start of segment i
-            store_start(i);
+            if (i > 0 || !a.first) store_start(i);    // (a given start is not stored again)
         }
         return;
     }
 
     {
+        // the chain's first start: S0 (or zeros), or in the lead form the given start state
+        const float* s_in = a.first ? a.starts + base * DK * dv : (a.s0 ? a.s0 + bh * DK * dv : nullptr);
         f32x4 cur;
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            cur[r] = a.s0 ? a.s0[bh * DK * dv + (int64_t)(row0 + 4 * g + r) * dv + col] : 0.f;
+        for (int r = 0; r < 4; ++r) cur[r] = s_in ? s_in[(int64_t)(row0 + 4 * g + r) * dv + col] : 0.f;
         put(cur, 0);
     }
 

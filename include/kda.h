@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 
 /* Storage type of q, k, v and o.  log_alpha, beta and every state are float32.
  * (KDA_DTYPE_FORCE_INT32 is not a dtype: it makes every non-negative int32 a valid value of
@@ -90,6 +90,15 @@ typedef enum {
  *   back in the serving stack": pass 1 builds every segment's (cumulative
  *   transition, zero-start state) pair, a prefix scan gives each segment's
  *   true start state, pass 2 reruns the segments in parallel from those.
+ * seg0_len: 0 = segments of equal length.  > 0 (unpacked batches, n_segments
+ *   >= 2) = the lead form: segment 0 holds seg0_len tokens (a multiple of
+ *   chunk, below T) and the other T - seg0_len tokens are cut into
+ *   n_segments - 1 equal segments of whole chunks.  Segment 0 needs no scan (it
+ *   starts from S0), so it runs in pass-2 form in the same launch as pass 1 over
+ *   segments 1 .. n_segments - 2, on the compute units that pass 1 leaves
+ *   free; its final state is the exact start of segment 1, and the scan and
+ *   pass 2 cover segments 1 .. n_segments - 1.  Results equal those of equal
+ *   segments up to rounding.
  * dv_block: value columns per workgroup of the one-pass / pass-2 launch, a
  *   multiple of 16 dividing dv.  The recurrence is independent per state
  *   column, so column blocks run in parallel; the shared per-chunk work
@@ -128,7 +137,10 @@ typedef struct {
     /* Optional launch timing, for profilers and benchmarks (NULL = off).  An
      * array of n_launch_events hipEvent_t handles, created by the caller.
      * Kernel launch i of the call (i = 0, 1, ... in launch order: one launch
-     * with one segment; pass 1, scan, pass 2 with several) records
+     * with one segment; pass 1, scan, pass 2 with several; lead (segment 0
+     * beside pass 1), scan, pass 2 in the lead form, without the scan when
+     * n_segments is 2; the segment-table build first for packed sequences with
+     * segments) records
      * launch_events[2i] just before it and launch_events[2i+1] just after it
      * on `stream`; launches beyond the array's capacity record nothing. */
     void* const* launch_events;
@@ -138,11 +150,16 @@ typedef struct {
     const int32_t* cu_seqlens;
     int32_t n_seqs;
     uint32_t flags;
+    int64_t seg0_len;
 } kda_plan_t;
 
 /* Fills *plan with the library's default for this problem: one pass when the
  * (batch, head) units alone cover MI355X's 256 compute units, otherwise enough
- * segments to cover them (at least two chunks per segment).  The default is
+ * segments to cover them (at least two chunks per segment).  When those
+ * segments would be long (at least 16 chunks each) the default takes the lead
+ * form: one more segment, segment 0 about 0.7 of the others' length (a pass-1
+ * chunk takes about 0.7 of a pass-2 chunk's time on MI355X), so the launch that
+ * runs it beside pass 1 ends together.  The default is
  * the same on every device (it does not query the device), so results round
  * the same everywhere; on a partitioned device pass n_segments yourself.
  * Returns KDA_OK or an argument error.  Makes no HIP call.
@@ -205,8 +222,9 @@ kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v,
  *
  * - A plan whose segment workspace (kda_chunk_fwd_workspace_bytes) exceeds
  *   KDA_NOALLOC_SCRATCH_BYTES is rejected with KDA_ERR_WORKSPACE before any
- *   HIP call.  The default plans of B=1, T=4096, H=16 and of B=1,
- *   T=1,048,576, H=32 (dk = dv = 128) need 48 MiB.
+ *   HIP call.  The default plans of B=1, T=4096, H=16 (16 segments) and of
+ *   B=1, T=1,048,576, H=32 (9 segments in the lead form), dk = dv = 128, need
+ *   48 and 54 MiB.
  * - On the first call on a device that needs the array, the library looks up
  *   its address on that device (hipGetSymbolAddress); a failure there returns
  *   KDA_ERR_HIP.

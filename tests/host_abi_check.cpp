@@ -26,6 +26,9 @@ struct Launch {
     int64_t seg_len;
     int32_t dv_block;
     const void* ws;
+    int32_t seg_lo = 0, seg_cnt = 0;   // chunk launches: the segments covered; scan: first in seg_lo
+    int64_t seg0_len = 0;
+    int32_t seg_cnt1 = 0;              // lead launch: pass-1 segments beside segment 0
 };
 std::vector<Launch> g_launches;
 unsigned char g_scratch_stub[64];
@@ -34,11 +37,20 @@ unsigned char g_scratch_stub[64];
 namespace kda {
 hipError_t launch_chunk(const ChunkArgs& a, hipStream_t) {
     g_launches.push_back({a.mode == 1 ? "pass1" : "chunk", a.mode, a.B, a.T, a.n_seg, a.seg_len, a.dv_block,
-                          a.s_loc});
+                          a.s_loc, a.seg_lo, a.seg_cnt, a.seg0_len});
+    return hipSuccess;
+}
+hipError_t launch_chunk_lead(const ChunkArgs& a0, const ChunkArgs& a1, hipStream_t) {
+    // a0 runs segment 0 in mode 0, a1 pass 1 (mode 1) over the segments after it
+    const bool ok = a0.mode == 0 && a1.mode == 1 && a0.seg_lo == 0 && a0.seg_cnt == 1 && a1.seg_lo == 1 &&
+                    a0.starts != nullptr && a1.s_loc != nullptr && a1.m_tr != nullptr &&
+                    a0.seg0_len == a1.seg0_len && a0.seg_len == a1.seg_len && a0.n_seg == a1.n_seg;
+    g_launches.push_back({ok ? "lead" : "lead-bad-args", 0, a0.B, a0.T, a0.n_seg, a0.seg_len, a0.dv_block,
+                          a1.s_loc, a0.seg_lo, a0.seg_cnt, a0.seg0_len, a1.seg_cnt});
     return hipSuccess;
 }
 hipError_t launch_scan(const ScanArgs& a, hipStream_t) {
-    g_launches.push_back({"scan", -1, a.B, 0, a.n_seg, 0, 0, a.s_loc});
+    g_launches.push_back({"scan", -1, a.B, 0, a.n_seg, 0, 0, a.s_loc, a.first});
     return hipSuccess;
 }
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t) {
@@ -165,6 +177,10 @@ void chunk_launches() {
         CHECK(g_launches[0].n_seg == 16 && g_launches[0].seg_len == 256, "plan %d x %lld", g_launches[0].n_seg,
               (long long)g_launches[0].seg_len);
         CHECK(g_launches[0].ws == A(8), "the caller's workspace is used");
+        // equal segments: pass 1 over segments 0 .. 14, the scan from S0, pass 2 over all 16
+        CHECK(g_launches[0].seg_lo == 0 && g_launches[0].seg_cnt == 15 && g_launches[0].seg0_len == 0, "pass-1 range");
+        CHECK(g_launches[1].seg_lo == 0, "scan from S0");
+        CHECK(g_launches[2].seg_lo == 0 && g_launches[2].seg_cnt == 16, "pass-2 range");
     }
     // the same through kda_chunk_fwd_noalloc: the library's workspace
     g_launches.clear();
@@ -173,7 +189,56 @@ void chunk_launches() {
     // the 1M-token workload's default plan: 8 segments of 131,072 tokens
     kda_plan_t p{};
     CHECK(kda_chunk_fwd_default_plan(1, 1 << 20, 32, 128, 128, 64, KDA_DTYPE_BF16, &p) == KDA_OK, "plan query");
-    CHECK(p.n_segments == 8 && p.dv_block == 128, "1M plan %d / %d", p.n_segments, p.dv_block);
+    // 8 equal segments would fill the 256 CUs in pass 2; the lead form adds segment 0 of
+    // floor(16384 / 8.7) = 1883 -> 16384 - 8 * 1883 = 1320 chunks beside pass 1
+    CHECK(p.n_segments == 9 && p.dv_block == 128 && p.seg0_len == 1320 * 64, "1M plan %d / %d / %lld",
+          p.n_segments, p.dv_block, (long long)p.seg0_len);
+    {
+        Call m;
+        m.T = 1 << 20; m.H = 32; m.dk = m.dv = 128; m.chunk = 64; m.dt = KDA_DTYPE_BF16; m.use_plan = false;
+        m.S0 = P<float>(5);
+        size_t need_m = 0;
+        CHECK(kda_chunk_fwd_workspace_bytes(1, 1 << 20, 32, 128, 128, 64, KDA_DTYPE_BF16, nullptr, &need_m) == KDA_OK,
+              "1M ws query");
+        CHECK(need_m == (size_t)32 * 9 * 3 * 128 * 128 * 4, "1M workspace %zu", need_m);
+        m.ws = A(8);
+        m.wsb = need_m;
+        g_launches.clear();
+        CHECK(m.run() == KDA_OK, "1M lead plan: %s", kda_last_error());
+        CHECK(g_launches.size() == 3, "1M lead plan: %zu launches", g_launches.size());
+        if (g_launches.size() == 3) {
+            CHECK(g_launches[0].what == "lead" && g_launches[0].seg_cnt1 == 7 && g_launches[0].seg0_len == 1320 * 64 &&
+                      g_launches[0].seg_len == 1883 * 64 && g_launches[0].n_seg == 9,
+                  "lead launch: %s pass-1 segments %d seg0 %lld seg_len %lld", g_launches[0].what.c_str(),
+                  g_launches[0].seg_cnt1, (long long)g_launches[0].seg0_len, (long long)g_launches[0].seg_len);
+            CHECK(g_launches[1].what == "scan" && g_launches[1].seg_lo == 1, "scan from segment 1");
+            CHECK(g_launches[2].what == "chunk" && g_launches[2].seg_lo == 1 && g_launches[2].seg_cnt == 8,
+                  "pass 2 over segments 1 .. 8");
+        }
+        // re-resolving the default plan explicitly gives the same execution
+        Call e = m;
+        e.use_plan = true;
+        e.plan = p;
+        g_launches.clear();
+        CHECK(e.run() == KDA_OK && g_launches.size() == 3 && g_launches[0].seg_len == 1883 * 64 &&
+                  g_launches[0].seg0_len == 1320 * 64,
+              "explicit copy of the default plan");
+        // the lead form's own checks
+        { Call x = e; x.plan.seg0_len = 100; expect_reject(x, KDA_ERR_UNSUPPORTED, "seg0_len not a multiple of chunk"); }
+        { Call x = e; x.plan.seg0_len = (int64_t)1 << 20; expect_reject(x, KDA_ERR_UNSUPPORTED, "seg0_len = T"); }
+        { Call x = e; x.plan.seg0_len = -64; expect_reject(x, KDA_ERR_UNSUPPORTED, "seg0_len < 0"); }
+        { Call x = e; x.plan.n_segments = 1; expect_reject(x, KDA_ERR_UNSUPPORTED, "seg0_len with one segment"); }
+        // two segments: segment 0 alone in the lead launch, no scan, pass 2 over segment 1
+        Call two = e;
+        two.plan.n_segments = 2;
+        two.plan.seg0_len = 4096;
+        g_launches.clear();
+        CHECK(two.run() == KDA_OK, "two-segment lead plan: %s", kda_last_error());
+        CHECK(g_launches.size() == 2 && g_launches[0].what == "lead" && g_launches[0].seg_cnt1 == 0 &&
+                  g_launches[1].what == "chunk" && g_launches[1].seg_lo == 1 && g_launches[1].seg_cnt == 1 &&
+                  g_launches[1].seg_len == ((1 << 20) - 4096),
+              "two-segment lead launches (%zu)", g_launches.size());
+    }
     // packed sequences with segments: segment table, pass 1, scan, pass 2; segments of
     // ceil(T / n_segments) tokens rounded up to whole chunks; ceil(T / seg_len) + n_seqs slots
     Call pk;
@@ -186,6 +251,7 @@ void chunk_launches() {
     CHECK(kda_chunk_fwd_workspace_bytes(1, 70000, 4, 128, 128, 64, KDA_DTYPE_BF16, &pk.plan, &need_pk) == KDA_OK,
           "packed ws query: %s", kda_last_error());
     expect_reject(pk, KDA_ERR_WORKSPACE, "packed segments without a workspace");
+    { Call x = pk; x.plan.seg0_len = 64; expect_reject(x, KDA_ERR_UNSUPPORTED, "seg0_len with packed sequences"); }
     pk.ws = A(8);
     pk.wsb = need_pk;
     g_launches.clear();

@@ -95,7 +95,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 1
+    assert lib.kda_abi_version() == 2
     for code in range(9):
         assert lib.kda_status_str(code).decode() not in ("", "unknown status")
     assert lib.kda_status_str(99) == b"unknown status"

@@ -194,6 +194,63 @@ def test_segments(g, shape, nseg):
     check(o, S, o_ref, S_ref, TOL[dtype], f"{shape} {nseg} segments")
 
 
+@pytest.mark.parametrize("shape,nseg,seg0,dvb", [
+    (("bf16", 1, 500, 2, 128, 128, 64), 3, 64, 0),      # a ragged last segment
+    (("f32", 1, 200, 2, 32, 32, 16), 4, 48, 16),        # two column blocks in segment 0's part
+    (("bf16", 2, 333, 1, 64, 64, 32), 2, 96, 0),        # two segments: no pass 1 beside it, no scan
+    (("bf16", 1, 1000, 3, 128, 64, 64), 5, 256, 0),     # fewer value columns than key channels
+    (("f32", 1, 64, 1, 16, 16, 16), 3, 16, 0),          # one-chunk segments
+], ids=lambda s: "-".join(map(str, s)) if isinstance(s, tuple) else str(s))
+def test_lead_segments(g, shape, nseg, seg0, dvb):
+    """The lead form of a segmented plan: segment 0 (seg0 tokens, from S0) runs in pass-2 form
+    in the same launch as pass 1 over segments 1 .. P-2, its final state is the start of
+    segment 1, the scan starts there and pass 2 covers segments 1 .. P-1.  Same bar as equal
+    segments, with a nonzero start state."""
+    dtype, B, T, H, dk, dv, chunk = shape
+    r = small_recipe(dtype, B, T, H, dk, dv, chunk, s0_std=0.1)
+    _say("case: lead segments", nseg, seg0, dvb, shape)
+    x = ks.make_prefill(r)
+    o_ref, S_ref = oracle.kda_loop(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["S0"])
+    plan = g.Plan(n_segments=nseg, dv_block=dvb, seg0_len=seg0)
+    o, S = run_prefill(g, x, dtype, chunk, plan=plan)
+    check(o, S, o_ref, S_ref, TOL[dtype], f"{shape} lead form, {nseg} segments, segment 0 of {seg0} tokens")
+
+
+def test_lead_segments_with_options(g):
+    """The lead form with the optional features: state checkpoints (written by segment 0 in the
+    lead launch and by pass 2), then raw gate logits with in-kernel q/k normalisation (the
+    pass-1 part of the lead launch and the scan's start from segment 1 included)."""
+    import torch
+    dtype, B, T, H, dk, dv, chunk, stride = "bf16", 1, 500, 2, 128, 128, 64, 64
+    plan = g.Plan(n_segments=3, dv_block=0, seg0_len=128)
+    _say("case: lead segments with checkpoints, then gate logits and q/k normalisation")
+    x = ks.make_prefill(small_recipe(dtype, B, T, H, dk, dv, chunk, s0_std=0.05))
+    dt = torch.bfloat16
+    args = [dev_tensor(x[n], dt) for n in ("q", "k", "v")]
+    args += [dev_tensor(x["log_alpha"], torch.float32), dev_tensor(x["beta"], torch.float32),
+             dev_tensor(x["S0"], torch.float32)]
+    o, S, ck = g.chunk_fwd(*args, chunk=chunk, plan=plan, ckpt_stride=stride)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.kda_chunked(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["S0"], chunk=chunk)
+    check(to_np(o), to_np(S), o_ref, S_ref, TOL[dtype], "lead form with checkpoints")
+    for j in range(T // stride):
+        tj = (j + 1) * stride
+        pre = lambda a: a[:, :tj]  # noqa: E731
+        _, Sj = oracle.kda_chunked(pre(x["q"]), pre(x["k"]), pre(x["v"]), pre(x["log_alpha"]), pre(x["beta"]),
+                                   x["S0"], chunk=chunk)
+        ej = oracle.rel_fro(to_np(ck[:, j]), Sj)
+        _say(f"  checkpoint {j} (after {tj} tokens): rel_fro {ej:.3e}")
+        assert ej <= TOL[dtype], (j, ej)
+    x = ks.make_prefill(small_recipe(dtype, B, T, H, dk, dv, chunk, qk="raw", s0_std=0.05, loga="logit15"))
+    o, S = g.chunk_fwd(*(dev_tensor(x[n], dt) for n in ("q", "k", "v")), dev_tensor(x["log_alpha"], torch.float32),
+                       dev_tensor(x["beta"], torch.float32), dev_tensor(x["S0"], torch.float32), chunk=chunk,
+                       plan=plan, gate=g.GATE_LOGITS, qk_norm=True)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.kda_loop(oracle.l2_normalize(x["q"]), oracle.l2_normalize(x["k"]), x["v"],
+                                   oracle.gate_from_logits(x["log_alpha"]), x["beta"], x["S0"])
+    check(to_np(o), to_np(S), o_ref, S_ref, TOL[dtype], "lead form with gate logits and q/k normalisation")
+
+
 def test_floor_stress_all_pinned(g):
     """Every token at the floor: 16-token tiles at exactly -80, 64-token chunks at -320."""
     r = small_recipe("bf16", 1, 256, 2, 128, 128, 64, loga="unif", pin_frac=1.0, beta_std=2.0)
@@ -266,7 +323,7 @@ def test_state_in_place_and_empty_sequence(g):
     r = small_recipe("bf16", 2, 100, 2, 64, 64, 32, s0_std=0.2)
     x = ks.make_prefill(r)
     o_ref, S_ref = oracle.kda_loop(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["S0"])
-    for plan in (g.Plan(1, 0), g.Plan(3, 64)):
+    for plan in (g.Plan(1, 0), g.Plan(3, 64), g.Plan(n_segments=3, dv_block=32, seg0_len=32)):
         o, S = run_prefill(g, x, "bf16", 32, plan=plan, inplace=True)
         check(o, S, o_ref, S_ref, TOL["bf16"], f"S_T aliases S0, {plan}")
     # T = 0 copies the start state
