@@ -775,34 +775,21 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int64_t bid
         }
         __syncthreads();
 
-        // ================= (3) inverses of the diagonal blocks of I + Diag(beta) A (fp32),
-        // right-looking: once x_s is final it is subtracted from every later row
+        // ================= (3) inverses of the diagonal blocks of I + Diag(beta) A (fp32), by
+        // forward substitution on the identity: wave p inverts block p with its rows across the
+        // lanes (lane 16 r + t holds row t of columns 4r .. 4r+3), so a step is four FMAs whose
+        // x_s comes from lane s of the same 16-lane row
         if constexpr (nxt) {
-            if (wave == 0 && (lane >> 4) < NT) {
-                const int p = lane >> 4, j = lane & 15;
+            if (wave < NT) {
+                const int p = wave, t = lane & 15, r4 = 4 * (lane >> 4);
                 const float* Ab = s_ad + p * 256;                // column s at Ab[16 s .. 16 s + 15]
-                float x[16];
+                float nl[15], x[4];
 #pragma unroll
-                for (int t = 0; t < 16; ++t) x[t] = (t == j) ? 1.f : 0.f;
-                // each step needs rows s+1.. of column s; the columns are read two steps ahead
-                // into a ring of three register buffers, so no step waits for its LDS read
-                f32x4 cb[3][4];
-                auto read_col = [&](int s, f32x4* c) {
+                for (int s = 0; s < 15; ++s) nl[s] = -Ab[16 * s + t];        // -beta A[t][s], 0 unless s < t
 #pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4)
-                        if (4 * q4 + 3 > s) c[q4] = *reinterpret_cast<const f32x4*>(Ab + 16 * s + 4 * q4);
-                };
-                read_col(0, cb[0]);
-                read_col(1, cb[1]);
-#pragma unroll
-                for (int s = 0; s < 15; ++s) {
-                    if (s + 2 < 15) read_col(s + 2, cb[(s + 2) % 3]);
-                    const f32x4* c = cb[s % 3];
-#pragma unroll
-                    for (int t = s + 1; t < 16; ++t) x[t] -= c[t >> 2][t & 3] * x[s];
-                }
-#pragma unroll
-                for (int t = 0; t < 16; ++t) s_an[(16 * p + t) * LC + 16 * p + j] = from_f32<OpT>(x[t]);
+                for (int c = 0; c < 4; ++c) x[c] = (t == r4 + c) ? 1.f : 0.f;
+                rows_forward_subst(x, nl);
+                *reinterpret_cast<V4*>(s_an + (16 * p + t) * LC + 16 * p + r4) = L4::from_f(x);
             }
             // v(n+1) into its staging tile (transition columns of pass 1 read zeros)
 #pragma unroll

@@ -192,6 +192,35 @@ template <int M> __device__ __forceinline__ float quad_xor(float x) {
 __device__ __forceinline__ float swap_adjacent(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
 }
+// Forward substitution with a unit lower-triangular 16 x 16 matrix I + L, its rows spread over
+// the 16 lanes of a row: lane t holds row t of four right-hand-side columns in x and row t of
+// the negated strictly lower part in nl (nl[s] = -L[t][s], zero for s >= t).  Step s adds
+// nl[s] x_s to every row, with x_s (final after step s - 1) read from lane s; rows t <= s add
+// zero.  On return lane t holds row t of (I + L)^-1 x.  The whole wave takes part (every lane
+// active).
+//
+// One block of v_fmac_f32_dpp: the multiply-add takes x_s through DPP row_newbcast:s (lane s
+// of the row) as its first source, which the compiler's own DPP folding cannot do for the
+// three-operand FMA it selects.  A DPP read needs two wait states after the instruction that
+// wrote its source: within the block four independent columns per step put three instructions
+// between a column's write and its next read, and the s_nop covers the writes before it.
+#define KDA_RFS_STEP(S, L)                                                         \
+    "v_fmac_f32_dpp %0, %0, %" #L " row_newbcast:" #S " row_mask:0xf bank_mask:0xf\n\t" \
+    "v_fmac_f32_dpp %1, %1, %" #L " row_newbcast:" #S " row_mask:0xf bank_mask:0xf\n\t" \
+    "v_fmac_f32_dpp %2, %2, %" #L " row_newbcast:" #S " row_mask:0xf bank_mask:0xf\n\t" \
+    "v_fmac_f32_dpp %3, %3, %" #L " row_newbcast:" #S " row_mask:0xf bank_mask:0xf\n\t"
+__device__ __forceinline__ void rows_forward_subst(float (&x)[4], const float (&nl)[15]) {
+    asm volatile("s_nop 1\n\t"
+                 KDA_RFS_STEP(0, 4) KDA_RFS_STEP(1, 5) KDA_RFS_STEP(2, 6) KDA_RFS_STEP(3, 7)
+                 KDA_RFS_STEP(4, 8) KDA_RFS_STEP(5, 9) KDA_RFS_STEP(6, 10) KDA_RFS_STEP(7, 11)
+                 KDA_RFS_STEP(8, 12) KDA_RFS_STEP(9, 13) KDA_RFS_STEP(10, 14) KDA_RFS_STEP(11, 15)
+                 KDA_RFS_STEP(12, 16) KDA_RFS_STEP(13, 17) KDA_RFS_STEP(14, 18)
+                 : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3])
+                 : "v"(nl[0]), "v"(nl[1]), "v"(nl[2]), "v"(nl[3]), "v"(nl[4]), "v"(nl[5]), "v"(nl[6]),
+                   "v"(nl[7]), "v"(nl[8]), "v"(nl[9]), "v"(nl[10]), "v"(nl[11]), "v"(nl[12]), "v"(nl[13]),
+                   "v"(nl[14]));
+}
+#undef KDA_RFS_STEP
 // Two adjacent output elements stored as one 4-byte (bf16) or 8-byte (float32) write.
 template <typename OpT> struct Pair2;
 template <> struct Pair2<bf16> {
