@@ -73,10 +73,11 @@ struct Resolved {
 };
 
 // Default lead form: a pass-1 chunk (the widened state [S | M], no q, no o) takes about this
-// fraction of a pass-2 chunk's time on MI355X (bf16, 128 x 128: 6.0 vs 8.5 us in the 1M-token
-// plan), so segment 0, run in pass-2 form beside pass 1, gets this fraction of the others'
-// length; only when the segments are long enough for the rounding to whole chunks not to matter.
-constexpr double kLeadRatio = 0.7;
+// fraction of a pass-2 chunk's time on MI355X (bf16, 128 x 128: 6.1 vs 8.1 us in the 1M-token
+// plan; a sweep of segment 0's length there had its optimum at this ratio), so segment 0, run
+// in pass-2 form beside pass 1, gets this fraction of the others' length; only when the
+// segments are long enough for the rounding to whole chunks not to matter.
+constexpr double kLeadRatio = 0.75;
 constexpr int64_t kLeadMinChunks = 16;
 
 constexpr int64_t kMaxSlots = 1 << 22;   // segment-table entries of one packed call

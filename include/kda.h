@@ -157,8 +157,8 @@ typedef struct {
  * (batch, head) units alone cover MI355X's 256 compute units, otherwise enough
  * segments to cover them (at least two chunks per segment).  When those
  * segments would be long (at least 16 chunks each) the default takes the lead
- * form: one more segment, segment 0 about 0.7 of the others' length (a pass-1
- * chunk takes about 0.7 of a pass-2 chunk's time on MI355X), so the launch that
+ * form: one more segment, segment 0 about 0.75 of the others' length (a pass-1
+ * chunk takes about 0.75 of a pass-2 chunk's time on MI355X), so the launch that
  * runs it beside pass 1 ends together.  The default is
  * the same on every device (it does not query the device), so results round
  * the same everywhere; on a partitioned device pass n_segments yourself.

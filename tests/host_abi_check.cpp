@@ -190,8 +190,8 @@ void chunk_launches() {
     kda_plan_t p{};
     CHECK(kda_chunk_fwd_default_plan(1, 1 << 20, 32, 128, 128, 64, KDA_DTYPE_BF16, &p) == KDA_OK, "plan query");
     // 8 equal segments would fill the 256 CUs in pass 2; the lead form adds segment 0 of
-    // floor(16384 / 8.7) = 1883 -> 16384 - 8 * 1883 = 1320 chunks beside pass 1
-    CHECK(p.n_segments == 9 && p.dv_block == 128 && p.seg0_len == 1320 * 64, "1M plan %d / %d / %lld",
+    // 16384 - 8 * floor(16384 / 8.75) = 16384 - 8 * 1872 = 1408 chunks beside pass 1
+    CHECK(p.n_segments == 9 && p.dv_block == 128 && p.seg0_len == 1408 * 64, "1M plan %d / %d / %lld",
           p.n_segments, p.dv_block, (long long)p.seg0_len);
     {
         Call m;
@@ -207,8 +207,8 @@ void chunk_launches() {
         CHECK(m.run() == KDA_OK, "1M lead plan: %s", kda_last_error());
         CHECK(g_launches.size() == 3, "1M lead plan: %zu launches", g_launches.size());
         if (g_launches.size() == 3) {
-            CHECK(g_launches[0].what == "lead" && g_launches[0].seg_cnt1 == 7 && g_launches[0].seg0_len == 1320 * 64 &&
-                      g_launches[0].seg_len == 1883 * 64 && g_launches[0].n_seg == 9,
+            CHECK(g_launches[0].what == "lead" && g_launches[0].seg_cnt1 == 7 && g_launches[0].seg0_len == 1408 * 64 &&
+                      g_launches[0].seg_len == 1872 * 64 && g_launches[0].n_seg == 9,
                   "lead launch: %s pass-1 segments %d seg0 %lld seg_len %lld", g_launches[0].what.c_str(),
                   g_launches[0].seg_cnt1, (long long)g_launches[0].seg0_len, (long long)g_launches[0].seg_len);
             CHECK(g_launches[1].what == "scan" && g_launches[1].seg_lo == 1, "scan from segment 1");
@@ -220,8 +220,8 @@ void chunk_launches() {
         e.use_plan = true;
         e.plan = p;
         g_launches.clear();
-        CHECK(e.run() == KDA_OK && g_launches.size() == 3 && g_launches[0].seg_len == 1883 * 64 &&
-                  g_launches[0].seg0_len == 1320 * 64,
+        CHECK(e.run() == KDA_OK && g_launches.size() == 3 && g_launches[0].seg_len == 1872 * 64 &&
+                  g_launches[0].seg0_len == 1408 * 64,
               "explicit copy of the default plan");
         // the lead form's own checks
         { Call x = e; x.plan.seg0_len = 100; expect_reject(x, KDA_ERR_UNSUPPORTED, "seg0_len not a multiple of chunk"); }
