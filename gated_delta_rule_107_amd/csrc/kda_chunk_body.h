@@ -167,6 +167,18 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int64_t bid
     const int colw = (int)cb * DVB + 16 * wave;      // first value column of this wave
     const bool chain = 16 * wave < DVB;              // this wave owns value columns
     const bool mchain = MODE == 1 && 16 * wave < DK; // ... transition columns 16w.. of M (MODE 1)
+    // Where this unit's final state goes, fixed here so that one pointer, not its ingredients,
+    // stays live across the chunk loop: MODE 0 the last segment's S_T, or in the lead form
+    // segment 0's final state (the true start of segment 1); MODE 1 the pair's slots.
+    float* fin_s = nullptr;
+    bf16* fin_m = nullptr;
+    if constexpr (MODE == 0) {
+        if (last_seg) fin_s = a.s_final + srow * DK * dv;
+        else if (a.seg0_len > 0 && seg == 0 && !a.seg_table) fin_s = a.starts + (bh * a.n_seg + 1) * DK * dv;
+    } else {
+        fin_s = a.s_loc + (bh * a.n_seg + seg) * DK * dv;
+        fin_m = reinterpret_cast<bf16*>(a.m_tr) + (bh * a.n_seg + seg) * 2 * DK * DK;
+    }
 
     const OpT* gq = reinterpret_cast<const OpT*>(a.q);
     const OpT* gk = reinterpret_cast<const OpT*>(a.k);
@@ -827,21 +839,16 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int64_t bid
         const int lane = threadIdx.x & 63, g4 = 4 * (lane >> 4), jl = lane & 15;
         const int col = colw + jl;
         if constexpr (MODE == 0) {
-            // the last segment's state is S_T; in the lead form segment 0's is the true start of
-            // segment 1, which the scan and pass 2 read from the start states
-            float* dst = nullptr;
-            if (chain && last_seg) dst = a.s_final + srow * DK * dv;
-            else if (chain && a.seg0_len > 0 && seg == 0 && !a.seg_table) dst = a.starts + (bh * a.n_seg + 1) * DK * dv;
-            if (dst) {
+            if (chain && fin_s) {
 #pragma unroll
                 for (int tau = 0; tau < NCT; ++tau)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) dst[(16 * tau + g4 + r) * dv + col] = Sacc[0][tau][r];
+                    for (int r = 0; r < 4; ++r) fin_s[(16 * tau + g4 + r) * dv + col] = Sacc[0][tau][r];
             }
         } else {
             if (chain) {
                 // the zero-start state goes to the scan in its accumulator-tile order
-                float* sl = a.s_loc + (bh * a.n_seg + seg) * DK * dv;
+                float* sl = fin_s;
 #pragma unroll
                 for (int tau = 0; tau < NCT; ++tau)
                     *reinterpret_cast<f32x4*>(sl + sloc_index(DK, 16 * tau + g4, col)) = Sacc[0][tau];
@@ -849,7 +856,7 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int64_t bid
             if (mchain) {
                 // the transition goes to the scan already split into bf16 high and low planes, in
                 // the order of the scan's A operand
-                bf16* mh = reinterpret_cast<bf16*>(a.m_tr) + (bh * a.n_seg + seg) * 2 * DK * DK;
+                bf16* mh = fin_m;
 #pragma unroll
                 for (int tau = 0; tau < NCT; ++tau)
 #pragma unroll

@@ -17,17 +17,19 @@
 
 namespace kda {
 
-template <typename OpT, int DK, int C, bool EXT>
+// EXT0 / EXT1: the extended instantiation (see chunk_kernel) for segment 0 / for pass 1; pass 1
+// has no checkpoints, so a call that asks only for those runs its plain body.
+template <typename OpT, int DK, int C, bool EXT0, bool EXT1>
 __global__ __launch_bounds__(512) void chunk_lead_kernel(ChunkArgs a0, ChunkArgs a1, int64_t n0) {
     const int64_t bid = blockIdx.x;                // uniform: each workgroup runs one of the two
-    if (bid < n0) chunk_body<OpT, DK, C, 0, EXT>(a0, bid);
-    else chunk_body<OpT, DK, C, 1, EXT>(a1, bid - n0);
+    if (bid < n0) chunk_body<OpT, DK, C, 0, EXT0>(a0, bid);
+    else chunk_body<OpT, DK, C, 1, EXT1>(a1, bid - n0);
 }
 
-template <typename OpT, int DK, int C, bool EXT>
+template <typename OpT, int DK, int C, bool EXT0, bool EXT1>
 static hipError_t launch_lead_e(const ChunkArgs& a0, const ChunkArgs& a1, hipStream_t st) {
     constexpr size_t lds = (size_t)lds_layout(sizeof(OpT), DK, C).total;
-    auto kern = chunk_lead_kernel<OpT, DK, C, EXT>;
+    auto kern = chunk_lead_kernel<OpT, DK, C, EXT0, EXT1>;
     static std::once_flag once;
     static hipError_t attr_err = hipSuccess;
     std::call_once(once, [&] {
@@ -44,8 +46,9 @@ static hipError_t launch_lead_e(const ChunkArgs& a0, const ChunkArgs& a1, hipStr
 
 template <typename OpT, int DK, int C>
 static hipError_t launch_lead_c(const ChunkArgs& a0, const ChunkArgs& a1, hipStream_t st) {
-    const bool ext = a0.flags != 0 || a0.ckpt;
-    return ext ? launch_lead_e<OpT, DK, C, true>(a0, a1, st) : launch_lead_e<OpT, DK, C, false>(a0, a1, st);
+    if (a0.flags != 0) return launch_lead_e<OpT, DK, C, true, true>(a0, a1, st);
+    if (a0.ckpt) return launch_lead_e<OpT, DK, C, true, false>(a0, a1, st);
+    return launch_lead_e<OpT, DK, C, false, false>(a0, a1, st);
 }
 
 template <typename OpT, int DK>
