@@ -725,26 +725,55 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int64_t bid
             // every task's loads and products come before any of the wave's stores.
             constexpr int NPAIR = NT * (NT + 1) / 2;
             constexpr int NSLOT = (NPAIR + 7) / 8;
+            // With outputs and more than 8 pairs (64-token chunks: 10), the pairs past the first 8
+            // are split into their A and M tiles, one tile per wave (waves 0 .. 2 (NPAIR - 8) - 1),
+            // so that no wave carries two pairs; a split tile reads its right operand itself.
+            constexpr bool SPLIT = want_o && NPAIR > 8;
+            static_assert(!SPLIT || (NSLOT == 2 && 2 * (NPAIR - 8) <= 8), "tile split assumes one extra slot");
+            auto pair_of = [&](int task, int& p, int& pp) {
+                int pr = task;
+                p = 0;
+                while (pr > p) { pr -= p + 1; ++p; }
+                pp = pr;                                          // pp <= p
+            };
+            auto right_of = [&](int p, int pp, const OpT*& right, int& rrow, const float*& fac) {
+                right = s_rh;
+                rrow = 16 * pp;
+                fac = nullptr;
+                if (RV) {
+                    if (p == pp) right = s_rd;
+                    else if (p - pp == 2) right = s_rf;                           // rows 16 pp
+                    else if (p - pp == 3) { right = s_rf; rrow = 32 + 16 * pp; }
+                } else {
+                    fac = p == pp ? s_fd + p * DKP : (p - pp >= 2 ? s_fo + pair_fo_index(p, pp) * DKP : nullptr);
+                }
+            };
             f32x4 acc[NSLOT], accm[NSLOT];
 #pragma unroll
             for (int sl = 0; sl < NSLOT; ++sl) {
-                const int task = wave + 8 * sl;
                 acc[sl] = f32x4{0.f, 0.f, 0.f, 0.f};
                 accm[sl] = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (task < NPAIR) {
-                    int pr = task, p = 0;
-                    while (pr > p) { pr -= p + 1; ++p; }
-                    const int pp = pr;                                // pp <= p
-                    const OpT* right = s_rh;
-                    int rrow = 16 * pp;
-                    const float* fac = nullptr;
-                    if (RV) {
-                        if (p == pp) right = s_rd;
-                        else if (p - pp == 2) right = s_rf;                           // rows 16 pp
-                        else if (p - pp == 3) { right = s_rf; rrow = 32 + 16 * pp; }
-                    } else {
-                        fac = p == pp ? s_fd + p * DKP : (p - pp >= 2 ? s_fo + pair_fo_index(p, pp) * DKP : nullptr);
+                if (SPLIT && sl == 1) {
+                    if (wave < 2 * (NPAIR - 8)) {                 // tile (wave & 1 ? M : A) of pair 8 + wave / 2
+                        int p, pp, rrow;
+                        pair_of(8 + wave / 2, p, pp);
+                        const OpT* right;
+                        const float* fac;
+                        right_of(p, pp, right, rrow, fac);
+                        const OpT* left = (wave & 1) ? s_ql : s_kl;
+#pragma unroll
+                        for (int ks = 0; ks < KNAT; ++ks)
+                            acc[sl] = MF::nat(left, LDK, 16 * p, right, LDK, rrow, ks * MF::KS, fac, acc[sl], lane);
                     }
+                    continue;
+                }
+                const int task = wave + 8 * sl;
+                if (task < NPAIR) {
+                    int p, pp, rrow;
+                    pair_of(task, p, pp);
+                    const OpT* right;
+                    const float* fac;
+                    right_of(p, pp, right, rrow, fac);
 #pragma unroll
                     for (int ks = 0; ks < KNAT; ++ks) {
                         if constexpr (want_o)
@@ -754,34 +783,47 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int64_t bid
                     }
                 }
             }
+            // an A tile: the diagonal block of beta A goes to s_ad (strictly lower, transposed:
+            // [p][s][t]), the others, as -beta A, to s_an; an M tile goes to s_mm (masked on the diagonal)
+            auto store_a = [&](int p, int pp, const f32x4& x) {
+                if (p == pp) {
+                    f32x4 col;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) col[r] = (jl < g4 + r) ? x[r] * sb_n[16 * p + g4 + r] : 0.f;
+                    *reinterpret_cast<f32x4*>(s_ad + (p * 16 + jl) * 16 + g4) = col;
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int t = 16 * p + g4 + r, s = 16 * pp + jl;
+                        s_an[t * LC + s] = from_f32<OpT>(-x[r] * sb_n[t]);
+                    }
+                }
+            };
+            auto store_m = [&](int p, int pp, const f32x4& x) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int tr = g4 + r;
+                    const int t = 16 * p + tr, s = 16 * pp + jl;
+                    s_mm[t * LC + s] = from_f32<OpT>((p == pp && jl > tr) ? 0.f : x[r]);
+                }
+            };
 #pragma unroll
             for (int sl = 0; sl < NSLOT; ++sl) {
+                if (SPLIT && sl == 1) {
+                    if (wave < 2 * (NPAIR - 8)) {
+                        int p, pp;
+                        pair_of(8 + wave / 2, p, pp);
+                        if (wave & 1) store_m(p, pp, acc[sl]);
+                        else store_a(p, pp, acc[sl]);
+                    }
+                    continue;
+                }
                 const int task = wave + 8 * sl;
                 if (task < NPAIR) {
-                    int pr = task, p = 0;
-                    while (pr > p) { pr -= p + 1; ++p; }
-                    const int pp = pr;
-                    if (p == pp) {
-                        // diagonal block of beta A, strictly lower, stored transposed: [p][s][t]
-                        f32x4 col;
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) col[r] = (jl < g4 + r) ? acc[sl][r] * sb_n[16 * p + g4 + r] : 0.f;
-                        *reinterpret_cast<f32x4*>(s_ad + (p * 16 + jl) * 16 + g4) = col;
-                    } else {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int t = 16 * p + g4 + r, s = 16 * pp + jl;
-                            s_an[t * LC + s] = from_f32<OpT>(-acc[sl][r] * sb_n[t]);
-                        }
-                    }
-                    if constexpr (want_o) {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int tr = g4 + r;
-                            const int t = 16 * p + tr, s = 16 * pp + jl;
-                            s_mm[t * LC + s] = from_f32<OpT>((p == pp && jl > tr) ? 0.f : accm[sl][r]);
-                        }
-                    }
+                    int p, pp;
+                    pair_of(task, p, pp);
+                    store_a(p, pp, acc[sl]);
+                    if constexpr (want_o) store_m(p, pp, accm[sl]);
                 }
             }
         }
