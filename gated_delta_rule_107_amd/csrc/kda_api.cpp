@@ -73,12 +73,14 @@ struct Resolved {
 };
 
 // Default lead form: a pass-1 chunk (the widened state [S | M], no q, no o) takes about this
-// fraction of a pass-2 chunk's time on MI355X (bf16, 128 x 128: 6.1 vs 8.1 us in the 1M-token
-// plan; a sweep of segment 0's length there had its optimum at this ratio), so segment 0, run
-// in pass-2 form beside pass 1, gets this fraction of the others' length; only when the
-// segments are long enough for the rounding to whole chunks not to matter.
+// fraction r of a pass-2 chunk's time on MI355X (bf16, 128 x 128: 6.1 vs 8.1 us in the 1M-token
+// plan; a sweep of segment 0's length there had its optimum at this ratio).  In pass-2-chunk
+// units, S equal segments of L chunks cost L (1 + r) (pass 1, then pass 2); the lead form with S
+// segments of l chunks after a segment 0 of c0 = chunks - S l costs max(c0, r l) + l (segment
+// 0 beside pass 1, then pass 2).  The default takes the lead form when that is at least
+// kLeadGain cheaper, with l the better of the two whole numbers around chunks / (S + r).
 constexpr double kLeadRatio = 0.75;
-constexpr int64_t kLeadMinChunks = 16;
+constexpr double kLeadGain = 0.98;
 
 constexpr int64_t kMaxSlots = 1 << 22;   // segment-table entries of one packed call
 
@@ -160,13 +162,25 @@ kda_status_t resolve_plan(int64_t B, int64_t T, int32_t H, int32_t dk, int32_t d
     out->n_seg = nchunks == 0 ? 1 : (int32_t)((nchunks + seg_chunks - 1) / seg_chunks);
     out->dv_block = dvb;
     if (dflt && out->n_seg >= 2) {
-        // lead form: one segment more, segment 0 kLeadRatio of the others' length, so that
-        // the launch running it beside pass 1 ends together and pass 2 covers one segment fewer
-        const int64_t S = out->n_seg;
-        const int64_t lc = (int64_t)((double)nchunks / ((double)S + kLeadRatio));
-        if (lc >= kLeadMinChunks) {
-            out->seg0_len = (nchunks - S * lc) * chunk;              // >= kLeadRatio lc chunks
-            out->seg_len = lc * chunk;
+        // lead form: one segment more, segment 0 sized so that the launch running it beside
+        // pass 1 ends together, and pass 2 covering one segment fewer (cost model above)
+        const int64_t S = nseg;                                     // pass-2 workgroups per unit
+        const double r = kLeadRatio;
+        double best = (double)seg_chunks * (1.0 + r) * kLeadGain;
+        int64_t best_l = 0;
+        const int64_t lf = (int64_t)((double)nchunks / ((double)S + r));
+        for (int64_t l = lf; l <= lf + 1; ++l) {
+            const int64_t c0 = nchunks - S * l;
+            if (l < 2 || c0 < 1) continue;
+            const double cost = ((double)c0 > r * (double)l ? (double)c0 : r * (double)l) + (double)l;
+            if (cost < best) {
+                best = cost;
+                best_l = l;
+            }
+        }
+        if (best_l > 0) {
+            out->seg0_len = (nchunks - S * best_l) * chunk;
+            out->seg_len = best_l * chunk;
             out->n_seg = (int32_t)(S + 1);
         }
     }

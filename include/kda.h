@@ -155,11 +155,11 @@ typedef struct {
 
 /* Fills *plan with the library's default for this problem: one pass when the
  * (batch, head) units alone cover MI355X's 256 compute units, otherwise enough
- * segments to cover them (at least two chunks per segment).  When those
- * segments would be long (at least 16 chunks each) the default takes the lead
- * form: one more segment, segment 0 about 0.75 of the others' length (a pass-1
- * chunk takes about 0.75 of a pass-2 chunk's time on MI355X), so the launch that
- * runs it beside pass 1 ends together.  The default is
+ * segments to cover them (at least two chunks per segment).  The default takes
+ * the lead form (seg0_len) when, counting a pass-1 chunk as 0.75 of a pass-2
+ * chunk's time (as measured on MI355X), it is at least 2 % shorter than the
+ * equal segments: one more segment, segment 0 sized so that the launch running
+ * it beside pass 1 ends together.  The default is
  * the same on every device (it does not query the device), so results round
  * the same everywhere; on a partitioned device pass n_segments yourself.
  * Returns KDA_OK or an argument error.  Makes no HIP call.

@@ -468,6 +468,21 @@ def test_long_sequence_segments_sampled(g):
                    f"long sequence h={h} ({p})")
 
 
+def test_lead_default_plan_two_batch_rows(g):
+    """The library's default plan chooses the lead form for long sequences: here 2 batch rows x
+    2 heads (dk = dv = 64) of 78,720 tokens (1,230 chunks), i.e. 4 units and 64 equal segments
+    of 20 chunks, against the lead form's 64 segments of 19 chunks after a segment 0 of 14.
+    Every (batch, head) is checked end to end, with a start state, per 64-token chunk."""
+    r = small_recipe("bf16", 2, 78720, 2, 64, 64, 64, s0_std=0.05)
+    p = g.default_plan(r.B, r.T, r.H, r.dk, r.dv, r.chunk)
+    _say(f"case: default lead plan, B2 T78720 H2 64/64 ({p})")
+    assert p.n_segments > 2 and p.seg0_len > 0
+    x = ks.make_prefill(r)
+    o, S = run_prefill(g, x, "bf16", 64)
+    o_ref, S_ref = oracle.kda_chunked(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["S0"], chunk=64)
+    check_full(o, S, o_ref, S_ref, TOL["bf16"], CHUNK_TOL["bf16"], f"default lead plan ({p})")
+
+
 def _oracle_head(r, h):
     """The oracle over the whole sequence of one keyed head (float64, chunked form)."""
     xs = {n: ks.gen_head(r, n, 0, h)[None, :, None] for n in ("q", "k", "v", "log_alpha", "beta")}
