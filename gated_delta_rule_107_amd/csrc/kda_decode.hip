@@ -235,13 +235,14 @@ __host__ __device__ constexpr int m_index(int t, int s) { return 6 + t * (t + 1)
 // S <- Diag(e^Gamma_last) S + sum_t (k_t e^(Gamma_last - Gamma_t)) u_t^T, so no cumulative
 // decay spans more than VG drafts.  With normalisation the raw k, q are used and the norms
 // scale the results in the reducer.
-// 512 threads per (n, h), 8 state rows each, at up to 128 VGPRs (4 waves per SIMD): two
-// workgroups per CU, so as much of the state is in flight as with the step kernel.  A group's
+// 256 threads per (n, h), 16 state rows each, at up to 168 VGPRs (3 waves per SIMD): three
+// workgroups, i.e. three states, per CU in flight (at 512 threads and 8 rows two fitted, and
+// verify was 8 % slower; at 4 waves per SIMD the 256-thread form spills).  A group's
 // per-draft inputs are loaded before the state (the first group) or during the previous
 // group, so that neither the small products nor the solve wait for memory.
-constexpr int VERIFY_THREADS = 512;
+constexpr int VERIFY_THREADS = 256;
 template <typename ET, int DK, int DV, bool NORM>
-__global__ __launch_bounds__((DecodeMap<DK, DV, VERIFY_THREADS>::NTB)) __attribute__((amdgpu_waves_per_eu(4))) void verify_kernel(
+__global__ __launch_bounds__((DecodeMap<DK, DV, VERIFY_THREADS>::NTB)) __attribute__((amdgpu_waves_per_eu(3))) void verify_kernel(
     const float* __restrict__ state, const ET* __restrict__ q, const ET* __restrict__ k,
     const ET* __restrict__ v, const float* __restrict__ log_alpha, const float* __restrict__ beta,
     ET* __restrict__ o, int H, int n_tok, unsigned flags) {
