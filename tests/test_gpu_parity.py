@@ -180,7 +180,10 @@ def test_last_chunk_full_small_chunks(g, shape, nseg):
                                    # fewer value columns than key channels: the segment pass's two
                                    # halves [S | M] differ in width
                                    ("bf16", 1, 500, 2, 128, 64, 64), ("f32", 1, 200, 2, 32, 16, 16),
-                                   ("bf16", 1, 300, 3, 64, 32, 32)],
+                                   ("bf16", 1, 300, 3, 64, 32, 32),
+                                   # float32 operands in 64-token chunks (dk <= 64 for float32; segment
+                                   # pass 1 defers two of its tiles to the inverse phase)
+                                   ("f32", 1, 257, 1, 64, 64, 64)],
                          ids=lambda s: "-".join(map(str, s)))
 @pytest.mark.parametrize("nseg", [2, 3, 8])
 def test_segments(g, shape, nseg):
