@@ -354,7 +354,7 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int64_t bid
     //   (4) v(n+1) into registers in the accumulator layout.
     // beta and e^Gamma_C of chunk n are read in (1) while gate prep writes chunk n+1's, so
     // they have two slots (chunk n uses slot n & 1); Khat^T(n+1) waits in registers until (2).
-    f32x4 X[NG][NT], QS[NT];                         // Kt S, Qt S of the chunk chained next
+    f32x4 X[NG][NT], QS[NT];                         // Kt S, (Qt S)^T of the chunk chained next
     B16 vr[NT];                                      // its v (value columns)
     V4 khr[4];                                       // Khat^T(n+1): 4 channels x 4 tokens
 
@@ -450,24 +450,19 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int64_t bid
 
         // ================= (1c) O = QS + M U of chunk n, stored straight from the accumulators
         // (its store instructions issue while the gate prep below keeps the vector units busy).
-        // Adjacent lanes pair up their columns: the even lane writes rows 4g, 4g+1 and the
-        // odd lane rows 4g+2, 4g+3 of columns (jl & ~1, jl | 1), two elements per store.
+        // QS and O are held transposed: lane (g, jl) holds token 16 p + jl, value columns 4g ..
+        // 4g+3, written by one store; rows past the chunk's last token (and every row of a wave
+        // without value columns) fall outside the store's buffer range and are dropped.
         if constexpr (cur && want_o) {
-            using P2 = Pair2<OpT>;
-            typename P2::V* o_w = reinterpret_cast<typename P2::V*>(go + ((b * T + t0) * H + h) * (int64_t)dv + colw);
-            const bool odd = jl & 1;
-            const int cpair = jl & ~1;
+            const unsigned rowb = (unsigned)tok_v * E;
+            const __amdgpu_buffer_rsrc_t o_rs =
+                bounded_rsrc(go + ((b * T + t0) * H + h) * (int64_t)dv + colw, chain ? (unsigned)Tc * rowb : 0u);
+            const unsigned o_off = tok_elem_off(jl, tok_v, g4) * (unsigned)E;
 #pragma unroll
             for (int p = 0; p < NT; ++p) {
 #pragma unroll
-                for (int qq = 0; qq <= p; ++qq) QS[p] = MF::k16(s_mm, LC, 16 * p, 16 * qq, ub[0][qq], QS[p], lane);
-                const float n0 = swap_adjacent(odd ? QS[p][0] : QS[p][2]);
-                const float n1 = swap_adjacent(odd ? QS[p][1] : QS[p][3]);
-                const int ra = 16 * p + g4 + (odd ? 2 : 0);
-                const typename P2::V w0 = odd ? P2::make(n0, QS[p][2]) : P2::make(QS[p][0], n0);
-                const typename P2::V w1 = odd ? P2::make(n1, QS[p][3]) : P2::make(QS[p][1], n1);
-                if (chain && ra < Tc) *at_bytes(o_w, tok_elem_off(ra, tok_v, cpair) * (unsigned)E) = w0;
-                if (chain && ra + 1 < Tc) *at_bytes(o_w, tok_elem_off(ra + 1, tok_v, cpair) * (unsigned)E) = w1;
+                for (int qq = 0; qq <= p; ++qq) QS[p] = MF::k16t(s_mm, LC, 16 * p, 16 * qq, ub[0][qq], QS[p], lane);
+                Store4<OpT>::st(o_rs, o_off + 16 * p * rowb, QS[p]);
             }
         }
 
@@ -675,7 +670,7 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int64_t bid
                         if constexpr (NCT == 1) {
 #pragma unroll
                             for (int G = 0; G < NG; ++G) X[G][p] = MF::k16(s_kt, LKQ, 16 * p, 0, sb[G][0], X[G][p], lane);
-                            if (want_o) QS[p] = MF::k16(s_qt, LKQ, 16 * p, 0, sb[0][0], QS[p], lane);
+                            if (want_o) QS[p] = MF::k16t(s_qt, LKQ, 16 * p, 0, sb[0][0], QS[p], lane);
                         } else {
 #pragma unroll
                             for (int s2 = 0; s2 < NCT / 2; ++s2) {
@@ -684,8 +679,8 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int64_t bid
                                     X[G][p] = MF::k32(s_kt, LKQ, 16 * p, 32 * s2, sb[G][2 * s2], sb[G][2 * s2 + 1],
                                                       X[G][p], lane);
                                 if (want_o)
-                                    QS[p] = MF::k32(s_qt, LKQ, 16 * p, 32 * s2, sb[0][2 * s2], sb[0][2 * s2 + 1], QS[p],
-                                                    lane);
+                                    QS[p] = MF::k32t(s_qt, LKQ, 16 * p, 32 * s2, sb[0][2 * s2], sb[0][2 * s2 + 1], QS[p],
+                                                     lane);
                             }
                         }
                     }
@@ -714,7 +709,7 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int64_t bid
 #pragma unroll
                             for (int G = 0; G < NG; ++G)
                                 X[G][p] = MF::mma32(ax[p & 1][s2], sb[G][2 * s2], sb[G][2 * s2 + 1], X[G][p]);
-                            if (want_o) QS[p] = MF::mma32(aq[p & 1][s2], sb[0][2 * s2], sb[0][2 * s2 + 1], QS[p]);
+                            if (want_o) QS[p] = MF::mma32t(aq[p & 1][s2], sb[0][2 * s2], sb[0][2 * s2 + 1], QS[p]);
                         }
                         __builtin_amdgcn_sched_barrier(0);
                     }

@@ -74,6 +74,23 @@ template <> struct MM<bf16> {
                                                 f32x4 acc, int lane) {
         return mma32(ld32(A, ld, r0, c0, lane), b0, b1, acc);
     }
+    // The same products transposed: acc^T += A B, i.e. lane l then holds (A B)[l % 16][4*(l/16) + r].
+    // The A and B fragments of a 16x16 instruction have the same lane layout (lane l: row or
+    // column l % 16, contraction block l / 16), so swapping the two operands transposes the result.
+    static __device__ __forceinline__ f32x4 k16t(const bf16* A, int ld, int r0, int c0, B16 b, f32x4 acc,
+                                                 int lane) {
+        const bf16x4 a = ld16(A, ld, r0, c0, lane);
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, b),
+                                                         __builtin_bit_cast(i16x4, a), acc, 0, 0, 0);
+    }
+    static __device__ __forceinline__ f32x4 mma32t(const A32& a, B16 b0, B16 b1, f32x4 acc) {
+        const bf16x8 b = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, a, acc, 0, 0, 0);
+    }
+    static __device__ __forceinline__ f32x4 k32t(const bf16* A, int ld, int r0, int c0, B16 b0, B16 b1,
+                                                 f32x4 acc, int lane) {
+        return mma32t(ld32(A, ld, r0, c0, lane), b0, b1, acc);
+    }
     // natural order, both operands in LDS:
     // acc += (A[ra + m][k0 + kk] * fac[k0 + kk]) * Bm[rb + n][k0 + kk] over kk < 32
     static __device__ __forceinline__ f32x4 nat(const bf16* A, int lda, int ra, const bf16* Bm, int ldb,
@@ -156,6 +173,25 @@ template <> struct MM<float> {
         for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[s], b1[s], acc, 0, 0, 0);
         return acc;
     }
+    // transposed products (see MM<bf16>::k16t)
+    static __device__ __forceinline__ f32x4 k16t(const float* A, int ld, int r0, int c0, B16 b, f32x4 acc,
+                                                 int lane) {
+        const f32x4 a = ld16(A, ld, r0, c0, lane);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(b[s], a[s], acc, 0, 0, 0);
+        return acc;
+    }
+    static __device__ __forceinline__ f32x4 mma32t(const A32& a, B16 b0, B16 b1, f32x4 acc) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(b0[s], a.lo[s], acc, 0, 0, 0);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(b1[s], a.hi[s], acc, 0, 0, 0);
+        return acc;
+    }
+    static __device__ __forceinline__ f32x4 k32t(const float* A, int ld, int r0, int c0, B16 b0, B16 b1,
+                                                 f32x4 acc, int lane) {
+        return mma32t(ld32(A, ld, r0, c0, lane), b0, b1, acc);
+    }
     static __device__ __forceinline__ f32x4 nat(const float* A, int lda, int ra, const float* Bm, int ldb,
                                                 int rb, int k0, const float* fac, f32x4 acc, int lane) {
         float a = A[(ra + (lane & 15)) * lda + k0 + (lane >> 4)];
@@ -188,10 +224,6 @@ template <int N> __device__ __forceinline__ float row_shr(float x) {
 template <int M> __device__ __forceinline__ float quad_xor(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), M == 1 ? 0xB1 : 0x4E, 0xF, 0xF, false));
 }
-// Value of the neighbouring lane (lanes 2i and 2i+1 swap).
-__device__ __forceinline__ float swap_adjacent(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
-}
 // Forward substitution with a unit lower-triangular 16 x 16 matrix I + L, its rows spread over
 // the 16 lanes of a row: lane t holds row t of four right-hand-side columns in x and row t of
 // the negated strictly lower part in nl (nl[s] = -L[t][s], zero for s >= t).  Step s adds
@@ -221,15 +253,27 @@ __device__ __forceinline__ void rows_forward_subst(float (&x)[4], const float (&
                    "v"(nl[14]));
 }
 #undef KDA_RFS_STEP
-// Two adjacent output elements stored as one 4-byte (bf16) or 8-byte (float32) write.
-template <typename OpT> struct Pair2;
-template <> struct Pair2<bf16> {
-    typedef bf16x2 V;
-    __device__ static V make(float a, float b) { return __builtin_bit_cast(V, pack_bf16x2(a, b)); }
+// ---------------------------------------------------------------- bounded row stores
+// A raw buffer resource (byte offsets, no stride) over the `bytes` bytes from `base`: a store
+// whose offset lies at or past the end is dropped by the hardware's range check, so the rows of
+// a chunk past its last token need no branch.  Word 3 is the gfx9 raw-buffer format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t bounded_rsrc(void* base, unsigned bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(base, 0, (int)bytes, 0x00020000);
+}
+typedef unsigned u32ev2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32ev4 __attribute__((ext_vector_type(4)));
+// Four consecutive output elements, one store at byte offset `off` of the resource.
+template <typename OpT> struct Store4;
+template <> struct Store4<bf16> {
+    static __device__ __forceinline__ void st(__amdgpu_buffer_rsrc_t rs, unsigned off, const f32x4& x) {
+        const u32ev2 w = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+        __builtin_amdgcn_raw_buffer_store_b64(w, rs, (int)off, 0, 0);
+    }
 };
-template <> struct Pair2<float> {
-    typedef float __attribute__((__vector_size__(2 * sizeof(float)))) V;
-    __device__ static V make(float a, float b) { return V{a, b}; }
+template <> struct Store4<float> {
+    static __device__ __forceinline__ void st(__amdgpu_buffer_rsrc_t rs, unsigned off, const f32x4& x) {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32ev4, x), rs, (int)off, 0, 0);
+    }
 };
 // ---------------------------------------------------------------- global addressing
 // base (wave-uniform, in scalar registers) + a 32-bit byte offset per lane: the form the
