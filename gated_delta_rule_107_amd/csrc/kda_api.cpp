@@ -73,13 +73,13 @@ struct Resolved {
 };
 
 // Default lead form: a pass-1 chunk (the widened state [S | M], no q, no o) takes about this
-// fraction r of a pass-2 chunk's time on MI355X (bf16, 128 x 128: 6.1 vs 8.1 us in the 1M-token
+// fraction r of a pass-2 chunk's time on MI355X (bf16, 128 x 128: 6.0 vs 7.5 us in the 1M-token
 // plan; a sweep of segment 0's length there had its optimum at this ratio).  In pass-2-chunk
 // units, S equal segments of L chunks cost L (1 + r) (pass 1, then pass 2); the lead form with S
 // segments of l chunks after a segment 0 of c0 = chunks - S l costs max(c0, r l) + l (segment
 // 0 beside pass 1, then pass 2).  The default takes the lead form when that is at least
 // kLeadGain cheaper, with l the better of the two whole numbers around chunks / (S + r).
-constexpr double kLeadRatio = 0.75;
+constexpr double kLeadRatio = 0.8;
 constexpr double kLeadGain = 0.98;
 
 constexpr int64_t kMaxSlots = 1 << 22;   // segment-table entries of one packed call

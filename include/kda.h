@@ -156,7 +156,7 @@ typedef struct {
 /* Fills *plan with the library's default for this problem: one pass when the
  * (batch, head) units alone cover MI355X's 256 compute units, otherwise enough
  * segments to cover them (at least two chunks per segment).  The default takes
- * the lead form (seg0_len) when, counting a pass-1 chunk as 0.75 of a pass-2
+ * the lead form (seg0_len) when, counting a pass-1 chunk as 0.8 of a pass-2
  * chunk's time (as measured on MI355X), it is at least 2 % shorter than the
  * equal segments: one more segment, segment 0 sized so that the launch running
  * it beside pass 1 ends together.  The default is

@@ -189,14 +189,14 @@ void chunk_launches() {
     // the 1M-token workload's default plan: 8 segments of 131,072 tokens
     kda_plan_t p{};
     CHECK(kda_chunk_fwd_default_plan(1, 1 << 20, 32, 128, 128, 64, KDA_DTYPE_BF16, &p) == KDA_OK, "plan query");
-    // 8 equal segments would fill the 256 CUs in pass 2 (cost 2048 x 1.75 = 3584 pass-2 chunks);
-    // the lead form with l = 1873 (l = floor(16384 / 8.75) = 1872 costs 1408 + 1872 = 3280; 1873
-    // costs max(1400, 1404.75) + 1873 = 3277.75) adds segment 0 of 1400 chunks beside pass 1
-    CHECK(p.n_segments == 9 && p.dv_block == 128 && p.seg0_len == 1400 * 64, "1M plan %d / %d / %lld",
+    // 8 equal segments would fill the 256 CUs in pass 2 (cost 2048 x 1.8 = 3686.4 pass-2 chunks);
+    // the lead form with l = 1862 (l = floor(16384 / 8.8) = 1861 costs 1496 + 1861 = 3357; 1862
+    // costs max(1488, 1489.6) + 1862 = 3351.6) adds segment 0 of 1488 chunks beside pass 1
+    CHECK(p.n_segments == 9 && p.dv_block == 128 && p.seg0_len == 1488 * 64, "1M plan %d / %d / %lld",
           p.n_segments, p.dv_block, (long long)p.seg0_len);
-    // 4 units (B2 H2): 64 equal segments of 20 chunks cost 35; at 1,280 chunks the lead form's
+    // 4 units (B2 H2): 64 equal segments of 20 chunks cost 36; at 1,280 chunks the lead form's
     // whole segments leave segment 0 either 64 chunks long (l = 19) or empty (l = 20), so the
-    // default keeps equal segments; at 1,230 chunks l = 19 leaves 14 (cost 33.25) and it leads
+    // default keeps equal segments; at 1,230 chunks l = 19 leaves 14 (cost 34.2) and it leads
     {
         kda_plan_t q{};
         CHECK(kda_chunk_fwd_default_plan(2, 81920, 2, 64, 64, 64, KDA_DTYPE_BF16, &q) == KDA_OK && q.n_segments == 64 &&
@@ -220,8 +220,8 @@ void chunk_launches() {
         CHECK(m.run() == KDA_OK, "1M lead plan: %s", kda_last_error());
         CHECK(g_launches.size() == 3, "1M lead plan: %zu launches", g_launches.size());
         if (g_launches.size() == 3) {
-            CHECK(g_launches[0].what == "lead" && g_launches[0].seg_cnt1 == 7 && g_launches[0].seg0_len == 1400 * 64 &&
-                      g_launches[0].seg_len == 1873 * 64 && g_launches[0].n_seg == 9,
+            CHECK(g_launches[0].what == "lead" && g_launches[0].seg_cnt1 == 7 && g_launches[0].seg0_len == 1488 * 64 &&
+                      g_launches[0].seg_len == 1862 * 64 && g_launches[0].n_seg == 9,
                   "lead launch: %s pass-1 segments %d seg0 %lld seg_len %lld", g_launches[0].what.c_str(),
                   g_launches[0].seg_cnt1, (long long)g_launches[0].seg0_len, (long long)g_launches[0].seg_len);
             CHECK(g_launches[1].what == "scan" && g_launches[1].seg_lo == 1, "scan from segment 1");
@@ -233,8 +233,8 @@ void chunk_launches() {
         e.use_plan = true;
         e.plan = p;
         g_launches.clear();
-        CHECK(e.run() == KDA_OK && g_launches.size() == 3 && g_launches[0].seg_len == 1873 * 64 &&
-                  g_launches[0].seg0_len == 1400 * 64,
+        CHECK(e.run() == KDA_OK && g_launches.size() == 3 && g_launches[0].seg_len == 1862 * 64 &&
+                  g_launches[0].seg0_len == 1488 * 64,
               "explicit copy of the default plan");
         // the lead form's own checks
         { Call x = e; x.plan.seg0_len = 100; expect_reject(x, KDA_ERR_UNSUPPORTED, "seg0_len not a multiple of chunk"); }
