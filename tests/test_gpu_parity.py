@@ -552,6 +552,58 @@ def test_state_checkpoints(g, shape, stride, nseg):
         assert ej <= TOL[dtype], (j, ej)
 
 
+@pytest.mark.parametrize("dtype,B,T,H,dk,dv,chunk,plan_args,lens", [
+    ("bf16", 2, 100, 3, 64, 64, 64, (1, 64, 0), None),        # one pass, ragged last chunk
+    ("bf16", 2, 100, 3, 64, 64, 64, (1, 32, 0), None),        # column blocks: most waves own no value column
+    ("bf16", 1, 300, 2, 128, 128, 64, (3, 128, 0), None),     # equal segments
+    ("bf16", 1, 300, 2, 128, 128, 64, (3, 128, 64), None),    # lead form
+    ("f32", 2, 37, 2, 32, 32, 32, (1, 32, 0), None),          # float32 outputs
+    ("bf16", 1, 206, 2, 64, 64, 64, None, [5, 70, 1, 130]),   # packed sequences, each with a ragged end
+], ids=["one-pass", "column-blocks", "segments", "lead", "f32", "packed"])
+def test_output_guard_zones(g, dtype, B, T, H, dk, dv, chunk, plan_args, lens):
+    """o is written by stores whose range ends at each chunk's last token: every element of o
+    is written (o starts as NaN and ends equal to the oracle's) and nothing outside o is
+    (guard zones on both sides of it keep their bit pattern)."""
+    import torch
+    _say(f"case: guard zones {dtype} B{B} T{T} H{H} {dk}/{dv} chunk {chunk} plan {plan_args} lens {lens}")
+    r = small_recipe(dtype, B, T, H, dk, dv, chunk, s0_std=0.05)
+    x = ks.make_prefill(r)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    bits = torch.int16 if dtype == "bf16" else torch.int32
+    n, G = B * T * H * dv, 64                                   # guard: 64 elements each side
+    buf = torch.full((G + n + G,), float("nan"), dtype=dt, device="cuda")
+    ref_bits = buf.view(bits).clone()
+    o = buf[G:G + n].view(B, T, H, dv)
+    args = [dev_tensor(x[nm], dt) for nm in ("q", "k", "v")]
+    args += [dev_tensor(x["log_alpha"], torch.float32), dev_tensor(x["beta"], torch.float32)]
+    if lens is None:
+        plan = g.Plan(plan_args[0], plan_args[1])
+        plan.seg0_len = plan_args[2]
+        _, S = g.chunk_fwd(*args, dev_tensor(x["S0"], torch.float32), chunk=chunk, plan=plan, o=o)
+    else:
+        assert B == 1 and sum(lens) == T
+        S0 = np.stack([np.stack([ks.gen_state(r, i, h) for h in range(H)]) for i in range(len(lens))])
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        _, S = g.chunk_fwd(*args, dev_tensor(S0, torch.float32), chunk=chunk, o=o,
+                           cu_seqlens=torch.from_numpy(cu).cuda())
+    torch.cuda.synchronize()
+    vb = buf.view(bits)
+    assert torch.equal(vb[:G], ref_bits[:G]) and torch.equal(vb[G + n:], ref_bits[G + n:]), "a store left o"
+    on, Sn = to_np(o), to_np(S)
+    assert np.isfinite(on).all(), "an element of o was not written"
+    if lens is None:
+        o_ref, S_ref = oracle.kda_chunked(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["S0"], chunk=chunk)
+        check(on, Sn, o_ref, S_ref, TOL[dtype], "guard-zone case")
+    else:
+        cu = np.concatenate([[0], np.cumsum(lens)])
+        for i in range(len(lens)):
+            a, b = int(cu[i]), int(cu[i + 1])
+            sl = lambda t: t[:, a:b]  # noqa: E731
+            o_ref, S_ref = oracle.kda_chunked(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["log_alpha"]),
+                                              sl(x["beta"]), S0[i:i + 1], chunk=chunk)
+            check(on[:, a:b], Sn[i:i + 1], o_ref, S_ref, TOL[dtype], f"guard-zone sequence {i} ({b - a} tokens)")
+
+
 @pytest.mark.parametrize("dtype,lens,H,dk,dv,chunk", [
     ("bf16", [100, 0, 64, 257, 1], 2, 128, 128, 64),
     ("f32", [17, 48, 3], 2, 32, 64, 16),
