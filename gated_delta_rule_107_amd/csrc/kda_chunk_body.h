@@ -452,7 +452,8 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int64_t bid
         // (its store instructions issue while the gate prep below keeps the vector units busy).
         // QS and O are held transposed: lane (g, jl) holds token 16 p + jl, value columns 4g ..
         // 4g+3, written by one store; rows past the chunk's last token (and every row of a wave
-        // without value columns) fall outside the store's buffer range and are dropped.
+        // without value columns) fall outside the store's buffer range and are dropped.  The
+        // range, Tc token rows, stays below 64 * 2^24 * 4 bytes = 2^32 by the bound on H * dv.
         if constexpr (cur && want_o) {
             const unsigned rowb = (unsigned)tok_v * E;
             const __amdgpu_buffer_rsrc_t o_rs =
