@@ -40,9 +40,15 @@ static hipError_t launch_chunk_m(const ChunkArgs& a, hipStream_t st) {
 
 template <typename OpT, int DK, int C>
 static hipError_t launch_chunk_t(const ChunkArgs& a, hipStream_t st) {
-    const bool ext = a.flags != 0 || (a.mode == 0 && a.ckpt);
-    if (a.mode == 1) return ext ? launch_chunk_m<OpT, DK, C, 1, true>(a, st) : launch_chunk_m<OpT, DK, C, 1, false>(a, st);
-    return ext ? launch_chunk_m<OpT, DK, C, 0, true>(a, st) : launch_chunk_m<OpT, DK, C, 0, false>(a, st);
+    // float32 operands need chunk * dk <= 4096 (LDS); the ABI rejects larger ones before any
+    // launch, so they are not instantiated
+    if constexpr (sizeof(OpT) == 4 && C * DK > 4096) return hipErrorInvalidValue;
+    else {
+        const bool ext = a.flags != 0 || (a.mode == 0 && a.ckpt);
+        if (a.mode == 1)
+            return ext ? launch_chunk_m<OpT, DK, C, 1, true>(a, st) : launch_chunk_m<OpT, DK, C, 1, false>(a, st);
+        return ext ? launch_chunk_m<OpT, DK, C, 0, true>(a, st) : launch_chunk_m<OpT, DK, C, 0, false>(a, st);
+    }
 }
 
 template <typename OpT, int DK>

@@ -868,7 +868,17 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int64_t bid
 
     if (nchunks > 0) {
         body(BoolC<false>{}, BoolC<true>{}, -1);
-        for (int64_t n = 0; n + 1 < nchunks; ++n) body(BoolC<true>{}, BoolC<true>{}, n);
+        if constexpr (EXT) {
+            // (the loop entered only when it runs: in this instantiation the compiler otherwise
+            // spills values that skip the loop around it)
+            if (nchunks > 1) {
+                int64_t n = 0;
+                do body(BoolC<true>{}, BoolC<true>{}, n);
+                while (++n + 1 < nchunks);
+            }
+        } else {
+            for (int64_t n = 0; n + 1 < nchunks; ++n) body(BoolC<true>{}, BoolC<true>{}, n);
+        }
         body(BoolC<true>{}, BoolC<false>{}, nchunks - 1);
     }
 

@@ -46,9 +46,13 @@ static hipError_t launch_lead_e(const ChunkArgs& a0, const ChunkArgs& a1, hipStr
 
 template <typename OpT, int DK, int C>
 static hipError_t launch_lead_c(const ChunkArgs& a0, const ChunkArgs& a1, hipStream_t st) {
-    if (a0.flags != 0) return launch_lead_e<OpT, DK, C, true, true>(a0, a1, st);
-    if (a0.ckpt) return launch_lead_e<OpT, DK, C, true, false>(a0, a1, st);
-    return launch_lead_e<OpT, DK, C, false, false>(a0, a1, st);
+    // (float32: chunk * dk <= 4096, as for the chunk kernel)
+    if constexpr (sizeof(OpT) == 4 && C * DK > 4096) return hipErrorInvalidValue;
+    else {
+        if (a0.flags != 0) return launch_lead_e<OpT, DK, C, true, true>(a0, a1, st);
+        if (a0.ckpt) return launch_lead_e<OpT, DK, C, true, false>(a0, a1, st);
+        return launch_lead_e<OpT, DK, C, false, false>(a0, a1, st);
+    }
 }
 
 template <typename OpT, int DK>
