@@ -523,7 +523,8 @@ def test_workload3_long_context_full_size(g):
     (("bf16", 2, 300, 2, 64, 64, 64), 128, 1),
     (("bf16", 1, 500, 2, 128, 128, 64), 64, 3),
     (("bf16", 1, 512, 2, 128, 128, 64), 256, 2),       # the last checkpoint is the final state
-], ids=["f32-tiny", "bf16-ragged", "bf16-segments", "bf16-final"])
+    (("bf16", 1, 64, 2, 128, 128, 64), 64, 1),         # one chunk: the chunk loop never runs
+], ids=["f32-tiny", "bf16-ragged", "bf16-segments", "bf16-final", "bf16-one-chunk"])
 def test_state_checkpoints(g, shape, stride, nseg):
     """State checkpoints every `stride` tokens (prefix reuse, orkas.ai page, section "The cost
     comes back in the serving stack"): checkpoint j must equal the oracle's state after the
@@ -692,6 +693,8 @@ def test_packed_sequences_with_segments(g, dtype, lens, H, dk, dv, chunk, nseg):
     ("f32", 1, 64, 2, 16, 16, 16, 1),
     ("bf16", 2, 333, 2, 64, 64, 32, 1),
     ("bf16", 1, 500, 2, 128, 128, 64, 3),
+    ("bf16", 1, 50, 2, 128, 128, 64, 1),       # one (partial) chunk: the chunk loop never runs
+    ("bf16", 1, 100, 2, 128, 128, 64, 1),      # two chunks: the loop runs once
 ])
 def test_prefill_gate_logits(g, dtype, B, T, H, dk, dv, chunk, nseg):
     """log_alpha holding raw logits x: the kernels form -5 sigmoid(x) themselves."""
@@ -808,6 +811,7 @@ def test_decode_verify_commit_full_size(g):
 
 @pytest.mark.parametrize("dtype,B,T,H,dk,dv,chunk,nseg,gate", [
     ("f32", 1, 64, 2, 16, 16, 16, 1, 0),
+    ("bf16", 1, 64, 2, 128, 128, 64, 1, 1),     # one chunk
     ("bf16", 2, 333, 2, 64, 64, 32, 1, 1),
     ("bf16", 1, 500, 2, 128, 128, 64, 3, 0),
     ("bf16", 1, 200, 1, 32, 128, 16, 2, 1),
