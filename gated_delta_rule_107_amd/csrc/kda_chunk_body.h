@@ -25,7 +25,9 @@
 //   KhT = (k e^(Gamma_C - Gamma))^T                                (<= 1)
 // A and M tiles are (KL or QL) Diag(f) RH^T with f = e^-tot_p (<= e^80, the
 // diagonal tile), f = 1 for adjacent sub-tiles and f = e^(r_p - r_pp+1) (<= 1)
-// further below; f is applied to the left operand in registers.
+// further below.  bf16 operands fold f into right-operand variants that gate prep
+// stores (RD = RH e^-tot_p; RF = RH e^tot_{pp+1}, RH e^(tot_{pp+1} + tot_{pp+2})); float32
+// operands apply f to the left operand in registers.
 //
 // Per chunk: gate prep from registers prefetched a chunk ahead writes the operands
 // above to LDS; A / M tiles run on MFMA together with X = Kt S, QS = Qt S; the four
@@ -77,10 +79,11 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const int64_t bid
     // pitch = 4 banks mod 32, so 8 consecutive rows hit 8 distinct bank quads.  Tiles read
     // 8 B per lane (the chained operands Kt, Qt, Khat^T, the solve and M blocks): pitch = 2
     // banks mod 32, so 16 consecutive rows hit 16 distinct bank pairs.  (bf16; float32 keeps
-    // 16-byte pitches so its 16-byte chained loads stay aligned.)
+    // 16-byte pitches so its 16-byte chained loads stay aligned.)  Other pitches measured
+    // slower: Kt / Qt at DKP + 8 by 10 %, the C-wide tiles at C + 8 by 3 %.
     constexpr int LDK = DKP + PADE;
-    constexpr int LKQ = DKP + (E == 2 ? 4 : 4);
-    constexpr int LC = C + (E == 2 ? 4 : 4);
+    constexpr int LKQ = DKP + 4;
+    constexpr int LC = C + 4;
     constexpr int KNAT = (E == 2) ? (DK + 31) / 32 : DK / 4;   // natural-order steps over channels
     constexpr bool want_o = MODE == 0;
     // state column groups per wave: one in MODE 0; in MODE 1 the widened state [S | M] as two,

@@ -145,8 +145,8 @@ __host__ __device__ constexpr Lds lds_layout(int E, int DK, int C) {
     const int NT = C / 16;
     const int DKP = DK < 32 ? 32 : DK;            // bf16 natural loads read 32 channels at a time
     const int LDK = DKP + PADE;
-    const int LKQ = DKP + 16 / E / (E == 2 ? 2 : 1);
-    const int LC = C + 16 / E / (E == 2 ? 2 : 1);
+    const int LKQ = DKP + 4;                      // (the pitches the chunk kernel uses)
+    const int LC = C + 4;
     Lds L{};
     int off = 0;
     L.kt = off;   off += align16(C * LKQ * E);
