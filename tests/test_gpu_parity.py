@@ -181,8 +181,7 @@ def test_last_chunk_full_small_chunks(g, shape, nseg):
                                    # halves [S | M] differ in width
                                    ("bf16", 1, 500, 2, 128, 64, 64), ("f32", 1, 200, 2, 32, 16, 16),
                                    ("bf16", 1, 300, 3, 64, 32, 32),
-                                   # float32 operands in 64-token chunks (dk <= 64 for float32; segment
-                                   # pass 1 defers two of its tiles to the inverse phase)
+                                   # float32 operands in 64-token chunks (chunk * dk <= 4096 for float32)
                                    ("f32", 1, 257, 1, 64, 64, 64)],
                          ids=lambda s: "-".join(map(str, s)))
 @pytest.mark.parametrize("nseg", [2, 3, 8])
