@@ -186,7 +186,7 @@ void chunk_launches() {
     g_launches.clear();
     CHECK(d.run(true) == KDA_OK, "noalloc: %s", kda_last_error());
     CHECK(g_launches.size() == 3 && g_launches[0].ws == g_scratch_stub, "noalloc uses the library workspace");
-    // the 1M-token workload's default plan: 8 segments of 131,072 tokens
+    // the 1M-token workload's default plan: the lead form of 9 segments
     kda_plan_t p{};
     CHECK(kda_chunk_fwd_default_plan(1, 1 << 20, 32, 128, 128, 64, KDA_DTYPE_BF16, &p) == KDA_OK, "plan query");
     // 8 equal segments would fill the 256 CUs in pass 2 (cost 2048 x 1.8 = 3686.4 pass-2 chunks);
