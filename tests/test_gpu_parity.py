@@ -517,6 +517,117 @@ def test_workload3_long_context_full_size(g):
                    f"workload 3 head {h}")
 
 
+# ------------------------------------------------------------------ the largest head count the ABI accepts
+
+# H * max(dk, dv) < 2^24: at dk = dv = 128 the token stride is 16,777,088 elements, so a lane 63
+# tokens into a chunk addresses log_alpha at 63 * 16,777,088 * 4 B ~ 4.228e9, 1.6 % below the
+# 2^32 its per-lane byte offset can hold.
+MAX_H = ((1 << 24) - 1) // 128
+MAX_KEYED = (0, MAX_H // 2, MAX_H - 1)
+
+
+def _max_heads_inputs(r, keyed):
+    """Inputs of recipe `r` drawn on the device one whole tensor per draw (sig15 log-decay,
+    L2-normalised q and k, beta = sigmoid(N(0,1)), S0 ~ s0_std N(0,1)); the heads in `keyed` are
+    then overwritten with gen_head's / gen_state's values, which the oracle regenerates."""
+    import torch
+    dev = torch.device("cuda:0")
+    dt = torch.bfloat16 if r.dtype == "bf16" else torch.float32
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(r.tag)
+    B, T, H = r.B, r.T, r.H
+    x = {}
+    for name, d in (("q", r.dk), ("k", r.dk), ("v", r.dv)):
+        t = torch.randn((B, T, H, d), generator=gen, device=dev, dtype=torch.float32)
+        if name != "v":
+            t.div_(torch.linalg.vector_norm(t, dim=-1, keepdim=True))
+        x[name] = t.to(dt)
+        del t
+    x["log_alpha"] = torch.randn((B, T, H, r.dk), generator=gen, device=dev,
+                                 dtype=torch.float32).mul_(1.5).sigmoid_().mul_(-5.0)
+    x["beta"] = torch.randn((B, T, H), generator=gen, device=dev, dtype=torch.float32).sigmoid_()
+    x["S0"] = torch.randn((B, H, r.dk, r.dv), generator=gen, device=dev, dtype=torch.float32).mul_(r.s0_std)
+    for h in keyed:
+        for name in ("q", "k", "v", "log_alpha", "beta"):
+            x[name][0, :, h] = torch.from_numpy(ks.gen_head(r, name, 0, h)).to(dev, x[name].dtype)
+        x["S0"][0, h] = torch.from_numpy(ks.gen_state(r, 0, h)).to(dev)
+    torch.cuda.synchronize()
+    return x
+
+
+def _keyed_head(r, h):
+    """Keyed inputs of head h as [1, T, 1, .] arrays (beta [1, T, 1]) and its S0 [1, 1, dk, dv]."""
+    xs = {nm: ks.gen_head(r, nm, 0, h)[None, :, None] for nm in ("q", "k", "v", "log_alpha", "beta")}
+    return xs, ks.gen_state(r, 0, h)[None, None]
+
+
+@pytest.mark.parametrize("dtype,chunk,nseg", [("bf16", 64, 1), ("bf16", 64, 2), ("f32", 32, 1)],
+                         ids=["bf16-one-pass", "bf16-segments", "f32-chunk32"])
+def test_prefill_max_heads(g, dtype, chunk, nseg):
+    """B=1, T=127 (a full chunk and a ragged one), H = 131,071 heads of dk = dv = 128, with a
+    start state: the largest token stride the ABI accepts.  The first, a middle and the last
+    head (whose addresses are the largest) are checked against the oracle element by element;
+    every other head must stay finite."""
+    import torch
+    r = small_recipe(dtype, 1, 127, MAX_H, 128, 128, chunk, s0_std=0.05)
+    _say(f"case: prefill at H={MAX_H} ({dtype}, chunk {chunk}, {nseg} segment(s)); generating inputs")
+    x = _max_heads_inputs(r, MAX_KEYED)
+    _say("running the GPU path")
+    o, S = g.chunk_fwd(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["S0"], chunk=chunk,
+                       plan=g.Plan(nseg, 128))
+    torch.cuda.synchronize()
+    del x
+    assert bool(torch.isfinite(S.amax(dim=(2, 3))).all()) and bool(torch.isfinite(o.float().amax(dim=(0, 1, 3))).all())
+    for h in MAX_KEYED:
+        xs, S0 = _keyed_head(r, h)
+        o_ref, S_ref = oracle.kda_loop(xs["q"], xs["k"], xs["v"], xs["log_alpha"], xs["beta"], S0)
+        check_full(to_np(o[:, :, h:h + 1]), to_np(S[:, h:h + 1]), o_ref, S_ref, TOL[dtype], CHUNK_TOL[dtype],
+                   f"H={MAX_H} head {h}", chunk=chunk)
+    del o, S
+    torch.cuda.empty_cache()
+
+
+def test_decode_family_max_heads(g):
+    """Decode step, verify of 4 drafts and commit at H = 131,071 heads of dk = dv = 128 (N = 1):
+    the first, a middle and the last head against the oracle."""
+    import torch
+    r = small_recipe("bf16", 1, 4, MAX_H, 128, 128, 16, s0_std=0.05)
+    _say(f"case: decode family at H={MAX_H}; generating inputs")
+    x = _max_heads_inputs(r, MAX_KEYED)
+    state = x["S0"]
+    keep = state.clone()
+    o_ver = g.decode_verify(state, x["q"], x["k"], x["v"], x["log_alpha"], x["beta"])
+    torch.cuda.synchronize()
+    assert torch.equal(state, keep), "verify wrote the state"
+    del keep
+    # token slices are cloned: a view of a size-1 batch axis counts as contiguous, and its base
+    # (H * 4 bytes into beta) would miss the 16-byte alignment the library requires
+    first = {nm: x[nm][:, 0].clone() for nm in ("q", "k", "v", "log_alpha", "beta")}
+    rest = {nm: x[nm][:, 1:].clone() for nm in ("q", "k", "v", "log_alpha", "beta")}
+    o_step = g.decode_step(state, first["q"], first["k"], first["v"], first["log_alpha"], first["beta"])
+    torch.cuda.synchronize()
+    S_step = {h: to_np(state[:, h:h + 1]) for h in MAX_KEYED}
+    # commit the remaining 3 drafts from the stepped state
+    n_acc = torch.full((1,), 3, dtype=torch.int32, device="cuda")
+    g.decode_commit(state, rest["q"], rest["k"], rest["v"], rest["log_alpha"], rest["beta"], n_acc)
+    torch.cuda.synchronize()
+    for h in MAX_KEYED:
+        xs, S0 = _keyed_head(r, h)
+        o_ref = oracle.kda_decode_verify(S0, xs["q"], xs["k"], xs["v"], xs["log_alpha"], xs["beta"])
+        eo = oracle.rel_fro(to_np(o_ver[:, :, h:h + 1]), o_ref)
+        os_ref, S1_ref = oracle.kda_decode_step(S0, xs["q"][:, 0], xs["k"][:, 0], xs["v"][:, 0],
+                                                xs["log_alpha"][:, 0], xs["beta"][:, 0])
+        es = oracle.rel_fro(to_np(o_step[:, h:h + 1]), os_ref)
+        e1 = oracle.rel_fro(S_step[h], S1_ref)
+        S4_ref = oracle.kda_decode_commit(S1_ref, xs["q"][:, 1:], xs["k"][:, 1:], xs["v"][:, 1:],
+                                          xs["log_alpha"][:, 1:], xs["beta"][:, 1:], np.array([3]))
+        e4 = oracle.rel_fro(to_np(state[:, h:h + 1]), S4_ref)
+        _say(f"H={MAX_H} head {h}: verify o {eo:.3e}, step o {es:.3e} S {e1:.3e}, commit S {e4:.3e}")
+        assert max(eo, es, e1, e4) <= TOL["bf16"], (h, eo, es, e1, e4)
+    del x, first, rest, state, o_ver, o_step
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("shape,stride,nseg", [
     (("f32", 1, 64, 2, 16, 16, 16), 32, 1),
     (("bf16", 2, 300, 2, 64, 64, 64), 128, 1),
