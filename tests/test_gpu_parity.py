@@ -347,6 +347,66 @@ def test_deterministic(g):
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
+@pytest.mark.parametrize("mode", ["one-pass", "segments", "packed", "packed-segments"])
+def test_nonfinite_inputs_stay_in_their_unit(g, mode):
+    """Input values are not checked, so a NaN or an Inf propagates; but only inside the
+    (sequence, head) it belongs to, and only forward: every other (sequence, head), and the
+    chunks of the poisoned one before the chunk holding it, are bit-identical to the same call
+    on clean inputs (units share no data; a chunk reads only earlier chunks' state)."""
+    import torch
+    H, dk, dv, chunk = 3, 64, 64, 64
+    packed = mode.startswith("packed")
+    nseg = 2 if mode.endswith("segments") else 1
+    if packed:
+        lens = [150, 90, 330]
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        B, T = 1, int(cu[-1])
+        # (tensor, batch row, token, head, channel, value): sequence 1 at its token 70 (its
+        # chunk 1), sequence 2 at its token 200 (its chunk 3)
+        spots = [("k", 0, 150 + 70, 1, 5, np.nan), ("v", 0, 240 + 200, 0, 7, np.inf)]
+        units = [(i, h) for i in range(len(lens)) for h in range(H)]
+        bad = {(1, 1): (150, 1), (2, 0): (240, 3)}          # unit -> (first token, poisoned chunk)
+        cu_d = torch.from_numpy(cu).cuda()
+    else:
+        B, T = 2, 300
+        spots = [("k", 0, 130, 1, 5, np.nan), ("v", 1, 70, 2, 7, np.inf)]
+        units = [(b, h) for b in range(B) for h in range(H)]
+        bad = {(0, 1): (0, 2), (1, 2): (0, 1)}
+        cu_d = None
+    r = small_recipe("bf16", B, T, H, dk, dv, chunk)
+    _say(f"case: non-finite inputs, {mode}")
+    x = ks.make_prefill(r)
+    NS = len(lens) if packed else B
+    S0 = np.stack([np.stack([ks.gen_state(r.with_shape(s0_std=0.05), i, h) for h in range(H)]) for i in range(NS)])
+    y = {n: x[n].copy() for n in ("q", "k", "v", "log_alpha", "beta")}
+    for name, b, t, h, c, val in spots:
+        y[name][b, t, h, c] = val
+
+    def run(inp):
+        args = [dev_tensor(inp[n], torch.bfloat16) for n in ("q", "k", "v")]
+        args += [dev_tensor(inp["log_alpha"], torch.float32), dev_tensor(inp["beta"], torch.float32),
+                 dev_tensor(S0, torch.float32)]
+        o, S = g.chunk_fwd(*args, chunk=chunk, plan=g.Plan(nseg, 0), cu_seqlens=cu_d)
+        torch.cuda.synchronize()
+        return o.float().cpu().numpy(), S.cpu().numpy()
+
+    o0, S0_out = run(x)
+    o1, S1_out = run(y)
+    assert np.isfinite(o0).all() and np.isfinite(S0_out).all()
+    for (i, h) in units:
+        lo, hi = (int(cu[i]), int(cu[i + 1])) if packed else (0, T)
+        b = 0 if packed else i
+        if (i, h) not in bad:
+            assert np.array_equal(o1[b, lo:hi, h], o0[b, lo:hi, h]), (mode, i, h)
+            assert np.array_equal(S1_out[i, h], S0_out[i, h]), (mode, i, h)
+            continue
+        first, n_bad = bad[(i, h)]
+        clean_end = first + n_bad * chunk
+        assert np.array_equal(o1[b, lo:clean_end, h], o0[b, lo:clean_end, h]), (mode, i, h, "earlier chunks")
+        assert not np.isfinite(S1_out[i, h]).all(), (mode, i, h, "the poison did not reach the state")
+    _say(f"{mode}: {len(units) - len(bad)} clean units bit-identical, poisoned units clean before their chunk")
+
+
 # ------------------------------------------------------------------ decode
 
 @pytest.mark.parametrize("dtype,dk,dv", [("f32", 16, 16), ("f32", 32, 128), ("bf16", 128, 128),
@@ -496,7 +556,7 @@ def test_workload3_long_context_full_size(g):
     default plan (segments, prefix scan, segment pass 2), as the benchmark runs it.  Heads 0
     and 21 hold keyed inputs and every one of their outputs and final states is checked
     against the oracle over the whole sequence; the other 30 heads are drawn on the device
-    with the same recipe and must stay finite."""
+    with the same recipe and must stay finite.  A second run must be bit-identical."""
     import torch
     r = ks.WORKLOADS[3]
     heads = (0, 21)
@@ -508,7 +568,11 @@ def test_workload3_long_context_full_size(g):
     _say(f"running the GPU path ({p})")
     o, S = g.chunk_fwd(xd["q"], xd["k"], xd["v"], xd["log_alpha"], xd["beta"], None, chunk=r.chunk)
     torch.cuda.synchronize()
-    del xd
+    # bitwise run-to-run determinism of the whole plan (lead launch, scan, pass 2) at full size
+    o2, S2 = g.chunk_fwd(xd["q"], xd["k"], xd["v"], xd["log_alpha"], xd["beta"], None, chunk=r.chunk)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(S, S2), "two runs of the same call differ"
+    del xd, o2, S2
     assert bool(torch.isfinite(S).all()) and bool(torch.isfinite(o.float().abs().amax(dim=(0, 1, 3))).all())
     for h in heads:
         _say(f"oracle over 1,048,576 tokens of head {h}")
