@@ -347,6 +347,72 @@ def test_deterministic(g):
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
+def test_concurrent_threads_and_streams(g):
+    """Calls are reentrant: three host threads, each on a stream of its own, run a one-pass
+    prefill, a segmented prefill and a run of decode steps at the same time (five rounds each,
+    into buffers of their own); every result is bit-identical to the same calls run one after
+    another on the default stream."""
+    import threading
+    import torch
+    ra = small_recipe("bf16", 2, 300, 3, 128, 128, 64, s0_std=0.05)
+    rb = small_recipe("bf16", 1, 1000, 2, 64, 64, 32, tag=ks.TAG_BASE + 101, s0_std=0.05)
+    xa, xb = ks.make_prefill(ra), ks.make_prefill(rb)
+    rd = ks.Recipe("dec", B=6, T=1, H=4, dk=128, dv=64, chunk=16, dtype="bf16", loga="unif", s0_std=0.05,
+                   tag=ks.TAG_BASE + 102, steps=8)
+    d = ks.make_decode(rd)
+
+    def dev_inputs(x):
+        t = {n: dev_tensor(x[n], torch.bfloat16) for n in ("q", "k", "v")}
+        t.update({n: dev_tensor(x[n], torch.float32) for n in ("log_alpha", "beta", "S0")})
+        return t
+
+    da, db = dev_inputs(xa), dev_inputs(xb)
+    dd = {n: [dev_tensor(d[n][s], torch.bfloat16 if n in ("q", "k", "v") else torch.float32) for s in range(rd.steps)]
+          for n in ("q", "k", "v", "log_alpha", "beta")}
+
+    def job_a():
+        return g.chunk_fwd(da["q"], da["k"], da["v"], da["log_alpha"], da["beta"], da["S0"], chunk=64,
+                           plan=g.Plan(1, 128))
+
+    def job_b():
+        return g.chunk_fwd(db["q"], db["k"], db["v"], db["log_alpha"], db["beta"], db["S0"], chunk=32,
+                           plan=g.Plan(4, 0))
+
+    def job_d():
+        state = dev_tensor(d["state"], torch.float32)
+        outs = [g.decode_step(state, *(dd[n][s] for n in ("q", "k", "v", "log_alpha", "beta")))
+                for s in range(rd.steps)]
+        return torch.stack(outs), state
+
+    jobs = {"a": job_a, "b": job_b, "d": job_d}
+    ref = {k: job() for k, job in jobs.items()}
+    torch.cuda.synchronize()
+    got, errors = {k: [] for k in jobs}, []
+
+    def worker(name):
+        try:
+            s = torch.cuda.Stream()                       # default priority
+            with torch.cuda.stream(s):
+                for _ in range(5):
+                    got[name].append(jobs[name]())
+            s.synchronize()
+        except Exception as e:                            # reported below, in the main thread
+            errors.append((name, repr(e)))
+
+    threads = [threading.Thread(target=worker, args=(k,)) for k in jobs]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for k in jobs:
+        assert len(got[k]) == 5, (k, len(got[k]))
+        for o, S in got[k]:
+            assert torch.equal(o, ref[k][0]) and torch.equal(S, ref[k][1]), k
+    _say("3 threads x 5 rounds on separate streams: bit-identical to the serial runs")
+
+
 @pytest.mark.parametrize("mode", ["one-pass", "segments", "packed", "packed-segments"])
 def test_nonfinite_inputs_stay_in_their_unit(g, mode):
     """Input values are not checked, so a NaN or an Inf propagates; but only inside the
