@@ -19,7 +19,9 @@ The same JSON line carries side figures, each timed the same way:
   * the headline step with state checkpoints every 512 tokens, with raw gate
     logits (KDA_GATE_LOGITS) and with q / k normalised in the kernels;
   * decode: 256 sequences x 32 heads, 128x128 float32 state, 64 consecutive
-    in-place steps, plus the speculative verify of 4 drafts and their commit.
+    in-place steps, plus the speculative verify of 4 drafts and their commit,
+    and the 64 steps of its first 1, 8 and 64 sequences as eager calls and as one
+    replay of a HIP graph that captured them (small batches are launch-bound).
 Rooflines: `roofline` is the dominant launch of the headline step (its
 algorithmic bytes over its mean duration, from HIP events the library records
 around each launch on the stream the kernels run on) with the whole step's
@@ -432,6 +434,58 @@ def bench_decode(g, torch, rd, d, reps):
     return ms, nsteps
 
 
+def bench_decode_graph(g, torch, rd, d, sizes=(1, 8, 64), reps=10):
+    """Small batches: the decode workload's 64 steps for its first N sequences (all heads),
+    as eager binding calls and as one replay of the same steps captured in a HIP graph;
+    median microseconds per step of each (the state restored, untimed, between repetitions)."""
+    dev = torch.device("cuda:0")
+    dt = torch.bfloat16
+    out = []
+    for N in sizes:
+        T_ = lambda a, t: torch.from_numpy(np.ascontiguousarray(a[:, :N])).to(dev, t)  # noqa: E731
+        pristine = torch.from_numpy(np.ascontiguousarray(d["state"][:N])).to(dev)
+        state = pristine.clone()
+        qs, ks_, vs = T_(d["q"], dt), T_(d["k"], dt), T_(d["v"], dt)
+        las, bs = T_(d["log_alpha"], torch.float32), T_(d["beta"], torch.float32)
+        nsteps = qs.shape[0]
+        o = torch.empty((nsteps, N, rd.H, rd.dv), dtype=dt, device=dev)
+
+        def run():
+            for s in range(nsteps):
+                g.decode_step(state, qs[s], ks_[s], vs[s], las[s], bs[s], o=o[s])
+
+        def timed(fn):
+            fn()                                            # warm-up
+            times = []
+            for _ in range(reps):
+                state.copy_(pristine)                       # restore (not timed)
+                torch.cuda.synchronize()
+                t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                t0.record()
+                fn()
+                t1.record()
+                torch.cuda.synchronize()
+                times.append(t0.elapsed_time(t1) * 1e3 / nsteps)
+            return float(np.median(times))
+
+        eager_us = timed(run)
+        side = torch.cuda.Stream()                          # default priority
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            run()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            run()
+        graph_us = timed(graph.replay)
+        nb = decode_bytes_per_step(N, rd.H, rd.dk, rd.dv, 2)
+        out.append({"sequences": N, "heads": rd.H, "eager_us_per_step": round(eager_us, 2),
+                    "graph_us_per_step": round(graph_us, 2), "graph_GBps": round(nb / (graph_us * 1e-6) / 1e9, 1)})
+        del graph
+    return {"steps": int(d["q"].shape[0]), "by_batch": out}
+
+
 # ----------------------------------------------------------------------------- measured HBM traffic
 
 PROFILES = os.path.join(ROOT, "profiles")
@@ -607,7 +661,8 @@ def main():
                             "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(dgbps / PEAK_HBM_GBPS, 4),
                             "traffic": measured_traffic(rd.name, "decode_kernel"), "launch_bytes": dbytes},
                "cpu_baseline": cpu_dec,
-               "speculative": bench_speculative(g, torch, rd, d, SPEC_DRAFTS, 2 * args.decode_reps)}
+               "speculative": bench_speculative(g, torch, rd, d, SPEC_DRAFTS, 2 * args.decode_reps),
+               "small_batch_hip_graph": bench_decode_graph(g, torch, rd, d)}
         log("decode:", json.dumps(dec))
     copy_gbps = copy_bandwidth(torch)
 
