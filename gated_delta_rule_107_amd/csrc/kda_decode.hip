@@ -44,9 +44,11 @@ template <int DK, int DV, int MAXT = 1024> struct DecodeMap {
 // (n n_tok + j) H + h of q, k, v, the gates, beta and o.
 // NORM: q and k are L2-normalised per token inside the kernel.  It is a compile-time
 // choice because its reductions, even untaken, push the plain step past the 64 VGPRs
-// that 8 waves per SIMD allow and make it spill.
+// that 8 waves per SIMD allow and make it spill; the normalising instantiations run at
+// 4 waves per SIMD instead (up to 128 VGPRs, 76-85 used at 128 x 128), where they do not
+// spill (at 8 they spilled up to 72 bytes per thread and were 1-2 % slower).
 template <typename ET, int DK, int DV, int MODE, bool NORM>
-__global__ __launch_bounds__((DecodeMap<DK, DV>::NTB)) __attribute__((amdgpu_waves_per_eu(8))) void decode_kernel(
+__global__ __launch_bounds__((DecodeMap<DK, DV>::NTB)) __attribute__((amdgpu_waves_per_eu(NORM ? 4 : 8))) void decode_kernel(
     float* __restrict__ state, const ET* __restrict__ q, const ET* __restrict__ k,
     const ET* __restrict__ v, const float* __restrict__ log_alpha,
     const float* __restrict__ beta, ET* __restrict__ o, const int* __restrict__ n_accept,
