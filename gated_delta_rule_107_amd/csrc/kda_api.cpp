@@ -106,12 +106,13 @@ kda_status_t resolve_plan(int64_t B, int64_t T, int32_t H, int32_t dk, int32_t d
         // Packed sequences: n_segments is the number of segments the packed row is cut into;
         // every sequence is split into segments of that length (whole chunks, at least two), so
         // only the sequences longer than it are split.  Default: one pass when the (sequence,
-        // head, column block) units cover the compute units, else enough segments to cover them.
+        // head, column block) units cover the compute units, else as many segments as one round
+        // of workgroups holds (as below).
         const int64_t ns = p.n_seqs;
         if (ns < 1) return fail(KDA_ERR_SHAPE, "n_seqs must be >= 1 (got %lld)", (long long)ns);
         out->n_seqs = (int32_t)ns;
         const int64_t per_slot = (int64_t)H * (dv / dvb);
-        if (nseg == 0) nseg = ns * per_slot < kPlanCUs ? (kPlanCUs + per_slot - 1) / per_slot : 1;
+        if (nseg == 0) nseg = ns * per_slot < kPlanCUs ? kPlanCUs / per_slot : 1;
         int64_t seg_chunks = nchunks == 0 ? 1 : (nchunks + nseg - 1) / nseg;
         if (seg_chunks < 2) seg_chunks = 2;
         if (nseg > 1 && seg_chunks < nchunks) {
@@ -144,13 +145,15 @@ kda_status_t resolve_plan(int64_t B, int64_t T, int32_t H, int32_t dk, int32_t d
     }
     const bool dflt = nseg == 0;
     if (nseg == 0) {
-        // enough workgroups to cover every compute unit; segments only when (b, h, column
-        // block) units alone cannot, and only if each segment keeps at least 2 chunks
+        // as many segments as fit the compute units in one round of workgroups (one workgroup
+        // of the 128 x 128 chunk kernel fills a CU's LDS, so a launch of more than kPlanCUs
+        // workgroups runs the excess in a second round); segments only when (b, h, column
+        // block) units alone leave CUs idle, and only if each segment keeps at least 2 chunks
         const int64_t units = B * H * (dv / dvb);
         const int64_t cus = kPlanCUs;
         nseg = 1;
         if (units < cus) {
-            nseg = (cus + units - 1) / units;
+            nseg = cus / units;
             if (nseg > nchunks / 2) nseg = nchunks / 2;
             if (nseg < 1) nseg = 1;
         }

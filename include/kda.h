@@ -125,7 +125,8 @@ typedef enum {
  *   ceil(T / n_segments) tokens (rounded up to whole chunks, at least two
  *   chunks), so only sequences longer than that are split, each with its own
  *   prefix scan; 0 = one pass when the (sequence, head, column block) units
- *   cover MI355X's 256 compute units, else enough segments to cover them
+ *   cover MI355X's 256 compute units, else floor(256 / (H x column blocks))
+ *   segments, one round of workgroups
  *   (needs T < 2^31; the segment tables are built on the device from
  *   cu_seqlens inside the workspace).
  * flags: kda_input_flag_t bits (0 = log-decays, q and k used as given).
@@ -154,8 +155,11 @@ typedef struct {
 } kda_plan_t;
 
 /* Fills *plan with the library's default for this problem: one pass when the
- * (batch, head) units alone cover MI355X's 256 compute units, otherwise enough
- * segments to cover them (at least two chunks per segment).  The default takes
+ * (batch, head) units alone leave fewer than half of MI355X's 256 compute units
+ * idle (units > 128), otherwise floor(256 / units) segments (at least two chunks
+ * per segment), so that each launch fits one round of workgroups (a chunk
+ * workgroup of dk = 128 fills a CU's LDS, and a launch of more workgroups than
+ * CUs runs the excess in a second round).  The default takes
  * the lead form (seg0_len) when, counting a pass-1 chunk as 0.8 of a pass-2
  * chunk's time (as measured on MI355X), it is at least 2 % shorter than the
  * equal segments: one more segment, segment 0 sized so that the launch running

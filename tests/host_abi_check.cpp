@@ -347,7 +347,51 @@ void offsets() {
 }
 }  // namespace
 
+// "plans" mode: one problem per stdin line, "B T H dk dv chunk dtype".  For each, the launches
+// kda_chunk_fwd makes under the default plan, then under an explicit copy of the plan that
+// kda_chunk_fwd_default_plan returns, one output line per problem:
+//   status workspace n_segments dv_block seg0_len | launches of the default | launches of the copy
+// with a launch written what:mode:seg_lo:seg_cnt:seg_cnt1:n_seg:seg_len:seg0_len:dv_block:B
+// (scan: seg_lo is the first segment it starts from).
+void print_launches() {
+    for (const Launch& L : g_launches)
+        std::printf(" %s:%d:%d:%d:%d:%d:%lld:%lld:%d:%lld", L.what.c_str(), L.mode, L.seg_lo, L.seg_cnt, L.seg_cnt1,
+                    L.n_seg, (long long)L.seg_len, (long long)L.seg0_len, L.dv_block, (long long)L.B);
+}
+
+int plans() {
+    char line[256];
+    while (std::fgets(line, sizeof line, stdin)) {
+        long long B = 0, T = 0;
+        int H = 0, dk = 0, dv = 0, chunk = 0, dt = 0;
+        if (std::sscanf(line, "%lld %lld %d %d %d %d %d", &B, &T, &H, &dk, &dv, &chunk, &dt) != 7) continue;
+        Call c;
+        c.B = B; c.T = T; c.H = H; c.dk = dk; c.dv = dv; c.chunk = chunk; c.dt = (kda_dtype_t)dt;
+        c.use_plan = false;
+        size_t need = 0;
+        kda_plan_t p{};
+        kda_status_t s = kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk, c.dt, nullptr, &need);
+        if (s == KDA_OK) s = kda_chunk_fwd_default_plan(B, T, H, dk, dv, chunk, c.dt, &p);
+        c.ws = need ? A(8) : nullptr;
+        c.wsb = need;
+        g_launches.clear();
+        if (s == KDA_OK) s = c.run();
+        std::printf("%d %zu %d %d %lld |", (int)s, need, p.n_segments, p.dv_block, (long long)p.seg0_len);
+        print_launches();
+        Call e = c;
+        e.use_plan = true;
+        e.plan = p;
+        g_launches.clear();
+        if (s == KDA_OK) s = e.run();
+        std::printf(" |");
+        print_launches();
+        std::printf(" %d\n", (int)s);
+    }
+    return 0;
+}
+
 int main(int argc, char** argv) {
+    if (argc > 1 && std::strcmp(argv[1], "plans") == 0) return plans();
     if (argc > 1 && std::strcmp(argv[1], "trace") == 0) {
         // one segmented call; the test reads the KDA_TRACE line from stderr
         Call d;

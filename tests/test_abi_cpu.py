@@ -86,6 +86,90 @@ def test_trace_prints_the_resolved_plan(host_check):
     assert "kda_chunk_fwd" not in quiet.stderr
 
 
+def _plan_shapes(n, seed=20261203):
+    """Seeded random problems over the supported set (B, H up to 9 x 300, T log-uniform up to 2^20,
+    the ABI's size bounds kept), plus edge cases around the segment and compute-unit thresholds."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    out = [(1, T, H, 128, 128, 64, BF16) for T in (0, 1, 63, 64, 65, 192, 255, 256, 257, 4096)
+           for H in (1, 16, 32, 48, 64, 100, 128, 129, 255, 256, 257)]
+    out += [(2, 81920, 2, 64, 64, 64, BF16), (2, 78720, 2, 64, 64, 64, BF16), (1, 1 << 20, 32, 128, 128, 64, BF16)]
+    while len(out) < n:
+        dt = int(rng.integers(0, 2))
+        dk, dv = (int(x) for x in rng.choice([16, 32, 64, 128], 2))
+        chunk = int(rng.choice([16, 32, 64]))
+        if dt == F32 and chunk * dk > 4096:
+            continue
+        B, H = int(rng.integers(1, 10)), int(rng.integers(1, 301))
+        T = int(np.exp(rng.uniform(0, np.log(1 << 20)))) if rng.random() < 0.95 else 0
+        if B * T > 1 << 22:
+            continue
+        out.append((B, T, H, dk, dv, chunk, dt))
+    return out
+
+
+def test_default_plans_are_well_formed(host_check):
+    """For ~3,000 problems, the default plan as kda_chunk_fwd executes it (recorded by the host
+    build's stub launchers): the segments tile [0, T) in whole chunks of at least two, the launch
+    sequence matches the plan's form, no launch has more workgroups than the 256 compute units hold
+    in one round (unless the units alone exceed them), segments are used exactly when at most half
+    of the compute units would otherwise be busy and the sequence has four chunks, the workspace
+    matches, and passing the returned plan back explicitly executes identically."""
+    shapes = _plan_shapes(3000)
+    stdin = "".join(" ".join(map(str, s)) + "\n" for s in shapes)
+    e = dict(os.environ)
+    e.pop("KDA_TRACE", None)
+    r = subprocess.run([host_check, "plans"], input=stdin, capture_output=True, text=True, env=e, timeout=300)
+    assert r.returncode == 0, r.stderr[-4000:]
+    lines = r.stdout.splitlines()
+    assert len(lines) == len(shapes)
+    bad = []
+    for (B, T, H, dk, dv, chunk, dt), line in zip(shapes, lines):
+        head, dflt, copy = line.split(" |")
+        status, need, nseg, dvb, seg0 = (int(x) for x in head.split())
+        copy_launches, status2 = copy.split()[:-1], int(copy.split()[-1])
+        L = [x.split(":") for x in dflt.split()]
+        what = [x[0] for x in L]
+        f = [[int(v) for v in x[1:]] for x in L]          # mode seg_lo seg_cnt seg_cnt1 n_seg seg_len seg0_len dvb B
+        units, nch = B * H, -(-T // chunk)
+        why = []
+        if status or status2:
+            why.append(f"status {status} / {status2}")
+        elif dflt.split() != copy_launches:
+            why.append("explicit copy differs")
+        elif dvb != dv:
+            why.append(f"dv_block {dvb}")
+        elif (nseg > 1) != (units <= 128 and nch >= 4):
+            why.append(f"{nseg} segments for {units} units, {nch} chunks")
+        elif nseg == 1:
+            if what != ["chunk"] or f[0][:3] != [0, 0, 1] or need or seg0:
+                why.append("one-pass launch")
+        else:
+            seg_len = f[0][5]
+            if need != B * H * nseg * (2 * dk * dv + dk * dk) * 4:
+                why.append(f"workspace {need}")
+            if seg_len % chunk or seg0 % chunk or seg_len < 2 * chunk:
+                why.append(f"segment lengths {seg0} / {seg_len}")
+            if seg0 == 0:
+                if not (nseg - 1) * seg_len < T <= nseg * seg_len:
+                    why.append(f"{nseg} x {seg_len} does not tile T")
+                if what != ["pass1", "scan", "chunk"] or f[0][:3] != [1, 0, nseg - 1] or f[1][1] != 0 \
+                        or f[2][:3] != [0, 0, nseg]:
+                    why.append("segmented launches")
+            else:
+                if not (0 < seg0 < T and seg0 + (nseg - 2) * seg_len < T <= seg0 + (nseg - 1) * seg_len):
+                    why.append(f"lead form {seg0} + {nseg - 1} x {seg_len} does not tile T")
+                if what != ["lead", "scan", "chunk"] or f[0][3] != nseg - 2 or f[1][1] != 1 or f[2][1:3] != [1, nseg - 1]:
+                    why.append("lead-form launches")
+            wgs = {"pass1": lambda x: x[2], "chunk": lambda x: x[2], "lead": lambda x: 1 + x[3]}
+            most = max(units * wgs[w](x) for w, x in zip(what, f) if w in wgs)
+            if most > 256:
+                why.append(f"a launch of {most} workgroups")
+        if why:
+            bad.append(((B, T, H, dk, dv, chunk, dt), why, line[:200]))
+    assert not bad, bad[:10]
+
+
 def test_exports_every_declared_function(lib):
     names = declared_functions()
     assert {"kda_chunk_fwd", "kda_decode_step", "kda_decode_verify", "kda_decode_commit", "kda_status_str",

@@ -667,6 +667,27 @@ def test_lead_default_plan_two_batch_rows(g):
     check_full(o, S, o_ref, S_ref, TOL["bf16"], CHUNK_TOL["bf16"], f"default lead plan ({p})")
 
 
+@pytest.mark.parametrize("B,T,H", [(1, 3000, 48), (3, 2000, 7)])
+def test_default_plan_head_counts_that_do_not_divide_the_cus(g, B, T, H):
+    """Head counts whose units do not divide the 256 compute units: the default plan takes
+    floor(256 / units) segments (one round of workgroups per launch); sampled (batch, head)
+    pairs against the oracle, chunk by chunk."""
+    r = small_recipe("bf16", B, T, H, 64, 64, 64, s0_std=0.05)
+    p = g.default_plan(r.B, r.T, r.H, r.dk, r.dv, r.chunk)
+    _say(f"case: default plan B{B} T{T} H{H} ({p})")
+    assert p.n_segments > 1 and B * H * (p.n_segments - (1 if p.seg0_len else 0)) <= 256
+    heads = sorted({0, H // 2, H - 1})
+    x = ks.make_prefill(r, heads=heads)
+    o, S = run_prefill(g, x, "bf16", 64)
+    for b in range(B):
+        for h in heads:
+            sl = lambda a: a[b:b + 1, :, h:h + 1]  # noqa: E731
+            o_ref, S_ref = oracle.kda_chunked(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["log_alpha"]),
+                                              x["beta"][b:b + 1, :, h:h + 1], x["S0"][b:b + 1, h:h + 1], chunk=64)
+            check_full(sl(o), S[b:b + 1, h:h + 1], o_ref, S_ref, TOL["bf16"], CHUNK_TOL["bf16"],
+                       f"B{B} T{T} H{H} b={b} h={h} ({p})")
+
+
 def _oracle_head(r, h):
     """The oracle over the whole sequence of one keyed head (float64, chunked form)."""
     xs = {n: ks.gen_head(r, n, 0, h)[None, :, None] for n in ("q", "k", "v", "log_alpha", "beta")}
