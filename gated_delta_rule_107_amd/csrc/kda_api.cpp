@@ -80,6 +80,11 @@ struct Resolved {
 // 0 beside pass 1, then pass 2).  The default takes the lead form when that is at least
 // kLeadGain cheaper, with l the better of the two whole numbers around chunks / (S + r).
 constexpr double kLeadRatio = 0.8;
+// Sequences shorter than this many chunks run in one pass: the two extra launches of a
+// segmented plan (pass 1 and the scan) cost more than they save below it (MI355X, dk = dv = 128,
+// chunk 64, one sequence x 8 or 32 heads: 4 chunks 33-34 us in one pass against 42-46 us in 2
+// segments; 8 chunks 59-60 us against 46-51 us in 4 segments).
+constexpr int64_t kMinChunksToSplit = 8;
 constexpr double kLeadGain = 0.98;
 
 constexpr int64_t kMaxSlots = 1 << 22;   // segment-table entries of one packed call
@@ -148,11 +153,12 @@ kda_status_t resolve_plan(int64_t B, int64_t T, int32_t H, int32_t dk, int32_t d
         // as many segments as fit the compute units in one round of workgroups (one workgroup
         // of the 128 x 128 chunk kernel fills a CU's LDS, so a launch of more than kPlanCUs
         // workgroups runs the excess in a second round); segments only when (b, h, column
-        // block) units alone leave CUs idle, and only if each segment keeps at least 2 chunks
+        // block) units alone leave CUs idle, only for sequences of kMinChunksToSplit chunks or
+        // more, and only if each segment keeps at least 2 chunks
         const int64_t units = B * H * (dv / dvb);
         const int64_t cus = kPlanCUs;
         nseg = 1;
-        if (units < cus) {
+        if (units < cus && nchunks >= kMinChunksToSplit) {
             nseg = cus / units;
             if (nseg > nchunks / 2) nseg = nchunks / 2;
             if (nseg < 1) nseg = 1;

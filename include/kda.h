@@ -156,8 +156,9 @@ typedef struct {
 
 /* Fills *plan with the library's default for this problem: one pass when the
  * (batch, head) units alone leave fewer than half of MI355X's 256 compute units
- * idle (units > 128), otherwise floor(256 / units) segments (at least two chunks
- * per segment), so that each launch fits one round of workgroups (a chunk
+ * idle (units > 128) or the sequence is shorter than 8 chunks, otherwise
+ * floor(256 / units) segments (at least two chunks per segment), so that each
+ * launch fits one round of workgroups (a chunk
  * workgroup of dk = 128 fills a CU's LDS, and a launch of more workgroups than
  * CUs runs the excess in a second round).  The default takes
  * the lead form (seg0_len) when, counting a pass-1 chunk as 0.8 of a pass-2

@@ -113,7 +113,7 @@ def test_default_plans_are_well_formed(host_check):
     build's stub launchers): the segments tile [0, T) in whole chunks of at least two, the launch
     sequence matches the plan's form, no launch has more workgroups than the 256 compute units hold
     in one round (unless the units alone exceed them), segments are used exactly when at most half
-    of the compute units would otherwise be busy and the sequence has four chunks, the workspace
+    of the compute units would otherwise be busy and the sequence has eight chunks, the workspace
     matches, and passing the returned plan back explicitly executes identically."""
     shapes = _plan_shapes(3000)
     stdin = "".join(" ".join(map(str, s)) + "\n" for s in shapes)
@@ -139,7 +139,7 @@ def test_default_plans_are_well_formed(host_check):
             why.append("explicit copy differs")
         elif dvb != dv:
             why.append(f"dv_block {dvb}")
-        elif (nseg > 1) != (units <= 128 and nch >= 4):
+        elif (nseg > 1) != (units <= 128 and nch >= 8):
             why.append(f"{nseg} segments for {units} units, {nch} chunks")
         elif nseg == 1:
             if what != ["chunk"] or f[0][:3] != [0, 0, 1] or need or seg0:
