@@ -111,13 +111,14 @@ kda_status_t resolve_plan(int64_t B, int64_t T, int32_t H, int32_t dk, int32_t d
         // Packed sequences: n_segments is the number of segments the packed row is cut into;
         // every sequence is split into segments of that length (whole chunks, at least two), so
         // only the sequences longer than it are split.  Default: one pass when the (sequence,
-        // head, column block) units cover the compute units, else as many segments as one round
-        // of workgroups holds (as below).
+        // head, column block) units cover the compute units or the packed row is shorter than
+        // kMinChunksToSplit chunks, else as many segments as one round of workgroups holds (as
+        // below).
         const int64_t ns = p.n_seqs;
         if (ns < 1) return fail(KDA_ERR_SHAPE, "n_seqs must be >= 1 (got %lld)", (long long)ns);
         out->n_seqs = (int32_t)ns;
         const int64_t per_slot = (int64_t)H * (dv / dvb);
-        if (nseg == 0) nseg = ns * per_slot < kPlanCUs ? kPlanCUs / per_slot : 1;
+        if (nseg == 0) nseg = ns * per_slot < kPlanCUs && nchunks >= kMinChunksToSplit ? kPlanCUs / per_slot : 1;
         int64_t seg_chunks = nchunks == 0 ? 1 : (nchunks + nseg - 1) / nseg;
         if (seg_chunks < 2) seg_chunks = 2;
         if (nseg > 1 && seg_chunks < nchunks) {

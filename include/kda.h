@@ -125,8 +125,8 @@ typedef enum {
  *   ceil(T / n_segments) tokens (rounded up to whole chunks, at least two
  *   chunks), so only sequences longer than that are split, each with its own
  *   prefix scan; 0 = one pass when the (sequence, head, column block) units
- *   cover MI355X's 256 compute units, else floor(256 / (H x column blocks))
- *   segments, one round of workgroups
+ *   cover MI355X's 256 compute units or T is shorter than 8 chunks, else
+ *   floor(256 / (H x column blocks)) segments, one round of workgroups
  *   (needs T < 2^31; the segment tables are built on the device from
  *   cu_seqlens inside the workspace).
  * flags: kda_input_flag_t bits (0 = log-decays, q and k used as given).
